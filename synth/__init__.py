@@ -1,0 +1,182 @@
+"""Seeded synthetic inputs for the block scorer and the block top-k.
+
+This module only draws numbers. It holds none of the selection method's
+arithmetic, so the CPU oracle (``oracle/``) and the HIP library can both be fed
+from it without sharing any code with each other.
+
+Generator
+---------
+* SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+  generators", OOPSLA 2014): element ``i`` (0-based) of the stream with seed
+  ``s`` is ``mix64(s + (i + 1) * 0x9E3779B97F4A7C15)``; it is counter based,
+  so any slice of a stream can be produced on its own.
+* U(0,1): ``(x >> 11) * 2**-53``.
+* N(0,1): Box-Muller in float64 on consecutive pairs ``(x[2i], x[2i+1])``
+  with ``u1 = ((x[2i] >> 11) + 1) * 2**-53`` (never 0) and
+  ``u2 = (x[2i+1] >> 11) * 2**-53``:
+  ``z[2i] = r cos(2 pi u2)``, ``z[2i+1] = r sin(2 pi u2)``, ``r = sqrt(-2 ln u1)``,
+  then rounded to float32.
+* Every tensor has its own stream: ``seed = mix64(BASE_SEED ^ fnv1a64(tag))``
+  where ``tag`` names the workload, the tensor and the context.
+
+Workloads
+---------
+The five workloads are the ones the pages benchmark (decode windows of a few
+queries, prompt chunks of 256 queries, 128-wide indexer keys, blocks of 4
+cells, a 2,048-cell selection); see ``c1`` .. ``c5``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+BASE_SEED = 20261202
+_GAMMA = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+_TWO_M53 = 2.0 ** -53
+
+
+def _mix64(z: np.ndarray) -> np.ndarray:
+    z = (z ^ (z >> np.uint64(30))) * _M1
+    z = (z ^ (z >> np.uint64(27))) * _M2
+    return z ^ (z >> np.uint64(31))
+
+
+def fnv1a64(text: str) -> int:
+    h = 0xCBF29CE484222325
+    for byte in text.encode():
+        h ^= byte
+        h = (h * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def stream_seed(tag: str) -> int:
+    z = np.array([(BASE_SEED ^ fnv1a64(tag)) & 0xFFFFFFFFFFFFFFFF], dtype=np.uint64)
+    return int(_mix64(z)[0])
+
+
+def splitmix64(seed: int, n: int, offset: int = 0) -> np.ndarray:
+    """Elements ``offset .. offset+n-1`` of the SplitMix64 stream ``seed``."""
+    with np.errstate(over="ignore"):
+        i = np.arange(offset + 1, offset + n + 1, dtype=np.uint64)
+        z = np.uint64(seed) + i * _GAMMA
+        return _mix64(z)
+
+
+def uniform01(tag: str, shape, dtype=np.float32) -> np.ndarray:
+    n = int(np.prod(shape))
+    x = splitmix64(stream_seed(tag), n)
+    u = (x >> np.uint64(11)).astype(np.float64) * _TWO_M53
+    return u.astype(dtype).reshape(shape)
+
+
+def normal(tag: str, shape, dtype=np.float32, chunk: int = 1 << 22) -> np.ndarray:
+    """N(0,1) by Box-Muller, generated in slices to bound host memory."""
+    n = int(np.prod(shape))
+    seed = stream_seed(tag)
+    out = np.empty(n, dtype=dtype)
+    npairs = (n + 1) // 2
+    for p0 in range(0, npairs, chunk):
+        p1 = min(npairs, p0 + chunk)
+        x = splitmix64(seed, 2 * (p1 - p0), offset=2 * p0)
+        u1 = ((x[0::2] >> np.uint64(11)).astype(np.float64) + 1.0) * _TWO_M53
+        u2 = (x[1::2] >> np.uint64(11)).astype(np.float64) * _TWO_M53
+        r = np.sqrt(-2.0 * np.log(u1))
+        z = np.empty(2 * (p1 - p0), dtype=np.float64)
+        z[0::2] = r * np.cos(2.0 * np.pi * u2)
+        z[1::2] = r * np.sin(2.0 * np.pi * u2)
+        lo = 2 * p0
+        hi = min(n, 2 * p1)
+        out[lo:hi] = z[: hi - lo].astype(dtype)
+    return out.reshape(shape)
+
+
+def quantize64(z: np.ndarray) -> np.ndarray:
+    """64 levels: ``clamp(rint(8 z), -32, 31) / 8`` (levels -4.0 .. 3.875)."""
+    return (np.clip(np.rint(z.astype(np.float64) * 8.0), -32, 31) / 8.0).astype(np.float32)
+
+
+def integers(tag: str, n: int, lo: int, hi: int) -> np.ndarray:
+    """n integers uniform in [lo, hi] (inclusive) from the stream ``tag``."""
+    x = splitmix64(stream_seed(tag), n)
+    span = np.uint64(hi - lo + 1)
+    return (lo + (x % span).astype(np.int64)).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# Workloads
+# --------------------------------------------------------------------------
+PAD_VALUE = np.float32(3.0e38)  # fills score-row padding past n_blocks; never read
+
+
+@dataclass
+class SelectWorkload:
+    """Scorer + top-k: q[nq,H,128], k[NB,128] N(0,1); w[nq,H] U(0,1)."""
+    name: str
+    nq: int
+    heads: int
+    n_blocks: int
+    block_size: int
+    width: int
+    call: str  # "decode" | "prompt"
+    head_dim: int = 128
+
+    def tensors(self):
+        q = normal(f"{self.name}/q", (self.nq, self.heads, self.head_dim))
+        k = normal(f"{self.name}/k", (self.n_blocks, self.head_dim))
+        w = uniform01(f"{self.name}/w", (self.nq, self.heads))
+        return q, k, w
+
+    def flops(self) -> float:
+        return 2.0 * self.nq * self.heads * self.head_dim * self.n_blocks
+
+
+@dataclass
+class TopkWorkload:
+    """Top-k only: scores[nq, ld] with n_blocks visible columns per row."""
+    name: str
+    nq: int
+    n_blocks: int
+    ld: int
+    block_size: int
+    width: int
+    call: str
+    variant: str = "continuous"  # continuous | q64 | equal
+
+    def scores(self) -> np.ndarray:
+        s = np.full((self.nq, self.ld), PAD_VALUE, dtype=np.float32)
+        if self.variant == "equal":
+            s[:, : self.n_blocks] = np.float32(1.0)
+            return s
+        z = normal(f"{self.name}/scores/{self.n_blocks}", (self.nq, self.n_blocks))
+        s[:, : self.n_blocks] = quantize64(z) if self.variant == "q64" else z
+        return s
+
+
+def c1() -> SelectWorkload:
+    return SelectWorkload("C1", nq=3, heads=8, n_blocks=1024, block_size=4, width=256, call="decode")
+
+
+C2_BLOCKS = (10240, 16384, 32768, 64512)  # 40,960 / 65,536 / 131,072 / 258,048 cells
+
+
+def c2(n_blocks: int) -> TopkWorkload:
+    return TopkWorkload("C2", nq=3, n_blocks=n_blocks, ld=65536, block_size=4, width=2048, call="decode")
+
+
+def c3() -> SelectWorkload:
+    return SelectWorkload("C3", nq=16, heads=16, n_blocks=65536, block_size=4, width=2048, call="decode")
+
+
+C4_BLOCKS = (32768, 65536, 100000, 130048)  # 131,072 / 262,144 / 400,000 / 520,192 cells
+
+
+def c4(n_blocks: int, variant: str = "continuous") -> TopkWorkload:
+    return TopkWorkload("C4", nq=256, n_blocks=n_blocks, ld=131072, block_size=4, width=2048,
+                        call="prompt", variant=variant)
+
+
+def c5() -> SelectWorkload:
+    return SelectWorkload("C5", nq=256, heads=32, n_blocks=131072, block_size=4, width=2048, call="prompt")

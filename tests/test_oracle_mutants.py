@@ -1,0 +1,85 @@
+"""The oracle's pins must catch plausible mistakes in the oracle itself.
+
+Each case edits one spot of a copy of ``oracle/qsa_oracle.c`` (a dropped term,
+a wrong sign, index or operand, a reversed order), compiles it on the CPU and
+runs the pins against it: at least one pin has to fail. The real oracle is
+never edited.
+"""
+import os
+
+import pytest
+
+import oracle
+import test_oracle_scores as S
+import test_oracle_topk as T
+
+SCORE_PINS = [
+    S.test_hand_example,
+    lambda lib: S.test_one_hot_keys_pick_a_coordinate(lib, 3),
+    S.test_nonnegative_inputs_reduce_to_gemv,
+    S.test_all_negative_dots_give_exact_zero,
+    S.test_single_head_weight_isolates_that_head,
+    S.test_mean_relu_matches_half_normal_closed_form,
+    S.test_scores_at_matches_full,
+]
+
+TOPK_PINS = [
+    lambda lib: T.test_hand_cases(lib, "topk_sort"),
+    lambda lib: T.test_hand_cases(lib, "topk_rule"),
+    lambda lib: T.test_brute_force_tiny(lib, 2),
+    lambda lib: T.test_increasing_keys_take_the_last_blocks(lib, "topk_sort", 4, 2047),
+    lambda lib: T.test_increasing_keys_take_the_last_blocks(lib, "topk_rule", 4, 2047),
+    lambda lib: T.test_invariants_on_prompt_like_rows(lib, "q64"),
+]
+
+# (name, original text, planted mistake, pins expected to notice)
+MUTANTS = [
+    ("relu dropped", "double relu = dot > 0.0 ? dot : 0.0;", "double relu = dot;", SCORE_PINS),
+    ("relu keeps negatives", "double relu = dot > 0.0 ? dot : 0.0;",
+     "double relu = dot < 0.0 ? dot : 0.0;", SCORE_PINS),
+    ("weight of head 0 for all heads", "total += (double)w[(int64_t)iq * heads + h] * relu;",
+     "total += (double)w[(int64_t)iq * heads] * relu;", SCORE_PINS),
+    ("weight not applied", "total += (double)w[(int64_t)iq * heads + h] * relu;",
+     "total += relu;", SCORE_PINS),
+    ("query layout [head][query]", "q + ((int64_t)iq * heads + h) * head_dim;",
+     "q + ((int64_t)h * nq + iq) * head_dim;", SCORE_PINS),
+    ("key row stride off by one", "k + (int64_t)b * head_dim;",
+     "k + (int64_t)b * (head_dim - 1);", SCORE_PINS),
+    ("last coordinate dropped", "for (int d = 0; d < head_dim; ++d)\n                    dot",
+     "for (int d = 0; d < head_dim - 1; ++d)\n                    dot", SCORE_PINS),
+    ("weight inside relu", "double relu = dot > 0.0 ? dot : 0.0;\n"
+     "                total += (double)w[(int64_t)iq * heads + h] * relu;",
+     "double wd = (double)w[(int64_t)iq * heads + h] * dot;\n"
+     "                total += wd > 0.0 ? wd : 0.0;", SCORE_PINS),
+    ("ties by highest cell", "return (a->cell > b->cell) - (a->cell < b->cell);",
+     "return (a->cell < b->cell) - (a->cell > b->cell);", TOPK_PINS),
+    ("keys ascending", "if (a->key > b->key)\n        return -1;",
+     "if (a->key > b->key)\n        return 1;\n    if (a->key < b->key)\n        return -1;\n    if (0)\n        return -1;",
+     TOPK_PINS),
+    ("cell takes the next block's key", "cells[c].key = scores[(int64_t)iq * ld + c / block_size];",
+     "cells[c].key = scores[(int64_t)iq * ld + (c + 1) / block_size];", TOPK_PINS),
+    ("active count ignored", "    if (!active)\n        return n_blocks;",
+     "    if (1)\n        return n_blocks;", TOPK_PINS),
+    ("above counts ties", "if (ordered_image(row[b]) > T)", "if (ordered_image(row[b]) >= T)", TOPK_PINS),
+    ("negative keys mapped by sign flip", "return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);",
+     "return (bits & 0x80000000u) ? (bits ^ 0x80000000u) : (bits | 0x80000000u);", TOPK_PINS),
+    ("signed zeros not merged", "    if (bits == 0x80000000u)\n        bits = 0u;", "", TOPK_PINS),
+    ("tie budget one too many", "} else if (key == T && budget > 0) {",
+     "} else if (key == T && budget >= 0) {", TOPK_PINS),
+]
+
+
+@pytest.mark.parametrize("name,orig,planted,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, name, orig, planted, pins):
+    src = open(oracle.SOURCE).read()
+    assert src.count(orig) >= 1, f"mutation site not found: {name}"
+    lib_path = oracle.compile_source(src.replace(orig, planted), os.path.join(tmp_path, "mutant.so"))
+    lib = oracle.Library(lib_path)
+    caught = []
+    for pin in pins:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(getattr(pin, "__name__", "pin"))
+            break
+    assert caught, f"no pin noticed the planted mistake '{name}'"
