@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-selection hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: the block scorer
+(qsa_block_scores) and then the block top-k (qsa_block_topk) on the scores it
+wrote - exactly what qsa_select enqueues - on the prompt-call workload:
+256 queries, 32 indexer heads, 128-wide keys, 131,072 blocks of 4 cells,
+a 2,048-cell selection. Inputs are seeded synthetic tensors (synth.c5) that
+are resident in HBM before the timed region starts.
+
+Prints ONE JSON line. Per-kernel times come from HIP events recorded on the
+stream the kernels run on (torch's current stream), around each entry point.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "qsa_select µs/call (score+top-k) decode nq=3 & prompt nq=256; % HBM/MFMA peak"
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+SCORER_SOURCE = os.path.join(ROOT, "sparse_attention_block_scores_amd", "csrc", "scores_kernel.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scores_kernel_c5_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the decode / top-k-only figures")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (to scale profiler byte counters)")
+    return ap.parse_args()
+
+
+def source_digest(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def event_pairs_mean_us(pairs) -> float:
+    return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) * 1000.0
+
+
+def measured_traffic(per_launch_flops_unit):
+    """HBM bytes per scorer launch from committed profiler counters, or None
+    when they are missing or were taken on another version of the kernel."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != source_digest(SCORER_SOURCE):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def timed_loop(torch, steps, body):
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        body(i)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1)  # ms
+
+
+def cpu_baseline(wl, q, k, w, budget_s=12.0):
+    """The oracle as it is, on the first queries of the same workload, until
+    about budget_s seconds of CPU work; scaled to microseconds per call."""
+    import numpy as np
+
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    done, elapsed, batch = 0, 0.0, 8
+    while done < wl.nq and elapsed < budget_s:
+        n = min(batch, wl.nq - done)
+        t = time.perf_counter()
+        s = oracle.block_scores(q[done:done + n], k, w[done:done + n])
+        oracle.topk_sort(s.astype(np.float32), wl.n_blocks, wl.block_size, wl.width)
+        elapsed += time.perf_counter() - t
+        done += n
+    return {
+        "value": round(elapsed / done * wl.nq * 1e6, 1),
+        "unit": "us/call",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {done} of {wl.nq} queries of the same workload (FP64 scores over all "
+                  f"{wl.n_blocks} blocks, then the full-sort top-k), {elapsed:.1f} s, scaled x{wl.nq / done:.2f}",
+    }
+
+
+def secondary(torch, qsa, synth, dev, reps=50):
+    """Decode-call latency at each context and top-k-only prompt figures."""
+    out = {}
+
+    def time_us(fn, n=reps):
+        for _ in range(3):
+            fn(0)
+        return timed_loop(torch, n, fn) / n * 1000.0
+
+    wl = synth.c1()
+    q, k, w = [torch.from_numpy(x).to(dev) for x in wl.tensors()]
+    ws = qsa.workspace(qsa.topk_workspace_bytes(wl.nq, wl.n_blocks, 4, wl.width, "decode"), dev)
+    s = torch.empty((wl.nq, wl.n_blocks), device=dev)
+    ids = torch.empty((wl.nq, wl.width), dtype=torch.int32, device=dev)
+    cnt = torch.empty((wl.nq,), dtype=torch.int32, device=dev)
+    out["decode_nq3_select_us"] = round(time_us(lambda i: qsa.select(q, k, w, 4, wl.width, "decode", scores=s,
+                                                                      ids=ids, counts=cnt, ws=ws)), 2)
+    wl3 = synth.c3()
+    q3, k3, w3 = [torch.from_numpy(x).to(dev) for x in wl3.tensors()]
+    ws3 = qsa.workspace(qsa.topk_workspace_bytes(wl3.nq, wl3.n_blocks, 4, wl3.width, "decode"), dev)
+    s3 = torch.empty((wl3.nq, wl3.n_blocks), device=dev)
+    ids3 = torch.empty((wl3.nq, wl3.width), dtype=torch.int32, device=dev)
+    cnt3 = torch.empty((wl3.nq,), dtype=torch.int32, device=dev)
+    out["decode_nq16_select_us"] = round(time_us(lambda i: qsa.select(q3, k3, w3, 4, wl3.width, "decode",
+                                                                       scores=s3, ids=ids3, counts=cnt3,
+                                                                       ws=ws3)), 2)
+    dec = {}
+    for nb in synth.C2_BLOCKS:
+        t = synth.c2(nb)
+        sc = torch.from_numpy(t.scores()).to(dev)
+        wsd = qsa.workspace(qsa.topk_workspace_bytes(t.nq, nb, 4, t.width, "decode"), dev)
+        idd = torch.empty((t.nq, t.width), dtype=torch.int32, device=dev)
+        cd = torch.empty((t.nq,), dtype=torch.int32, device=dev)
+        dec[str(nb * 4)] = round(time_us(lambda i: qsa.block_topk(sc, nb, 4, t.width, "decode", ids=idd,
+                                                                  counts=cd, ws=wsd)), 2)
+    out["decode_nq3_topk_us_by_cells"] = dec
+    prm = {}
+    for nb in synth.C4_BLOCKS:
+        t = synth.c4(nb)
+        host = t.scores()
+        # Four distinct score buffers (4 x 128 MiB) so that reads come from HBM,
+        # not from the 256 MB last-level cache.
+        bufs = [torch.from_numpy(host).to(dev) for _ in range(4)]
+        wsp = qsa.workspace(qsa.topk_workspace_bytes(t.nq, nb, 4, t.width, "prompt"), dev)
+        idp = torch.empty((t.nq, t.width), dtype=torch.int32, device=dev)
+        cp = torch.empty((t.nq,), dtype=torch.int32, device=dev)
+        us = time_us(lambda i: qsa.block_topk(bufs[i % 4], nb, 4, t.width, "prompt", ids=idp, counts=cp,
+                                              ws=wsp), n=40)
+        gbs = t.nq * nb * 4 / us / 1e3
+        prm[str(nb * 4)] = {"us": round(us, 2), "scores_GBps": round(gbs, 1),
+                            "hbm_frac": round(gbs / PEAK_HBM_GBS, 3)}
+        del bufs
+    out["prompt_nq256_topk_by_cells"] = prm
+    return out
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build measures the single-GPU hot path "
+              "(use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_attention_block_scores_amd as qsa
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda", 0)
+    wl = synth.c5()
+    q_h, k_h, w_h = wl.tensors()
+    q, k, w = (torch.from_numpy(x).to(dev) for x in (q_h, k_h, w_h))
+    scores = torch.empty((wl.nq, wl.n_blocks), dtype=torch.float32, device=dev)
+    ids = torch.empty((wl.nq, wl.width), dtype=torch.int32, device=dev)
+    counts = torch.empty((wl.nq,), dtype=torch.int32, device=dev)
+    ws = qsa.workspace(qsa.topk_workspace_bytes(wl.nq, wl.n_blocks, wl.block_size, wl.width, wl.call), dev)
+
+    if args.copy_calibration_mib:
+        src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(i, record=True):
+        if record:
+            ev[i][0].record()
+        qsa.block_scores(q, k, w, scores=scores)
+        if record:
+            ev[i][1].record()
+        qsa.block_topk(scores, wl.n_blocks, wl.block_size, wl.width, wl.call, ids=ids, counts=counts, ws=ws)
+        if record:
+            ev[i][2].record()
+
+    for _ in range(args.warmup):
+        step(0, record=False)
+    torch.cuda.synchronize()
+    total_ms = timed_loop(torch, args.steps, step)
+    ms_per_step = total_ms / args.steps
+    scorer_us = event_pairs_mean_us([(e[0], e[1]) for e in ev])
+    topk_us = event_pairs_mean_us([(e[1], e[2]) for e in ev])
+
+    # The same work through the single qsa_select entry point.
+    for _ in range(2):
+        qsa.select(q, k, w, wl.block_size, wl.width, wl.call, scores=scores, ids=ids, counts=counts, ws=ws)
+    sel_ms = timed_loop(torch, args.steps, lambda i: qsa.select(q, k, w, wl.block_size, wl.width, wl.call,
+                                                                scores=scores, ids=ids, counts=counts, ws=ws))
+    select_us = sel_ms / args.steps * 1000.0
+
+    tflops = wl.flops() / (scorer_us * 1e-6) / 1e12
+    traffic = measured_traffic(None)
+    line = {
+        "metric": METRIC,
+        "value": round(ms_per_step * 1000.0, 1),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "prompt-call select: 256 queries x 32 indexer heads x K=128 against "
+                               "131,072 blocks of 4 cells, width 2,048 cells",
+                   "nq": wl.nq, "heads": wl.heads, "head_dim": wl.head_dim, "n_blocks": wl.n_blocks,
+                   "block_size": wl.block_size, "width": wl.width, "call": wl.call},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "scores_kernel (FP32 MFMA scorer)",
+                     "flops_per_launch": wl.flops(), "kernel_us": round(scorer_us, 2)},
+        "topk_us": round(topk_us, 2),
+        "qsa_select_single_call_us": round(select_us, 1),
+    }
+    if not args.no_secondary:
+        line["secondary"] = secondary(torch, qsa, synth, dev)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, q_h, k_h, w_h)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * qsa.h - C ABI of libqsa.so: sparse-attention block selection on MI355X
+ * (gfx950).
+ *
+ * Two steps make up the selection an indexer runs before sparse attention:
+ *
+ *  1. Block scores (Strata pull #1091 "qsa_select: FP32 tiled block scores
+ *     below sm_80", section What). For query q and key block b,
+ *         score[q][b] = sum_h w[q][h] * max(0, dot(q[q][h][:], k[b][:]))
+ *     with a 128-wide indexer key: a dense FP32 contraction over rows of
+ *     (query, indexer head), a relu per head, and a weighted head sum.
+ *
+ *  2. Block top-k (Strata pull #3987, section Approach; Strata pull #2093
+ *     "sm_75: the prompt path's top-k with one full read of the scores",
+ *     section Beschreibung). Each block holds `block_size` cells and every
+ *     cell carries its block's score as its key. The selection is the first
+ *     min(width, visible cells) cells in the order (key descending, cell id
+ *     ascending): a threshold T (the width-th largest cell key), every cell
+ *     above T, and a tie budget of cells equal to T filled from the lowest
+ *     block (then lowest cell) upward. Cells are written in ascending order.
+ *     -0.0 and +0.0 are equal keys. Keys must be finite (NaN and Inf are
+ *     outside the contract: results are unspecified but the call is safe).
+ *
+ * Calls. A decode call carries no active-block count: all n_blocks blocks are
+ * visible to every query. A prompt call may carry a per-query active-block
+ * count: query q sees blocks [0, min(max(active[q], 0), n_blocks)).
+ *
+ * Memory and streams. Every pointer argument except `opt` and `out` structs
+ * is caller-owned DEVICE memory; the library never allocates, frees or keeps
+ * device memory of its own and holds no device globals. All work is enqueued
+ * on `stream` (a hipStream_t; NULL = the default stream) and the calls return
+ * without synchronising. Nothing is printed.
+ *
+ * Errors. Arguments are checked on the host before anything is launched; a
+ * call that returns anything but QSA_OK has enqueued nothing. QSA_EHIP means
+ * a launch failed (work enqueued before the failure may still run).
+ *
+ * Workspace. The top-k needs a scratch area of qsa_topk_workspace_bytes()
+ * bytes, 256-byte aligned. Its counter region must be zero before its first
+ * use (qsa_workspace_init() zero-fills it, so does any zero fill); every call
+ * that completes leaves it zero again. Calls that may run concurrently (two
+ * streams) need separate workspaces.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qsa_status {
+    QSA_OK = 0,
+    QSA_EINVAL = 1,        /* argument out of range, inconsistent or misaligned */
+    QSA_EUNSUPPORTED = 2,  /* valid request this build does not implement */
+    QSA_EWORKSPACE = 3,    /* workspace NULL, misaligned or too small */
+    QSA_EHIP = 4           /* a HIP launch or runtime call failed */
+} qsa_status;
+
+typedef enum qsa_call {
+    QSA_DECODE = 0,  /* no active-block count: every block is visible */
+    QSA_PROMPT = 1   /* optional per-query active-block count */
+} qsa_call;
+
+/* Top-k path choice. AUTO is what production callers use; the others force a
+ * path for tests and measurements. Every path returns the same ids. */
+enum {
+    QSA_PATH_AUTO = 0,
+    QSA_PATH_SPLIT = 1,    /* exact chunked split: per-chunk stage A, per-query stage B */
+    QSA_PATH_ONEREAD = 2   /* prompt calls: sampled bound, one read, exact fallback per query */
+};
+
+/* Sampling of the one-read path's lower bound (results never depend on it). */
+enum {
+    QSA_SAMPLE_AUTO = 0,
+    QSA_SAMPLE_STRIDE = 1, /* every 32nd block (one key per 128-byte line) */
+    QSA_SAMPLE_LINES = 2   /* 32 consecutive blocks out of every 1,024 */
+};
+
+/* Optional knobs; pass NULL for the defaults. Zero-initialise and set only
+ * what is needed. None of them changes a result. */
+typedef struct qsa_options {
+    int32_t topk_path;      /* QSA_PATH_* */
+    int32_t chunk_blocks;   /* SPLIT chunk size in blocks: 0 = auto, else 64..15360, multiple of 4 */
+    int32_t sample;         /* QSA_SAMPLE_* */
+    int32_t force_fallback; /* ONEREAD: every query takes the exact fallback over its whole row */
+    int32_t oneread_blocks; /* ONEREAD blocks streamed per batch: 0 or 16384 (others QSA_EUNSUPPORTED) */
+    int32_t reserved[3];    /* must be zero */
+} qsa_options;
+
+/* The launch plan the top-k would use; exported so host code and tests can
+ * inspect the dispatch without a GPU. Sizes are for the largest query. */
+typedef struct qsa_topk_plan {
+    int32_t path;            /* QSA_PATH_SPLIT or QSA_PATH_ONEREAD */
+    int32_t r_blocks;        /* blocks a full selection touches: ceil(min(width, n_blocks*bs) / bs) */
+    int32_t chunk_blocks;    /* SPLIT chunk size: the fewest chunks of <= 4,104 blocks, equal sizes */
+    int32_t n_chunks;        /* SPLIT chunks per query */
+    int32_t split_threads;   /* SPLIT workgroup size */
+    int32_t stage_b_lds;     /* 1 if stage B keeps its candidates in LDS */
+    int32_t oneread_blocks;  /* ONEREAD blocks streamed per batch */
+    int32_t oneread_groups;  /* ONEREAD workgroups per query (1) */
+    int32_t cap;             /* ONEREAD candidate cap per query (blocks) */
+    int32_t sample_stride;   /* 32 */
+    int32_t sample_mode;     /* QSA_SAMPLE_STRIDE or QSA_SAMPLE_LINES */
+    int32_t ks;              /* sample rank of the bound: 2*r_blocks/32 + 16 */
+    uint64_t workspace_bytes;
+} qsa_topk_plan;
+
+/*
+ * qsa_block_scores - step 1 (Strata pull #1091, section What).
+ *
+ *   q       [nq][n_heads][head_dim] float, row-major, 16-byte aligned
+ *   k       [n_blocks][head_dim]    float, row-major, 16-byte aligned
+ *   w       [nq][n_heads]           float
+ *   scores  [nq][ld_scores]         float output; columns >= n_blocks untouched
+ *   head_dim must be 128 (else QSA_EUNSUPPORTED); 1 <= n_heads <= 64;
+ *   nq >= 1, n_blocks >= 1, ld_scores >= n_blocks.
+ *   FP32 inputs, FP32 matrix-core products with FP32 accumulation.
+ */
+qsa_status qsa_block_scores(const float *q, const float *k, const float *w,
+                            float *scores, int64_t ld_scores,
+                            int32_t nq, int32_t n_heads, int32_t head_dim,
+                            int32_t n_blocks, void *stream);
+
+/* Bytes of workspace qsa_block_topk / qsa_select need for these sizes and
+ * options (0 if the arguments are invalid). */
+size_t qsa_topk_workspace_bytes(int32_t nq, int32_t n_blocks, int32_t block_size,
+                                int32_t width, qsa_call call, const qsa_options *opt);
+
+/* Fill the plan for these arguments (host only; no GPU needed). */
+qsa_status qsa_topk_plan_get(int32_t nq, int32_t n_blocks, int32_t block_size,
+                             int32_t width, qsa_call call, const qsa_options *opt,
+                             qsa_topk_plan *out);
+
+/* Zero-fill `bytes` of workspace on `stream` (a kernel, not a memset). */
+qsa_status qsa_workspace_init(void *workspace, size_t bytes, void *stream);
+
+/*
+ * qsa_block_topk - step 2 (Strata pull #3987, section Approach; Strata pull
+ * #2093, section Beschreibung).
+ *
+ *   scores         [nq][ld_scores] float; only columns < n_blocks are read
+ *   active_blocks  [nq] int32, PROMPT only (NULL = every block visible);
+ *                  non-NULL with QSA_DECODE is QSA_EINVAL
+ *   cell_ids       [nq][width] int32 output: selected cell ids b*block_size+j,
+ *                  ascending, then -1 up to width
+ *   counts         [nq] int32 output or NULL: min(width, visible cells)
+ *   workspace      qsa_topk_workspace_bytes(...) bytes (see above)
+ *   1 <= block_size, 1 <= width, n_blocks * block_size < 2^31, nq >= 1.
+ */
+qsa_status qsa_block_topk(const float *scores, int64_t ld_scores, int32_t nq,
+                          int32_t n_blocks, int32_t block_size, int32_t width,
+                          qsa_call call, const int32_t *active_blocks,
+                          int32_t *cell_ids, int32_t *counts,
+                          void *workspace, size_t workspace_bytes, void *stream,
+                          const qsa_options *opt);
+
+/*
+ * qsa_select - qsa_block_scores followed by qsa_block_topk on the scores it
+ * wrote (`scores` is the caller's buffer and holds the scores afterwards).
+ * Same argument rules as the two calls above.
+ */
+qsa_status qsa_select(const float *q, const float *k, const float *w,
+                      int32_t n_heads, int32_t head_dim,
+                      float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks,
+                      int32_t block_size, int32_t width, qsa_call call,
+                      const int32_t *active_blocks, int32_t *cell_ids, int32_t *counts,
+                      void *workspace, size_t workspace_bytes, void *stream,
+                      const qsa_options *opt);
+
+/* Static text for a status code. */
+const char *qsa_status_str(qsa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -1,0 +1,250 @@
+"""ctypes binding of libqsa.so (include/qsa.h): argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; this module
+turns torch tensors into device pointers and the current HIP stream into a
+hipStream_t, and raises on a non-OK status. If the library has not been built
+it raises instead of computing anything some other way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libqsa.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "qsa.h")
+
+QSA_OK, QSA_EINVAL, QSA_EUNSUPPORTED, QSA_EWORKSPACE, QSA_EHIP = range(5)
+DECODE, PROMPT = 0, 1
+PATH_AUTO, PATH_SPLIT, PATH_ONEREAD = 0, 1, 2
+SAMPLE_AUTO, SAMPLE_STRIDE, SAMPLE_LINES = 0, 1, 2
+
+
+class QSAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+class Options(ctypes.Structure):
+    """qsa_options: optional knobs; none of them changes a result."""
+    _fields_ = [
+        ("topk_path", ctypes.c_int32),
+        ("chunk_blocks", ctypes.c_int32),
+        ("sample", ctypes.c_int32),
+        ("force_fallback", ctypes.c_int32),
+        ("oneread_blocks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
+    ]
+
+
+class Plan(ctypes.Structure):
+    """qsa_topk_plan."""
+    _fields_ = [
+        ("path", ctypes.c_int32),
+        ("r_blocks", ctypes.c_int32),
+        ("chunk_blocks", ctypes.c_int32),
+        ("n_chunks", ctypes.c_int32),
+        ("split_threads", ctypes.c_int32),
+        ("stage_b_lds", ctypes.c_int32),
+        ("oneread_blocks", ctypes.c_int32),
+        ("oneread_groups", ctypes.c_int32),
+        ("cap", ctypes.c_int32),
+        ("sample_stride", ctypes.c_int32),
+        ("sample_mode", ctypes.c_int32),
+        ("ks", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libqsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(
+                f"{LIBRARY} is missing: build it with `python -m sparse_attention_block_scores_amd.build`")
+        L = ctypes.CDLL(LIBRARY)
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.qsa_status_str.argtypes = [i32]
+        L.qsa_status_str.restype = ctypes.c_char_p
+        L.qsa_block_scores.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P]
+        L.qsa_topk_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, P]
+        L.qsa_topk_workspace_bytes.restype = sz
+        L.qsa_topk_plan_get.argtypes = [i32, i32, i32, i32, i32, P, P]
+        L.qsa_workspace_init.argtypes = [P, sz, P]
+        L.qsa_block_topk.argtypes = [P, i64, i32, i32, i32, i32, i32, P, P, P, P, sz, P, P]
+        L.qsa_select.argtypes = [P, P, P, i32, i32, P, i64, i32, i32, i32, i32, i32, P, P, P, P, sz, P, P]
+        for name in ("qsa_block_scores", "qsa_topk_plan_get", "qsa_workspace_init", "qsa_block_topk",
+                     "qsa_select"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def declared_functions() -> list[str]:
+    """Function names declared in include/qsa.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_ ]*?[\s*]+(qsa_[a-z_]+)\s*\(",
+                                 text, re.M)))
+
+
+def status_str(status: int) -> str:
+    return lib().qsa_status_str(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != QSA_OK:
+        raise QSAError(status, where)
+
+
+def _call_code(call) -> int:
+    if call in ("decode", DECODE):
+        return DECODE
+    if call in ("prompt", PROMPT):
+        return PROMPT
+    raise ValueError(f"call must be 'decode' or 'prompt', not {call!r}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _opt(options):
+    return None if options is None else ctypes.byref(options)
+
+
+def make_options(**kw) -> Options:
+    o = Options()
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def topk_plan(nq, n_blocks, block_size, width, call, options=None) -> dict:
+    p = Plan()
+    _check(lib().qsa_topk_plan_get(nq, n_blocks, block_size, width, _call_code(call), _opt(options),
+                                   ctypes.byref(p)), "qsa_topk_plan_get")
+    return p.as_dict()
+
+
+def topk_workspace_bytes(nq, n_blocks, block_size, width, call, options=None) -> int:
+    n = lib().qsa_topk_workspace_bytes(nq, n_blocks, block_size, width, _call_code(call), _opt(options))
+    if n == 0:
+        raise QSAError(QSA_EINVAL, "qsa_topk_workspace_bytes")
+    return n
+
+
+def workspace(nbytes: int, device=None, stream=None) -> torch.Tensor:
+    """A zero-filled workspace of nbytes (256-byte aligned)."""
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    ws = buf[off:off + nbytes]
+    _check(lib().qsa_workspace_init(_ptr(ws), nbytes, _stream(stream)), "qsa_workspace_init")
+    return ws
+
+
+def block_scores(q, k, w, scores=None, stream=None):
+    """score[q,b] = sum_h w[q,h] relu(q[q,h,:] . k[b,:]) -> float32 [nq, ld]."""
+    _dev(q, torch.float32, "q"), _dev(k, torch.float32, "k"), _dev(w, torch.float32, "w")
+    if not (q.is_contiguous() and k.is_contiguous() and w.is_contiguous()):
+        raise ValueError("q, k and w must be contiguous")
+    nq, heads, head_dim = q.shape
+    n_blocks = k.shape[0]
+    if k.shape[1] != head_dim or tuple(w.shape) != (nq, heads):
+        raise ValueError("shape mismatch between q, k and w")
+    if scores is None:
+        scores = torch.empty((nq, n_blocks), dtype=torch.float32, device=q.device)
+    _dev(scores, torch.float32, "scores")
+    if scores.dim() != 2 or scores.shape[0] != nq or scores.stride(1) != 1:
+        raise ValueError("scores must be [nq, ld] with unit column stride")
+    _check(lib().qsa_block_scores(_ptr(q), _ptr(k), _ptr(w), _ptr(scores), scores.stride(0), nq, heads,
+                                  head_dim, n_blocks, _stream(stream)), "qsa_block_scores")
+    return scores
+
+
+def _topk_outputs(nq, width, device, ids, counts):
+    if ids is None:
+        ids = torch.empty((nq, width), dtype=torch.int32, device=device)
+    if counts is None:
+        counts = torch.empty((nq,), dtype=torch.int32, device=device)
+    _dev(ids, torch.int32, "ids"), _dev(counts, torch.int32, "counts")
+    if not ids.is_contiguous() or tuple(ids.shape) != (nq, width):
+        raise ValueError("ids must be a contiguous [nq, width] int32 tensor")
+    return ids, counts
+
+
+def _active(active, nq):
+    if active is None:
+        return None
+    _dev(active, torch.int32, "active")
+    if tuple(active.shape) != (nq,) or not active.is_contiguous():
+        raise ValueError("active must be a contiguous [nq] int32 tensor")
+    return active
+
+
+def block_topk(scores, n_blocks, block_size, width, call, active=None, ids=None, counts=None,
+               ws=None, options=None, stream=None):
+    """Selected cell ids [nq, width] (ascending, -1 tail) and counts [nq]."""
+    _dev(scores, torch.float32, "scores")
+    if scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be [nq, ld] with unit column stride")
+    nq = scores.shape[0]
+    code = _call_code(call)
+    active = _active(active, nq)
+    ids, counts = _topk_outputs(nq, width, scores.device, ids, counts)
+    need = topk_workspace_bytes(nq, n_blocks, block_size, width, code, options)
+    if ws is None:
+        ws = workspace(need, scores.device, stream)
+    _check(lib().qsa_block_topk(_ptr(scores), scores.stride(0), nq, n_blocks, block_size, width, code,
+                                _ptr(active), _ptr(ids), _ptr(counts), _ptr(ws), ws.numel(),
+                                _stream(stream), _opt(options)), "qsa_block_topk")
+    return ids, counts
+
+
+def select(q, k, w, block_size, width, call, scores=None, active=None, ids=None, counts=None,
+           ws=None, options=None, stream=None):
+    """Scores then top-k: returns (scores, ids, counts)."""
+    for t, n in ((q, "q"), (k, "k"), (w, "w")):
+        _dev(t, torch.float32, n)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    nq, heads, head_dim = q.shape
+    n_blocks = k.shape[0]
+    if scores is None:
+        scores = torch.empty((nq, n_blocks), dtype=torch.float32, device=q.device)
+    _dev(scores, torch.float32, "scores")
+    code = _call_code(call)
+    active = _active(active, nq)
+    ids, counts = _topk_outputs(nq, width, q.device, ids, counts)
+    need = topk_workspace_bytes(nq, n_blocks, block_size, width, code, options)
+    if ws is None:
+        ws = workspace(need, q.device, stream)
+    _check(lib().qsa_select(_ptr(q), _ptr(k), _ptr(w), heads, head_dim, _ptr(scores), scores.stride(0), nq,
+                            n_blocks, block_size, width, code, _ptr(active), _ptr(ids), _ptr(counts),
+                            _ptr(ws), ws.numel(), _stream(stream), _opt(options)), "qsa_select")
+    return scores, ids, counts

@@ -1,0 +1,305 @@
+// qsa_api.hip - the C ABI of libqsa.so: argument checks, the top-k dispatch
+// plan, workspace layout and the launches. Nothing here allocates device
+// memory, synchronises or prints.
+#include <stdint.h>
+#include <string.h>
+
+#include "qsa_internal.h"
+
+namespace qsa {
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+qsa_status check_options(const qsa_options *opt)
+{
+    if (!opt)
+        return QSA_OK;
+    for (int i = 0; i < 3; ++i)
+        if (opt->reserved[i] != 0)
+            return QSA_EINVAL;
+    if (opt->topk_path < QSA_PATH_AUTO || opt->topk_path > QSA_PATH_ONEREAD)
+        return QSA_EINVAL;
+    if (opt->chunk_blocks != 0 &&
+        (opt->chunk_blocks < kMinChunk || opt->chunk_blocks > kMaxChunk || opt->chunk_blocks % 4 != 0))
+        return QSA_EINVAL;
+    if (opt->sample < QSA_SAMPLE_AUTO || opt->sample > QSA_SAMPLE_LINES)
+        return QSA_EINVAL;
+    if (opt->force_fallback != 0 && opt->force_fallback != 1)
+        return QSA_EINVAL;
+    if (opt->oneread_blocks != 0 && opt->oneread_blocks != kOneReadBatch)
+        return QSA_EUNSUPPORTED;
+    return QSA_OK;
+}
+
+} // namespace
+
+qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int32_t width,
+                          qsa_call call, const qsa_options *opt, TopkPlan &plan)
+{
+    memset(&plan, 0, sizeof plan);
+    if (nq < 0 || n_blocks < 0 || block_size < 1 || width < 1)
+        return QSA_EINVAL;
+    if (call != QSA_DECODE && call != QSA_PROMPT)
+        return QSA_EINVAL;
+    if ((int64_t)n_blocks * block_size >= ((int64_t)1 << 31))
+        return QSA_EINVAL;
+    if (nq > 65535)
+        return QSA_EUNSUPPORTED;
+    const qsa_status os = check_options(opt);
+    if (os != QSA_OK)
+        return os;
+
+    qsa_topk_plan &p = plan.pub;
+    const int64_t cells = (int64_t)n_blocks * block_size;
+    const int64_t wmax = cells < width ? cells : width;
+    p.r_blocks = (int32_t)((wmax + block_size - 1) / block_size);
+
+    // Split geometry: the fewest chunks of at most kChunkBound blocks, equal
+    // sizes rounded up to a multiple of 4 (or the forced size).
+    if (opt && opt->chunk_blocks) {
+        p.chunk_blocks = opt->chunk_blocks;
+    } else {
+        const int32_t nb = n_blocks > 0 ? n_blocks : 1;
+        const int32_t k = (nb + kChunkBound - 1) / kChunkBound;
+        p.chunk_blocks = ((nb + k - 1) / k + 3) / 4 * 4;
+    }
+    p.n_chunks = n_blocks > 0 ? (n_blocks + p.chunk_blocks - 1) / p.chunk_blocks : 1;
+    p.split_threads = kSplitThreads;
+    const int64_t cap_c = p.r_blocks < p.chunk_blocks ? p.r_blocks : p.chunk_blocks;
+    plan.cand_stride = ((int64_t)p.n_chunks * (cap_c > 0 ? cap_c : 1) + 3) / 4 * 4;
+    p.stage_b_lds = plan.cand_stride <= kStageBLdsWords ? 1 : 0;
+
+    // One-read geometry: one workgroup per query streaming batches of blocks.
+    p.oneread_blocks = kOneReadBatch;
+    p.oneread_groups = 1;
+    p.cap = kOneReadCap;
+    p.sample_stride = kSampleStride;
+    p.sample_mode = (opt && opt->sample) ? opt->sample : QSA_SAMPLE_LINES;
+    p.ks = 2 * p.r_blocks / kSampleStride + 16;
+
+    // Dispatch.
+    int path = opt ? opt->topk_path : QSA_PATH_AUTO;
+    if (path == QSA_PATH_AUTO)
+        path = (call == QSA_PROMPT && n_blocks >= kOneReadMinBlocks && nq >= kOneReadMinQueries)
+                   ? QSA_PATH_ONEREAD
+                   : QSA_PATH_SPLIT;
+    p.path = path;
+
+    // Workspace: only the split keeps candidates in global memory.
+    TopkLayout &L = plan.lay;
+    size_t off = 0;
+    if (path == QSA_PATH_SPLIT) {
+        const size_t q = (size_t)(nq > 0 ? nq : 1);
+        L.split_tickets = off; off = align_up(off + q * 4);
+        L.split_meta = off;    off = align_up(off + q * (size_t)p.n_chunks * 8);
+        L.split_keys = off;    off = align_up(off + q * (size_t)plan.cand_stride * 4);
+        L.split_blocks = off;  off = align_up(off + q * (size_t)plan.cand_stride * 4);
+    } else {
+        off = kAlign;  // nothing is kept; a minimal non-empty workspace
+    }
+    L.bytes = off;
+    p.workspace_bytes = off;
+    return QSA_OK;
+}
+
+namespace {
+
+qsa_status check_topk_args(const float *scores, int64_t ld, int32_t nq, int32_t n_blocks,
+                           qsa_call call, const int32_t *active, const int32_t *ids,
+                           const int32_t *counts)
+{
+    if (nq > 0 && (!scores || !ids))
+        return QSA_EINVAL;
+    if (ld < n_blocks || ld < 1)
+        return QSA_EINVAL;
+    if (call == QSA_DECODE && active)
+        return QSA_EINVAL;
+    if (!aligned(scores, 4) || !aligned(ids, 4) || !aligned(counts, 4) || !aligned(active, 4))
+        return QSA_EINVAL;
+    return QSA_OK;
+}
+
+TopkGeom make_geom(const float *scores, int64_t ld, int32_t nq, int32_t n_blocks, int32_t bs,
+                   int32_t width, const int32_t *active, int32_t *ids, int32_t *counts)
+{
+    TopkGeom g;
+    g.scores = scores;
+    g.ld = ld;
+    g.nq = nq;
+    g.n_blocks = n_blocks;
+    g.bs = bs;
+    g.width = width;
+    g.active = active;
+    g.ids = ids;
+    g.counts = counts;
+    g.vec4 = (aligned(scores, 16) && ld % 4 == 0) ? 1 : 0;
+    return g;
+}
+
+template <class T>
+T *at(void *base, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(base) + off); }
+
+qsa_status run_topk(const TopkGeom &g, const TopkPlan &plan, void *ws, hipStream_t s,
+                    const qsa_options *opt)
+{
+    const qsa_topk_plan &p = plan.pub;
+    if (p.path == QSA_PATH_ONEREAD) {
+        OneReadArgs oa;
+        oa.g = g;
+        oa.mode = p.sample_mode;
+        oa.force_flag = (opt && opt->force_fallback) ? 1 : 0;
+        return launch_oneread(oa, s) == hipSuccess ? QSA_OK : QSA_EHIP;
+    }
+    const TopkLayout &L = plan.lay;
+    SplitArgs sa;
+    sa.g = g;
+    sa.tickets = at<uint32_t>(ws, L.split_tickets);
+    sa.meta = at<uint32_t>(ws, L.split_meta);
+    sa.cand_keys = at<uint32_t>(ws, L.split_keys);
+    sa.cand_blocks = at<int32_t>(ws, L.split_blocks);
+    sa.cand_stride = plan.cand_stride;
+    sa.chunk = p.chunk_blocks;
+    sa.n_chunks = p.n_chunks;
+    const int64_t stage_b = p.stage_b_lds ? plan.cand_stride : 0;
+    sa.lds_words = (int32_t)(stage_b > p.chunk_blocks ? stage_b : p.chunk_blocks);
+    return launch_split(sa, s) == hipSuccess ? QSA_OK : QSA_EHIP;
+}
+
+qsa_status check_score_args(const float *q, const float *k, const float *w, const float *scores,
+                            int64_t ld, int32_t nq, int32_t heads, int32_t head_dim, int32_t n_blocks)
+{
+    if (nq < 0 || n_blocks < 0 || heads < 1 || head_dim < 1)
+        return QSA_EINVAL;
+    if (ld < n_blocks || ld < 1)
+        return QSA_EINVAL;
+    if (head_dim != 128 || heads > 64)
+        return QSA_EUNSUPPORTED;
+    if (nq > 0 && n_blocks > 0 && (!q || !k || !w || !scores))
+        return QSA_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4) || !aligned(scores, 4))
+        return QSA_EINVAL;
+    if ((int64_t)nq * 64 > 0x7fffffffLL)
+        return QSA_EUNSUPPORTED;
+    return QSA_OK;
+}
+
+} // namespace
+} // namespace qsa
+
+using namespace qsa;
+
+extern "C" {
+
+const char *qsa_status_str(qsa_status status)
+{
+    switch (status) {
+    case QSA_OK: return "ok";
+    case QSA_EINVAL: return "invalid argument";
+    case QSA_EUNSUPPORTED: return "unsupported argument";
+    case QSA_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case QSA_EHIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+qsa_status qsa_topk_plan_get(int32_t nq, int32_t n_blocks, int32_t block_size, int32_t width,
+                             qsa_call call, const qsa_options *opt, qsa_topk_plan *out)
+{
+    if (!out)
+        return QSA_EINVAL;
+    TopkPlan plan;
+    const qsa_status st = make_topk_plan(nq, n_blocks, block_size, width, call, opt, plan);
+    if (st == QSA_OK)
+        *out = plan.pub;
+    return st;
+}
+
+size_t qsa_topk_workspace_bytes(int32_t nq, int32_t n_blocks, int32_t block_size, int32_t width,
+                                qsa_call call, const qsa_options *opt)
+{
+    TopkPlan plan;
+    if (make_topk_plan(nq, n_blocks, block_size, width, call, opt, plan) != QSA_OK)
+        return 0;
+    return plan.lay.bytes;
+}
+
+qsa_status qsa_workspace_init(void *workspace, size_t bytes, void *stream)
+{
+    if (!workspace || !aligned(workspace, kAlign))
+        return QSA_EWORKSPACE;
+    return launch_zero(workspace, bytes, (hipStream_t)stream) == hipSuccess ? QSA_OK : QSA_EHIP;
+}
+
+qsa_status qsa_block_scores(const float *q, const float *k, const float *w, float *scores,
+                            int64_t ld_scores, int32_t nq, int32_t n_heads, int32_t head_dim,
+                            int32_t n_blocks, void *stream)
+{
+    const qsa_status st = check_score_args(q, k, w, scores, ld_scores, nq, n_heads, head_dim, n_blocks);
+    if (st != QSA_OK)
+        return st;
+    if (nq == 0 || n_blocks == 0)
+        return QSA_OK;
+    ScoreArgs a{q, k, w, scores, ld_scores, nq, n_heads, n_blocks};
+    return launch_scores(a, (hipStream_t)stream) == hipSuccess ? QSA_OK : QSA_EHIP;
+}
+
+qsa_status qsa_block_topk(const float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks,
+                          int32_t block_size, int32_t width, qsa_call call,
+                          const int32_t *active_blocks, int32_t *cell_ids, int32_t *counts,
+                          void *workspace, size_t workspace_bytes, void *stream,
+                          const qsa_options *opt)
+{
+    TopkPlan plan;
+    qsa_status st = make_topk_plan(nq, n_blocks, block_size, width, call, opt, plan);
+    if (st != QSA_OK)
+        return st;
+    st = check_topk_args(scores, ld_scores, nq, n_blocks, call, active_blocks, cell_ids, counts);
+    if (st != QSA_OK)
+        return st;
+    if (nq == 0)
+        return QSA_OK;
+    if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < plan.lay.bytes)
+        return QSA_EWORKSPACE;
+    const TopkGeom g = make_geom(scores, ld_scores, nq, n_blocks, block_size, width, active_blocks,
+                                 cell_ids, counts);
+    return run_topk(g, plan, workspace, (hipStream_t)stream, opt);
+}
+
+qsa_status qsa_select(const float *q, const float *k, const float *w, int32_t n_heads,
+                      int32_t head_dim, float *scores, int64_t ld_scores, int32_t nq,
+                      int32_t n_blocks, int32_t block_size, int32_t width, qsa_call call,
+                      const int32_t *active_blocks, int32_t *cell_ids, int32_t *counts,
+                      void *workspace, size_t workspace_bytes, void *stream,
+                      const qsa_options *opt)
+{
+    qsa_status st = check_score_args(q, k, w, scores, ld_scores, nq, n_heads, head_dim, n_blocks);
+    if (st != QSA_OK)
+        return st;
+    TopkPlan plan;
+    st = make_topk_plan(nq, n_blocks, block_size, width, call, opt, plan);
+    if (st != QSA_OK)
+        return st;
+    st = check_topk_args(scores, ld_scores, nq, n_blocks, call, active_blocks, cell_ids, counts);
+    if (st != QSA_OK)
+        return st;
+    if (nq == 0)
+        return QSA_OK;
+    if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < plan.lay.bytes)
+        return QSA_EWORKSPACE;
+    if (n_blocks > 0) {
+        ScoreArgs a{q, k, w, scores, ld_scores, nq, n_heads, n_blocks};
+        if (launch_scores(a, (hipStream_t)stream) != hipSuccess)
+            return QSA_EHIP;
+    }
+    const TopkGeom g = make_geom(scores, ld_scores, nq, n_blocks, block_size, width, active_blocks,
+                                 cell_ids, counts);
+    return run_topk(g, plan, workspace, (hipStream_t)stream, opt);
+}
+
+} // extern "C"

@@ -1,0 +1,95 @@
+// qsa_internal.h - host/device argument blocks and host-side planning shared
+// by the library's translation units (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qsa.h"
+
+namespace qsa {
+
+// ---------------------------------------------------------------- top-k
+constexpr int kSplitThreads = 512;        // workgroup of the exact split kernel
+constexpr int kOneReadThreads = 512;      // one workgroup per query on the one-read path
+constexpr int kOneReadF4 = 8;             // float4 loads in flight per thread and batch
+constexpr int kOneReadBatch = kOneReadThreads * kOneReadF4 * 4;  // blocks streamed per batch
+constexpr int kChunkBound = 4104;         // split chunks: the fewest of at most this many blocks
+constexpr int kMinChunk = 64;
+constexpr int kMaxChunk = 15360;          // keeps a chunk's keys under 60 KB of LDS
+constexpr int kStageBLdsWords = 15360;    // stage B keeps up to this many candidate keys in LDS
+constexpr int kOneReadCap = 4096;         // one-read candidate cap per query (blocks)
+constexpr int kOneReadMinBlocks = 28672;  // prompt calls from this many blocks ...
+constexpr int kOneReadMinQueries = 64;    // ... and this many queries use the one-read path
+constexpr int kSampleStride = 32;
+
+// Workspace layout of the split (byte offsets, 256-byte aligned).
+struct TopkLayout {
+    size_t split_tickets;   // u32 [nq]
+    size_t split_meta;      // u32 [nq][n_chunks][2] : {count, chunk threshold}
+    size_t split_keys;      // u32 [nq][cand_stride]
+    size_t split_blocks;    // i32 [nq][cand_stride]
+    size_t bytes;
+};
+
+struct TopkPlan {
+    qsa_topk_plan pub;
+    int64_t cand_stride;    // split candidates per query, a multiple of 4
+    TopkLayout lay;
+};
+
+// Fills `plan`; returns QSA_OK or the argument error.
+qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int32_t width,
+                          qsa_call call, const qsa_options *opt, TopkPlan &plan);
+
+struct TopkGeom {
+    const float *scores;
+    int64_t ld;
+    int32_t nq;
+    int32_t n_blocks;
+    int32_t bs;
+    int32_t width;
+    const int32_t *active;  // nullable
+    int32_t *ids;
+    int32_t *counts;        // nullable
+    int32_t vec4;           // rows are 16-byte aligned (float4 loads allowed)
+};
+
+struct SplitArgs {
+    TopkGeom g;
+    uint32_t *tickets;
+    uint32_t *meta;
+    uint32_t *cand_keys;
+    int32_t *cand_blocks;
+    int64_t cand_stride;
+    int32_t chunk;
+    int32_t n_chunks;
+    int32_t lds_words;      // dynamic LDS words available (>= chunk)
+};
+
+struct OneReadArgs {
+    TopkGeom g;
+    int32_t mode;           // QSA_SAMPLE_STRIDE / QSA_SAMPLE_LINES
+    int32_t force_flag;     // take the exact path for every query
+};
+
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+hipError_t launch_split(const SplitArgs &a, hipStream_t s);
+hipError_t launch_oneread(const OneReadArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------- scores
+struct ScoreArgs {
+    const float *q;
+    const float *k;
+    const float *w;
+    float *scores;
+    int64_t ld;
+    int32_t nq;
+    int32_t heads;
+    int32_t n_blocks;
+};
+
+hipError_t launch_scores(const ScoreArgs &a, hipStream_t s);
+
+} // namespace qsa

@@ -1,0 +1,470 @@
+// topk_device.h - workgroup-level building blocks of the block top-k on gfx950.
+//
+// The selection rule (Strata pull #3987, section Approach; Strata pull #2093
+// "sm_75: the prompt path's top-k with one full read of the scores", section
+// Beschreibung): with r the number of blocks a selection touches, T is the
+// r-th largest block key; blocks above T are taken, then blocks equal to T in
+// ascending block order until r blocks are taken; the last block taken in
+// that order may contribute only part of its cells. Everything below works on
+// 32-bit order-preserving block keys, so "largest" is plain unsigned order.
+//
+// Radix select. Each digit is a 256-bin LDS histogram of the keys still in
+// play, and a scan of the bins from the top picks the bin holding the target
+// rank (the pages pick every digit with a parallel scan of 256 bins, Strata
+// pull #3987, section Approach). Digits are taken over the keys' actual range
+// [min, max] rather than at fixed bit positions: the first digit splits the
+// range into 256 equal bins, the next splits the chosen bin, and so on, so a
+// narrow range needs fewer passes and equal keys need none.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+constexpr int kWave = 64;
+
+// Order-preserving image of an FP32 key in uint32 (-0.0 folded onto +0.0).
+__device__ __forceinline__ uint32_t key_of(float f)
+{
+    uint32_t b = __float_as_uint(f);
+    b = (b == 0x80000000u) ? 0u : b;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x / kWave); }
+
+__device__ __forceinline__ uint64_t lanes_below()
+{
+    const int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ uint32_t count_below(uint64_t mask)
+{
+    return (uint32_t)__popcll(mask & lanes_below());
+}
+
+// ------------------------------------------------------------ wave scans
+// Row shifts within rows of 16 lanes, then the row broadcasts join rows
+// (0,1) and (2,3), then the two halves. Lanes a shift does not reach add 0.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x)
+{
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t x)
+{
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false));
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(x), 63);
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_max(x), 63);
+}
+
+// min(a) == ~max(~a)
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) { return ~wave_max(~x); }
+
+// Workgroup barrier that orders LDS only: global loads stay in flight across
+// it (a full __syncthreads() would first wait for every outstanding load).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ void lds_add(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Count digit d in an LDS histogram. Digits are taken over the keys' own range
+// (see radix_select_range), so even skewed keys spread over many bins; equal
+// keys never reach a histogram at all.
+__device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t d) { lds_add(&hist[d], 1u); }
+
+// ------------------------------------------------------------ key sources
+// Keys in LDS (16-byte aligned array).
+struct LdsKeys {
+    const uint32_t *p;
+    static constexpr bool vec = true;
+    __device__ __forceinline__ uint4 load4(int i) const { return *reinterpret_cast<const uint4 *>(p + i); }
+    __device__ __forceinline__ uint32_t load1(int i) const { return p[i]; }
+};
+
+// Keys already mapped, in global memory (16-byte aligned array).
+struct GlobalKeys {
+    const uint32_t *p;
+    static constexpr bool vec = true;
+    __device__ __forceinline__ uint4 load4(int i) const { return *reinterpret_cast<const uint4 *>(p + i); }
+    __device__ __forceinline__ uint32_t load1(int i) const { return p[i]; }
+};
+
+// FP32 block scores in global memory, mapped on load. `aligned` means p is
+// 16-byte aligned, so float4 loads are allowed at multiples of 4.
+struct RowKeys {
+    const float *p;
+    bool aligned;
+    static constexpr bool vec = false;  // decided at run time through `aligned`
+    __device__ __forceinline__ uint4 load4(int i) const
+    {
+        const float4 f = *reinterpret_cast<const float4 *>(p + i);
+        return make_uint4(key_of(f.x), key_of(f.y), key_of(f.z), key_of(f.w));
+    }
+    __device__ __forceinline__ uint32_t load1(int i) const { return key_of(p[i]); }
+};
+
+template <class Src>
+__device__ __forceinline__ bool vector_ok(const Src &s)
+{
+    if constexpr (Src::vec)
+        return true;
+    else
+        return s.aligned;
+}
+
+// f(key) for every key 0..n-1, in no particular order; vector loads, four
+// in flight per thread.
+template <int NT, class Src, class F>
+__device__ __forceinline__ void for_each_key(const Src &src, int n, F f)
+{
+    if (vector_ok(src)) {
+        const int n4 = n >> 2;
+        int i = threadIdx.x;
+        for (; i + 3 * NT < n4; i += 4 * NT) {
+            const uint4 a = src.load4(4 * i), b = src.load4(4 * (i + NT));
+            const uint4 c = src.load4(4 * (i + 2 * NT)), d = src.load4(4 * (i + 3 * NT));
+            f(a.x); f(a.y); f(a.z); f(a.w);
+            f(b.x); f(b.y); f(b.z); f(b.w);
+            f(c.x); f(c.y); f(c.z); f(c.w);
+            f(d.x); f(d.y); f(d.z); f(d.w);
+        }
+        for (; i < n4; i += NT) {
+            const uint4 a = src.load4(4 * i);
+            f(a.x); f(a.y); f(a.z); f(a.w);
+        }
+        for (int j = (n4 << 2) + (int)threadIdx.x; j < n; j += NT)
+            f(src.load1(j));
+    } else {
+        int j = threadIdx.x;
+        for (; j + 3 * NT < n; j += 4 * NT) {
+            const uint32_t a = src.load1(j), b = src.load1(j + NT), c = src.load1(j + 2 * NT),
+                           d = src.load1(j + 3 * NT);
+            f(a); f(b); f(c); f(d);
+        }
+        for (; j < n; j += NT)
+            f(src.load1(j));
+    }
+}
+
+// ------------------------------------------------------------ shared state
+constexpr int kDigitBits = 8;
+constexpr int kBins = 1 << kDigitBits;
+
+template <int NT>
+struct SelectShared {
+    static constexpr int NW = NT / kWave;
+    alignas(16) uint32_t hist[3][kBins];  // rotating: fill one, pick from it, clear the one before
+    uint32_t red[2][NW];
+    uint32_t wave_ties[NW];
+    uint32_t wave_gts[NW];
+};
+
+template <int NT>
+__device__ __forceinline__ void clear_hists(SelectShared<NT> &sh)
+{
+    uint4 *h = reinterpret_cast<uint4 *>(&sh.hist[0][0]);
+    for (int i = threadIdx.x; i < 3 * kBins / 4; i += NT)
+        h[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+template <int NT>
+__device__ __forceinline__ void clear_hist(SelectShared<NT> &sh, int which)
+{
+    uint4 *h = reinterpret_cast<uint4 *>(&sh.hist[which][0]);
+    for (int i = threadIdx.x; i < kBins / 4; i += NT)
+        h[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Workgroup min and max of a per-thread pair (all threads call).
+template <int NT>
+__device__ __forceinline__ void wg_minmax(uint32_t lo, uint32_t hi, SelectShared<NT> &sh, uint32_t &mn,
+                                          uint32_t &mx)
+{
+    constexpr int NW = NT / kWave;
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane_id() == 0) {
+        sh.red[0][wave_id()] = lo;
+        sh.red[1][wave_id()] = hi;
+    }
+    lds_barrier();
+    mn = 0xFFFFFFFFu;
+    mx = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        mn = min(mn, sh.red[0][w]);
+        mx = max(mx, sh.red[1][w]);
+    }
+    lds_barrier();
+}
+
+// The bin of a histogram (highest bin first) that holds rank r, and the count
+// of everything in higher bins. Every wave computes it on its own: lane l owns
+// the kBins/64 bins just below the (kBins/64)*l highest.
+__device__ __forceinline__ void wave_pick(const uint32_t *hist, uint32_t r, uint32_t &bin, uint32_t &higher)
+{
+    constexpr int PL = kBins / kWave;
+    const int lane = lane_id();
+    const int lo_bin = kBins - PL * (lane + 1);
+    uint32_t c[PL];
+#pragma unroll
+    for (int i = 0; i < PL / 4; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(hist + lo_bin + 4 * i);
+        c[4 * i] = v.x; c[4 * i + 1] = v.y; c[4 * i + 2] = v.z; c[4 * i + 3] = v.w;
+    }
+    uint32_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+        mine += c[i];
+    const uint32_t before = wave_incl_sum(mine) - mine;
+    const uint64_t hit = __ballot(before < r && r <= before + mine);
+    const int L = hit ? (int)__ffsll((unsigned long long)hit) - 1 : 0;
+    // In the lane that holds rank r, walk its bins from the highest down.
+    uint32_t cum = before, my_bin = 0, my_higher = 0;
+#pragma unroll
+    for (int i = PL - 1; i >= 0; --i) {
+        if (cum < r && r <= cum + c[i]) {
+            my_bin = (uint32_t)(lo_bin + i);
+            my_higher = cum;
+        }
+        cum += c[i];
+    }
+    bin = (uint32_t)__builtin_amdgcn_readlane((int)my_bin, L);
+    higher = (uint32_t)__builtin_amdgcn_readlane((int)my_higher, L);
+}
+
+// Rank-th largest key (1-based, 1 <= rank <= n) among keys 0..n-1 of src, and
+// the number of keys strictly above it. [kmin, kmax] must bound the keys.
+// All threads call. The histograms must be zero on entry and a barrier must
+// separate this call from any earlier one; they are zero again on return.
+// Each pass costs one barrier: every wave picks the digit itself, and the
+// histogram filled two passes earlier is cleared while the next one fills.
+template <int NT, class Src>
+__device__ __forceinline__ void radix_select_range(const Src &src, int n, uint32_t rank, uint32_t kmin,
+                                                   uint32_t kmax, SelectShared<NT> &sh, uint32_t &T,
+                                                   uint32_t &n_above)
+{
+    uint32_t lo = kmin, span = kmax - kmin, r = rank, above = 0;
+    int p = 0;
+    while (span != 0) {
+        const int bits = 32 - __clz(span);
+        const int s = bits > kDigitBits ? bits - kDigitBits : 0;
+        uint32_t *hist = sh.hist[p % 3];
+        for_each_key<NT>(src, n, [&](uint32_t k) {
+            const uint32_t sub = k - lo;
+            if (sub <= span)
+                hist_add(hist, sub >> s);
+        });
+        lds_barrier();
+        uint32_t d, h;
+        wave_pick(hist, r, d, h);
+        clear_hist<NT>(sh, (p + 2) % 3);  // filled two passes ago; every wave has read it
+        r -= h;
+        above += h;
+        lo += d << s;
+        span = (s == 0) ? 0u : min(span - (d << s), (1u << s) - 1u);
+        ++p;
+    }
+    if (p > 0) {
+        lds_barrier();  // every wave is done reading the last histogram
+        clear_hist<NT>(sh, (p - 1) % 3);
+    }
+    T = lo;
+    n_above = above;
+}
+
+// Min and max key of src[0..n).
+template <int NT, class Src>
+__device__ __forceinline__ void key_range(const Src &src, int n, SelectShared<NT> &sh, uint32_t &mn, uint32_t &mx)
+{
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for_each_key<NT>(src, n, [&](uint32_t k) {
+        lo = min(lo, k);
+        hi = max(hi, k);
+    });
+    wg_minmax<NT>(lo, hi, sh, mn, mx);
+}
+
+template <int NT, class Src>
+__device__ __forceinline__ void radix_select(const Src &src, int n, uint32_t rank, SelectShared<NT> &sh,
+                                             uint32_t &T, uint32_t &n_above)
+{
+    uint32_t mn, mx;
+    key_range<NT>(src, n, sh, mn, mx);
+    radix_select_range<NT>(src, n, rank, mn, mx, sh, T, n_above);
+}
+
+// Walk items 0..n-1 in order and take every item with key > T plus the first
+// `tie_budget` items with key == T (tie_budget >= 1). Taken item i gets the
+// output slot `first` (a running sum of weights: `unit` per taken item, except
+// the last taken tie, which weighs `last_unit`), and emit(i, first, weight) is
+// called for it. Waves own contiguous ranges of items, walked 256 at a time
+// (four per lane); the only workgroup exchange is one round of per-wave counts.
+template <int NT, class Src, class Emit>
+__device__ __forceinline__ void ordered_take(const Src &src, int n, uint32_t T, uint32_t tie_budget, uint32_t unit,
+                             uint32_t last_unit, SelectShared<NT> &sh, Emit emit)
+{
+    constexpr int NW = NT / kWave;
+    constexpr int STEP = 4 * kWave;
+    const int lane = lane_id(), wid = wave_id();
+    const int per_wave = ((n + NW - 1) / NW + STEP - 1) / STEP * STEP;
+    const int lo = wid * per_wave;
+    const int hi = min(n, lo + per_wave);
+    const bool vec = vector_ok(src);
+
+    auto load = [&](int base, uint32_t k[4], bool ok[4]) {
+        const int i0 = base + 4 * lane;
+        if (vec && i0 + 3 < hi) {
+            const uint4 v = src.load4(i0);
+            k[0] = v.x; k[1] = v.y; k[2] = v.z; k[3] = v.w;
+            ok[0] = ok[1] = ok[2] = ok[3] = true;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                ok[j] = i0 + j < hi;
+                k[j] = ok[j] ? src.load1(i0 + j) : 0u;
+            }
+        }
+    };
+
+    uint32_t ties = 0, gts = 0;
+    for (int base = lo; base < hi; base += STEP) {
+        uint32_t k[4];
+        bool ok[4];
+        load(base, k, ok);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            ties += (uint32_t)__popcll(__ballot(ok[j] && k[j] == T));
+            gts += (uint32_t)__popcll(__ballot(ok[j] && k[j] > T));
+        }
+    }
+    if (lane == 0) {
+        sh.wave_ties[wid] = ties;
+        sh.wave_gts[wid] = gts;
+    }
+    lds_barrier();
+    uint32_t ties_before = 0, taken_before = 0;
+    for (int v = 0; v < wid; ++v) {
+        const uint32_t t = sh.wave_ties[v];
+        const uint32_t left = tie_budget > ties_before ? tie_budget - ties_before : 0u;
+        taken_before += sh.wave_gts[v] + (t < left ? t : left);
+        ties_before += t;
+    }
+    lds_barrier();
+    if (gts == 0 && ties_before >= tie_budget)
+        return;  // nothing of this wave's range is taken
+
+    const uint32_t shortfall = unit - last_unit;
+    bool short_seen = ties_before >= tie_budget;
+    for (int base = lo; base < hi; base += STEP) {
+        uint32_t k[4];
+        bool ok[4];
+        load(base, k, ok);
+        bool tie[4], take[4], shrt[4];
+        uint32_t own_ties = 0, own_take = 0;
+        uint32_t tie_rank[4], take_rank[4];
+        bool own_short_before[4];
+        bool any_short_before = false;
+        uint64_t tie_m[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            tie[j] = ok[j] && k[j] == T;
+            tie_m[j] = __ballot(tie[j]);
+        }
+        uint32_t lanes_ties = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            lanes_ties += count_below(tie_m[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            tie_rank[j] = ties_before + lanes_ties + own_ties;
+            own_ties += tie[j] ? 1u : 0u;
+            take[j] = ok[j] && (k[j] > T || (tie[j] && tie_rank[j] < tie_budget));
+            shrt[j] = tie[j] && tie_rank[j] == tie_budget - 1;
+        }
+        uint64_t take_m[4], short_m = 0;
+        uint32_t lanes_take = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            take_m[j] = __ballot(take[j]);
+            lanes_take += count_below(take_m[j]);
+            short_m |= __ballot(shrt[j]);
+        }
+        const bool short_in_lower_lanes = (short_m & lanes_below()) != 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            take_rank[j] = taken_before + lanes_take + own_take;
+            own_take += take[j] ? 1u : 0u;
+            own_short_before[j] = any_short_before;
+            any_short_before = any_short_before || shrt[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (take[j]) {
+                const bool after = short_seen || short_in_lower_lanes || own_short_before[j];
+                emit(base + 4 * lane + j, unit * take_rank[j] - (after ? shortfall : 0u),
+                     shrt[j] ? last_unit : unit);
+            }
+        }
+        uint32_t step_take = 0, step_ties = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            step_take += (uint32_t)__popcll(take_m[j]);
+            step_ties += (uint32_t)__popcll(tie_m[j]);
+        }
+        taken_before += step_take;
+        ties_before += step_ties;
+        short_seen = short_seen || short_m != 0;
+    }
+}
+
+// Device-scope release of this workgroup's global writes, then one ticket.
+// Returns true (in every thread) for the workgroup that arrives last.
+__device__ __forceinline__ bool last_to_arrive(uint32_t *ticket, uint32_t expected, uint32_t *s_flag)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        const uint32_t prev =
+            __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_flag[0] = (prev == expected - 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    const bool last = s_flag[0] != 0;
+    if (last)
+        __threadfence();
+    return last;
+}
+
+} // namespace qsa

@@ -1,0 +1,434 @@
+// topk_kernels.hip - block top-k kernels for gfx950.
+//
+//  * split_kernel: the exact chunked split (Strata pull #3987, section
+//    Approach). Stage A: one workgroup per (query, chunk) loads the chunk's
+//    block keys into LDS once and keeps the chunk's own top-r blocks (block
+//    order) as candidates. A query's selection restricted to one chunk is a
+//    prefix of that chunk's order, so the candidates hold every selected
+//    block. Stage B: the workgroup that finishes a query last (an atomic
+//    ticket, no waiting) runs the same rule over the candidates and writes the
+//    cells. With one chunk the single workgroup writes the cells directly.
+//    Used for decode calls (few queries: the chunks fill the GPU) and for
+//    prompt calls too small for the one-read path.
+//
+//  * oneread_kernel: the prompt path with one read of the scores (Strata
+//    pull #2093 "sm_75: the prompt path's top-k with one full read of the
+//    scores", section Beschreibung), one workgroup per query. A lower bound LB
+//    is the KS-th largest of a sample of the query's block keys
+//    (KS = 2*r/32 + 16); one streaming pass keeps the blocks with key >= LB in
+//    LDS, in block order. If they hold at least the selection's cells, the
+//    threshold is >= LB and the rule over the candidates gives the exact
+//    selection. Otherwise (too few cells, or more candidates than the cap) the
+//    query takes the exact path over its whole row in the same workgroup; the
+//    key range found during the streaming pass seeds it, so equal keys finish
+//    without further histograms. Workgroups never talk to each other, so no
+//    device-scope fences are needed.
+#include "qsa_internal.h"
+#include "topk_device.h"
+
+namespace qsa {
+
+namespace {
+
+struct QuerySel {
+    int n_vis;      // visible blocks
+    int wq;         // cells selected: min(width, n_vis * bs)
+    int r;          // blocks the selection touches: ceil(wq / bs)
+    int last_unit;  // cells of the last block in (key desc, block asc) order
+};
+
+__device__ __forceinline__ QuerySel query_sel(const TopkGeom &g, int q)
+{
+    QuerySel s;
+    int nv = g.n_blocks;
+    if (g.active) {
+        const int a = g.active[q];
+        nv = a < 0 ? 0 : (a > g.n_blocks ? g.n_blocks : a);
+    }
+    s.n_vis = nv;
+    const int64_t cells = (int64_t)nv * g.bs;
+    s.wq = (int)(cells < g.width ? cells : (int64_t)g.width);
+    s.r = (s.wq + g.bs - 1) / g.bs;
+    s.last_unit = s.r > 0 ? s.wq - g.bs * (s.r - 1) : 0;
+    return s;
+}
+
+template <int NT>
+__device__ __forceinline__ void write_empty(const TopkGeom &g, int q)
+{
+    int32_t *out = g.ids + (int64_t)q * g.width;
+    for (int p = threadIdx.x; p < g.width; p += NT)
+        out[p] = -1;
+    if (g.counts && threadIdx.x == 0)
+        g.counts[q] = 0;
+}
+
+// Cells of one taken block: `cnt` consecutive ids from block*bs at out[first].
+__device__ __forceinline__ void write_cells(int32_t *out, uint32_t first, uint32_t cnt, int32_t cell0,
+                                            uint32_t limit)
+{
+    if (cnt == 4 && (first & 3u) == 0 && first + 4 <= limit) {
+        *reinterpret_cast<int4 *>(out + first) = make_int4(cell0, cell0 + 1, cell0 + 2, cell0 + 3);
+        return;
+    }
+    for (uint32_t j = 0; j < cnt; ++j)
+        if (first + j < limit)
+            out[first + j] = cell0 + (int32_t)j;
+}
+
+// Final selection over n candidate blocks (n >= qs.r) that contain the
+// query's whole selection, in ascending block order: writes the cells, the -1
+// tail and the count. Histograms must be zero on entry.
+template <int NT, class Src, class BlockAt>
+__device__ __forceinline__ void select_cells(const Src &src, int n, const QuerySel &qs, BlockAt block_at, const TopkGeom &g,
+                             int q, SelectShared<NT> &sh, bool have_range = false, uint32_t kmin = 0,
+                             uint32_t kmax = 0)
+{
+    int32_t *out = g.ids + (int64_t)q * g.width;
+    uint32_t T, above;
+    if (have_range)
+        radix_select_range<NT>(src, n, (uint32_t)qs.r, kmin, kmax, sh, T, above);
+    else
+        radix_select<NT>(src, n, (uint32_t)qs.r, sh, T, above);
+    const int bs = g.bs;
+    const uint32_t limit = (uint32_t)qs.wq;
+    ordered_take<NT>(src, n, T, (uint32_t)qs.r - above, (uint32_t)bs, (uint32_t)qs.last_unit, sh,
+                     [&](int i, uint32_t first, uint32_t cnt) {
+                         write_cells(out, first, cnt, block_at(i) * bs, limit);
+                     });
+    for (int p = qs.wq + (int)threadIdx.x; p < g.width; p += NT)
+        out[p] = -1;
+    if (g.counts && threadIdx.x == 0)
+        g.counts[q] = qs.wq;
+}
+
+// Keys of blocks [b0, b0+n) of row q into LDS.
+template <int NT>
+__device__ __forceinline__ void load_keys_lds(const TopkGeom &g, int q, int b0, int n, uint32_t *s)
+{
+    const float *row = g.scores + (int64_t)q * g.ld + b0;
+    if (g.vec4 && (b0 & 3) == 0) {
+        const float4 *r4 = reinterpret_cast<const float4 *>(row);
+        const int n4 = (n + 3) >> 2;
+        for (int i = threadIdx.x; i < n4; i += NT) {
+            const float4 v = r4[i];
+            const int b = i << 2;
+            if (b + 3 < n) {
+                *reinterpret_cast<uint4 *>(s + b) = make_uint4(key_of(v.x), key_of(v.y), key_of(v.z), key_of(v.w));
+            } else {
+                s[b] = key_of(v.x);
+                if (b + 1 < n) s[b + 1] = key_of(v.y);
+                if (b + 2 < n) s[b + 2] = key_of(v.z);
+            }
+        }
+    } else {
+        for (int i = threadIdx.x; i < n; i += NT)
+            s[i] = key_of(row[i]);
+    }
+}
+
+} // namespace
+
+// ------------------------------------------------------------------ split
+template <int NT>
+__global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint32_t s_keys[];
+    __shared__ SelectShared<NT> sh;
+    __shared__ uint32_t s_flag[1];
+    const TopkGeom g = a.g;
+    const int q = blockIdx.y;
+    const int c = blockIdx.x;
+    const QuerySel qs = query_sel(g, q);
+    if (qs.r == 0) {
+        if (c == 0)
+            write_empty<NT>(g, q);
+        return;
+    }
+    const int nchq = (qs.n_vis + a.chunk - 1) / a.chunk;
+    if (c >= nchq)
+        return;
+    const int b0 = c * a.chunk;
+    const int nc = min(a.chunk, qs.n_vis - b0);
+    clear_hists<NT>(sh);
+    load_keys_lds<NT>(g, q, b0, nc, s_keys);
+    lds_barrier();
+    const LdsKeys lds{s_keys};
+
+    if (nchq == 1) {
+        select_cells<NT>(lds, nc, qs, [&](int i) { return b0 + i; }, g, q, sh);
+        return;
+    }
+
+    // Stage A: this chunk's top-r blocks in block order.
+    const int cap_q = min(qs.r, a.chunk);
+    uint32_t *ckey = a.cand_keys + (int64_t)q * a.cand_stride + (int64_t)c * cap_q;
+    int32_t *cblk = a.cand_blocks + (int64_t)q * a.cand_stride + (int64_t)c * cap_q;
+    uint32_t T = 0, budget = (uint32_t)nc;  // a chunk no larger than r is kept whole
+    if (nc > qs.r) {
+        uint32_t above;
+        radix_select<NT>(lds, nc, (uint32_t)qs.r, sh, T, above);
+        budget = (uint32_t)qs.r - above;
+    }
+    ordered_take<NT>(lds, nc, T, budget, 1u, 1u, sh, [&](int i, uint32_t pos, uint32_t) {
+        if (pos < (uint32_t)cap_q) {
+            ckey[pos] = s_keys[i];
+            cblk[pos] = b0 + i;
+        }
+    });
+    if (threadIdx.x == 0) {
+        uint32_t *m = a.meta + ((int64_t)q * a.n_chunks + c) * 2;
+        m[0] = (uint32_t)min(nc, qs.r);
+        m[1] = T;
+    }
+    if (!last_to_arrive(&a.tickets[q], (uint32_t)nchq, s_flag))
+        return;
+
+    // Stage B: candidates of all chunks, contiguous and in block order (every
+    // chunk but the last is full).
+    const int last_n = min(qs.r, qs.n_vis - (nchq - 1) * a.chunk);
+    const int total = (nchq - 1) * cap_q + last_n;
+    const uint32_t *gkey = a.cand_keys + (int64_t)q * a.cand_stride;
+    const int32_t *gblk = a.cand_blocks + (int64_t)q * a.cand_stride;
+    auto blk = [&](int i) { return gblk[i]; };
+    if (total <= a.lds_words) {
+        const int n4 = total >> 2;
+        for (int i = threadIdx.x; i < n4; i += NT)
+            *reinterpret_cast<uint4 *>(s_keys + 4 * i) = *reinterpret_cast<const uint4 *>(gkey + 4 * i);
+        for (int i = (n4 << 2) + (int)threadIdx.x; i < total; i += NT)
+            s_keys[i] = gkey[i];
+        lds_barrier();
+        select_cells<NT>(lds, total, qs, blk, g, q, sh);
+    } else {
+        select_cells<NT>(GlobalKeys{gkey}, total, qs, blk, g, q, sh);
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&a.tickets[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------ one read
+// Each wave streams its own contiguous eighth of the row, F4 float4 loads per
+// lane and step, two steps in flight, and keeps its candidates in its own LDS
+// region; there is no workgroup barrier while the row streams.
+template <int NT, int F4, bool VEC>
+__global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
+{
+    constexpr int NW = NT / kWave;
+    constexpr int STEP = kWave * 4 * F4;       // blocks a wave reads per step
+    constexpr int WCAP = kOneReadCap / NW;     // candidates a wave may keep
+    __shared__ __attribute__((aligned(16))) uint32_t s_wkey[kOneReadCap];  // sample, then per-wave candidates
+    __shared__ __attribute__((aligned(16))) int32_t s_wblk[kOneReadCap];
+    __shared__ __attribute__((aligned(16))) uint32_t s_ckey[kOneReadCap];  // candidates in block order
+    __shared__ __attribute__((aligned(16))) int32_t s_cblk[kOneReadCap];
+    __shared__ SelectShared<NT> sh;
+    __shared__ uint32_t s_wcnt[NW];
+
+    const TopkGeom g = a.g;
+    const int q = blockIdx.x;
+    const QuerySel qs = query_sel(g, q);
+    if (qs.r == 0) {
+        write_empty<NT>(g, q);
+        return;
+    }
+    const int n = qs.n_vis;
+    const float *row = g.scores + (int64_t)q * g.ld;
+    const int lane = lane_id(), wid = wave_id();
+
+    // Sample of the block keys for the bound.
+    int ns;
+    if (a.mode == QSA_SAMPLE_STRIDE) {
+        ns = (n + kSampleStride - 1) / kSampleStride;
+    } else {
+        const int full = n / 1024, rem = n % 1024;
+        ns = full * kSampleStride + min(rem, kSampleStride);
+    }
+    ns = min(ns, kOneReadCap);
+    const uint32_t ks = 2u * (uint32_t)qs.r / kSampleStride + 16u;
+    const bool all_cells = (int64_t)n * g.bs <= (int64_t)qs.wq;
+    const bool use_bound = !all_cells && !a.force_flag && (uint32_t)ns >= ks;
+
+    // This wave's blocks [w0, w1).
+    const int per_wave = ((n + NW - 1) / NW + 255) / 256 * 256;
+    const int w0 = min(n, wid * per_wave);
+    const int w1 = min(n, w0 + per_wave);
+    const int nsteps = (w1 - w0 + STEP - 1) / STEP;
+
+    // Every load below is unconditional: a lane with nothing to read re-reads
+    // block 0 (the row has at least one visible block here) and the value is
+    // ignored. A load under a branch makes the compiler lose count of the
+    // loads in flight and wait for all of them before the next use.
+    auto load_step = [&](int st, float4 (&v)[F4]) {
+#pragma unroll
+        for (int j = 0; j < F4; ++j) {
+            const int i0 = w0 + st * STEP + j * 4 * kWave + 4 * lane;
+            if constexpr (VEC) {
+                v[j] = *reinterpret_cast<const float4 *>(row + (i0 < w1 ? i0 : 0));
+            } else {
+                v[j].x = row[i0 < w1 ? i0 : 0];
+                v[j].y = row[i0 + 1 < w1 ? i0 + 1 : 0];
+                v[j].z = row[i0 + 2 < w1 ? i0 + 2 : 0];
+                v[j].w = row[i0 + 3 < w1 ? i0 + 3 : 0];
+            }
+        }
+    };
+
+    // The sample goes into registers first (SPT per thread), then the first
+    // two steps of the stream are issued behind it.
+    constexpr int SPT = kOneReadCap / NT;
+    float smp[SPT];
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+        const int i = (int)threadIdx.x + u * NT;
+        const int ic = (use_bound && i < ns) ? i : 0;
+        const int b = a.mode == QSA_SAMPLE_STRIDE ? ic * kSampleStride
+                                                  : (ic / kSampleStride) * 1024 + (ic % kSampleStride);
+        smp[u] = row[b];
+    }
+    clear_hists<NT>(sh);
+    float4 A[F4], B[F4];
+    load_step(0, A);  // in flight while the bound is found
+    load_step(1, B);
+    if (use_bound) {
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int i = (int)threadIdx.x + u * NT;
+            if (i < ns)
+                s_wkey[i] = key_of(smp[u]);
+        }
+    }
+    lds_barrier();
+    uint32_t bound = 0;  // 0 keeps every block
+    if (use_bound) {
+        uint32_t above;
+        radix_select<NT>(LdsKeys{s_wkey}, ns, ks, sh, bound, above);
+    }
+    lds_barrier();  // the sample is no longer read
+
+    // One read: keep blocks with key >= bound, in block order, up to WCAP.
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    uint32_t wcnt = 0;  // wave-uniform
+    uint32_t *wkey = s_wkey + wid * WCAP;
+    int32_t *wblk = s_wblk + wid * WCAP;
+    auto consume = [&](int st, const float4 (&v)[F4]) {
+#pragma unroll
+        for (int j = 0; j < F4; ++j) {
+            const int i0 = w0 + st * STEP + j * 4 * kWave + 4 * lane;
+            const float f[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+            uint32_t key[4];
+            bool keep[4];
+            uint32_t below = 0, step = 0;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bool valid = i0 + s < w1;
+                key[s] = key_of(f[s]);
+                if (valid) {
+                    kmin = min(kmin, key[s]);
+                    kmax = max(kmax, key[s]);
+                }
+                keep[s] = valid && key[s] >= bound;
+                const uint64_t m = __ballot(keep[s]);
+                below += count_below(m);
+                step += (uint32_t)__popcll(m);
+            }
+            if (step == 0)
+                continue;
+            uint32_t pos = wcnt + below;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (keep[s]) {
+                    if (pos < (uint32_t)WCAP) {
+                        wkey[pos] = key[s];
+                        wblk[pos] = i0 + s;
+                    }
+                    ++pos;
+                }
+            }
+            wcnt += step;
+        }
+    };
+    // Branch-free body (a step past the wave's range reads block 0 and is
+    // ignored); the last pair is peeled so no load is left in flight at the end.
+    int st = 0;
+    for (; st + 2 < nsteps; st += 2) {
+        consume(st, A);
+        load_step(st + 2, A);
+        consume(st + 1, B);
+        load_step(st + 3, B);
+    }
+    consume(st, A);
+    consume(st + 1, B);
+    if (lane == 0)
+        s_wcnt[wid] = wcnt;
+    uint32_t row_min, row_max;
+    wg_minmax<NT>(kmin, kmax, sh, row_min, row_max);  // its barrier also publishes s_wcnt
+
+    uint32_t before = 0, total = 0;
+    bool over = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t c = s_wcnt[w];
+        before += w < wid ? c : 0u;
+        total += c;
+        over = over || c > (uint32_t)WCAP;
+    }
+    if (!a.force_flag && !over && (uint64_t)total * (uint64_t)g.bs >= (uint64_t)qs.wq) {
+        for (int i = lane; i < (int)wcnt; i += kWave) {
+            s_ckey[before + i] = wkey[i];
+            s_cblk[before + i] = wblk[i];
+        }
+        lds_barrier();
+        select_cells<NT>(LdsKeys{s_ckey}, (int)total, qs, [&](int i) { return s_cblk[i]; }, g, q, sh);
+        return;
+    }
+    // Flagged: the exact rule over the whole row, read from global memory.
+    select_cells<NT>(RowKeys{row, VEC}, n, qs, [&](int i) { return i; }, g, q, sh, true, row_min, row_max);
+}
+
+// ------------------------------------------------------------------- utility
+__global__ void zero_kernel(uint32_t *p, size_t n)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        p[i] = 0u;
+}
+
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s)
+{
+    const size_t n = bytes / 4;
+    if (n == 0)
+        return hipSuccess;
+    const size_t blocks = (n + 255) / 256;
+    const unsigned grid = (unsigned)(blocks < 4096 ? blocks : 4096);
+    hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, (uint32_t *)p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_split(const SplitArgs &a, hipStream_t s)
+{
+    static bool lds_limit_raised = false;
+    if (!lds_limit_raised) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&split_kernel<kSplitThreads>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 kStageBLdsWords * 4);
+        if (e != hipSuccess)
+            return e;
+        lds_limit_raised = true;
+    }
+    const dim3 grid((unsigned)a.n_chunks, (unsigned)a.g.nq);
+    hipLaunchKernelGGL(split_kernel<kSplitThreads>, grid, dim3(kSplitThreads), (size_t)a.lds_words * 4, s,
+                       a);
+    return hipGetLastError();
+}
+
+hipError_t launch_oneread(const OneReadArgs &a, hipStream_t s)
+{
+    if (a.g.vec4)
+        hipLaunchKernelGGL((oneread_kernel<kOneReadThreads, kOneReadF4, true>), dim3((unsigned)a.g.nq),
+                           dim3(kOneReadThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((oneread_kernel<kOneReadThreads, kOneReadF4, false>), dim3((unsigned)a.g.nq),
+                           dim3(kOneReadThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+} // namespace qsa

@@ -1,0 +1,149 @@
+"""Host-side checks of libqsa.so that need no GPU: the library loads, exports
+every function include/qsa.h declares, plans the dispatch, and rejects bad
+arguments before launching anything."""
+import ctypes
+
+import pytest
+
+import sparse_attention_block_scores_amd as qsa
+from sparse_attention_block_scores_amd import _binding as B
+
+FAKE = 1 << 20  # an aligned, never dereferenced stand-in for a device pointer
+
+
+def test_library_exports_every_declared_function():
+    names = qsa.declared_functions()
+    assert set(names) >= {"qsa_block_scores", "qsa_block_topk", "qsa_select", "qsa_status_str",
+                          "qsa_topk_workspace_bytes", "qsa_topk_plan_get", "qsa_workspace_init"}
+    L = qsa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert qsa.status_str(0) == "ok"
+    assert "workspace" in qsa.status_str(3)
+    assert qsa.status_str(99) == "unknown status"
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIBRARY", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="build"):
+        B.lib()
+
+
+def test_dispatch_decode_uses_split_with_page_chunks():
+    p = qsa.topk_plan(3, 64512, 4, 2048, "decode")
+    assert p["path"] == qsa.PATH_SPLIT
+    assert p["r_blocks"] == 512
+    assert p["n_chunks"] == 16 and p["chunk_blocks"] == 4032  # fewest chunks of <= 4,104 blocks
+    assert p["stage_b_lds"] == 1
+
+
+def test_dispatch_prompt_threshold_and_ks():
+    big = qsa.topk_plan(256, 32768, 4, 2048, "prompt")
+    small = qsa.topk_plan(256, 28671, 4, 2048, "prompt")
+    assert big["path"] == qsa.PATH_ONEREAD and small["path"] == qsa.PATH_SPLIT
+    assert big["ks"] == 2 * 512 // 32 + 16 == 48
+    assert big["cap"] == 4096 and big["sample_stride"] == 32
+    assert qsa.topk_plan(16, 32768, 4, 2048, "prompt")["path"] == qsa.PATH_SPLIT  # few queries
+
+
+def test_forced_paths_and_workspace_growth():
+    o = qsa.make_options(topk_path=qsa.PATH_SPLIT, chunk_blocks=64)
+    p = qsa.topk_plan(8, 10000, 4, 2048, "prompt", o)
+    assert p["path"] == qsa.PATH_SPLIT and p["n_chunks"] == (10000 + 63) // 64
+    assert qsa.topk_workspace_bytes(8, 10000, 4, 2048, "prompt", o) > \
+        qsa.topk_workspace_bytes(8, 10000, 4, 2048, "prompt")
+    p = qsa.topk_plan(2, 5000, 3, 100, "decode", qsa.make_options(topk_path=qsa.PATH_ONEREAD))
+    assert p["path"] == qsa.PATH_ONEREAD and p["r_blocks"] == 34
+
+
+@pytest.mark.parametrize("nb", [1, 4104, 4105, 10240, 16384, 32768, 64512, 100000])
+def test_split_chunks_are_the_fewest_of_at_most_4104(nb):
+    p = qsa.topk_plan(3, nb, 4, 2048, "decode")
+    assert p["n_chunks"] == -(-nb // 4104)
+    assert p["chunk_blocks"] <= 4104 and p["chunk_blocks"] % 4 == 0
+    assert p["chunk_blocks"] * p["n_chunks"] >= nb
+
+
+def test_width_larger_than_context():
+    p = qsa.topk_plan(1, 10, 4, 2048, "decode")
+    assert p["r_blocks"] == 10
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(chunk_blocks=63), B.QSA_EINVAL),
+    (dict(chunk_blocks=66), B.QSA_EINVAL),
+    (dict(chunk_blocks=15364), B.QSA_EINVAL),
+    (dict(topk_path=7), B.QSA_EINVAL),
+    (dict(sample=9), B.QSA_EINVAL),
+    (dict(oneread_blocks=2048), B.QSA_EUNSUPPORTED),
+    (dict(reserved=(1, 0, 0)), B.QSA_EINVAL),
+])
+def test_bad_options_rejected(kw, status):
+    with pytest.raises(B.QSAError) as e:
+        qsa.topk_plan(4, 1000, 4, 64, "decode", qsa.make_options(**kw))
+    assert e.value.status == status
+
+
+def _topk(L, **over):
+    a = dict(scores=FAKE, ld=1000, nq=4, n_blocks=1000, bs=4, width=64, call=0, active=None, ids=FAKE,
+             counts=None, ws=FAKE, ws_bytes=1 << 30, stream=None, opt=None)
+    a.update(over)
+    return L.qsa_block_topk(a["scores"], a["ld"], a["nq"], a["n_blocks"], a["bs"], a["width"], a["call"],
+                            a["active"], a["ids"], a["counts"], a["ws"], a["ws_bytes"], a["stream"],
+                            a["opt"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ld=999), B.QSA_EINVAL),
+    (dict(bs=0), B.QSA_EINVAL),
+    (dict(width=0), B.QSA_EINVAL),
+    (dict(nq=-1), B.QSA_EINVAL),
+    (dict(call=2), B.QSA_EINVAL),
+    (dict(active=FAKE), B.QSA_EINVAL),          # decode calls carry no active count
+    (dict(scores=FAKE + 2), B.QSA_EINVAL),      # misaligned
+    (dict(ids=None), B.QSA_EINVAL),
+    (dict(n_blocks=1 << 29, ld=1 << 29, bs=4), B.QSA_EINVAL),  # cell ids would overflow int32
+    (dict(ws=None), B.QSA_EWORKSPACE),
+    (dict(ws=FAKE + 64), B.QSA_EWORKSPACE),
+    (dict(ws_bytes=16), B.QSA_EWORKSPACE),
+    (dict(nq=70000), B.QSA_EUNSUPPORTED),
+])
+def test_topk_argument_errors(over, status):
+    assert _topk(qsa.lib(), **over) == status
+
+
+def test_topk_zero_queries_is_a_no_op():
+    assert _topk(qsa.lib(), nq=0, scores=None, ids=None, ws=None) == B.QSA_OK
+
+
+def _scores(L, **over):
+    a = dict(q=FAKE, k=FAKE, w=FAKE, s=FAKE, ld=100, nq=2, h=8, d=128, nb=100)
+    a.update(over)
+    return L.qsa_block_scores(a["q"], a["k"], a["w"], a["s"], a["ld"], a["nq"], a["h"], a["d"], a["nb"],
+                              None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d=64), B.QSA_EUNSUPPORTED),
+    (dict(h=65), B.QSA_EUNSUPPORTED),
+    (dict(h=0), B.QSA_EINVAL),
+    (dict(ld=99), B.QSA_EINVAL),
+    (dict(q=FAKE + 4), B.QSA_EINVAL),   # q rows are read 16 bytes at a time
+    (dict(k=None), B.QSA_EINVAL),
+])
+def test_score_argument_errors(over, status):
+    assert _scores(qsa.lib(), **over) == status
+
+
+def test_scores_empty_is_a_no_op():
+    assert _scores(qsa.lib(), nq=0) == B.QSA_OK
+    assert _scores(qsa.lib(), nb=0) == B.QSA_OK
+
+
+def test_plan_struct_size_matches_header():
+    assert ctypes.sizeof(B.Plan) == 12 * 4 + 8
+    assert ctypes.sizeof(B.Options) == 8 * 4

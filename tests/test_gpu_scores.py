@@ -1,0 +1,83 @@
+"""GPU block scores against the FP64 oracle, within the score tolerance:
+|gpu - oracle| <= 1e-4 * max(|oracle|, 1% of the query's mean |oracle|)
+(score definition: Strata pull #1091 'qsa_select: FP32 tiled block scores
+below sm_80', section What). Where a test uses weights of both signs, the
+scale is sum_h |w_h| relu(dot_h) instead of |oracle| (heads can cancel)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_block_scores_amd as qsa
+import synth
+from qsa_testutil import assert_scores_close, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gpu_scores(q, k, w, ld=None, fill=None):
+    nq, nb = q.shape[0], k.shape[0]
+    ld = nb if ld is None else ld
+    s = torch.full((nq, ld), float("nan") if fill is None else fill, dtype=torch.float32, device="cuda")
+    qsa.block_scores(to_dev(q), to_dev(k), to_dev(w), scores=s)
+    torch.cuda.synchronize()
+    return s.cpu().numpy()
+
+
+def test_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "scores_hand.json")))
+    q = np.zeros((g["nq"], g["heads"], g["head_dim"]), np.float32)
+    k = np.zeros((g["n_blocks"], g["head_dim"]), np.float32)
+    for a, h, d, v in g["q_entries"]:
+        q[a, h, d] = v
+    for b, d, v in g["k_entries"]:
+        k[b, d] = v
+    say("scores hand example")
+    s = gpu_scores(q, k, np.array(g["w"], np.float32))
+    assert s.tolist() == g["scores"]
+
+
+@pytest.mark.parametrize("heads", [1, 2, 3, 4, 5, 8, 12, 16, 17, 31, 32, 33, 48, 64])
+@pytest.mark.parametrize("nq,n_blocks", [(1, 1), (3, 1000), (7, 4133), (19, 2049)])
+def test_shapes(heads, nq, n_blocks):
+    tag = f"gpu/scores/{heads}/{nq}/{n_blocks}"
+    q = synth.normal(tag + "/q", (nq, heads, 128))
+    k = synth.normal(tag + "/k", (n_blocks, 128))
+    w = synth.uniform01(tag + "/w", (nq, heads)) * 2.0 - 0.5  # some negative weights too
+    ld = n_blocks + 3
+    say(f"scores heads={heads} nq={nq} nb={n_blocks}")
+    s = gpu_scores(q, k, w, ld=ld, fill=7.0)
+    ref = oracle.block_scores(q, k, w)
+    terms = oracle.block_scores(np.abs(q), np.abs(k), np.abs(w))
+    assert_scores_close(s[:, :n_blocks], ref, f"h={heads} nq={nq} nb={n_blocks}", terms)
+    assert (s[:, n_blocks:] == 7.0).all(), "columns past n_blocks were written"
+
+
+def test_decode_select_shapes_full():
+    for wl in (synth.c1(), synth.c3()):
+        q, k, w = wl.tensors()
+        say(f"scores {wl.name} full")
+        s = gpu_scores(q, k, w)
+        ref = oracle.block_scores(q, k, w)
+        assert_scores_close(s, ref, wl.name)
+
+
+def test_prompt_select_shape_sampled():
+    wl = synth.c5()
+    q, k, w = wl.tensors()
+    say("scores C5 full size")
+    s = gpu_scores(q, k, w)
+    qi = synth.integers("gpu/scores/C5/qi", 20000, 0, wl.nq - 1).astype(np.int32)
+    bi = synth.integers("gpu/scores/C5/bi", 20000, 0, wl.n_blocks - 1).astype(np.int32)
+    ref = oracle.block_scores_at(q, k, w, qi, bi)
+    rows = oracle.block_scores(q[:2], k, w[:2])  # two whole rows for the per-row floor
+    floor = 0.01 * np.abs(rows).mean()
+    tol = 1e-4 * np.maximum(np.abs(ref), floor)
+    err = np.abs(s[qi, bi].astype(np.float64) - ref)
+    assert (err <= tol).all(), f"worst {np.max(err / tol):.3f} x tolerance"
+    assert_scores_close(s[:2], rows, "C5 rows 0-1")

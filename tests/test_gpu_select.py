@@ -1,0 +1,56 @@
+"""qsa_select end to end (scores then top-k in one call).
+
+Two checks per query:
+ * the ids equal the oracle's top-k of the very scores the GPU produced
+   (bit-exact: same FP32 inputs to both selections);
+ * against the oracle's FP64 scores the ids may differ only in blocks whose
+   score lies within twice the score tolerance of the threshold score.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_block_scores_amd as qsa
+import synth
+from qsa_testutil import assert_ids_equal, assert_scores_close, check_selection_near_threshold, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_select(wl, active=None, options=None):
+    q, k, w = wl.tensors()
+    act = None if active is None else to_dev(active)
+    say(f"select {wl.name} nq={wl.nq} nb={wl.n_blocks} {wl.call}")
+    scores, ids, counts = qsa.select(to_dev(q), to_dev(k), to_dev(w), wl.block_size, wl.width, wl.call,
+                                     active=act, options=options)
+    torch.cuda.synchronize()
+    return (q, k, w), scores.cpu().numpy(), ids.cpu().numpy(), counts.cpu().numpy()
+
+
+@pytest.mark.parametrize("make", [synth.c1, synth.c3])
+def test_decode_select(make):
+    wl = make()
+    (q, k, w), s, ids, counts = run_select(wl)
+    assert_ids_equal((ids, counts), oracle.topk_sort(s, wl.n_blocks, wl.block_size, wl.width), wl.name)
+    ref = oracle.block_scores(q, k, w)
+    assert_scores_close(s, ref, wl.name)
+    for i in range(wl.nq):
+        check_selection_near_threshold(ids[i], counts[i], ref[i], wl.block_size, wl.width, f"{wl.name} q{i}")
+
+
+def test_prompt_select_full_size():
+    wl = synth.c5()
+    (q, k, w), s, ids, counts = run_select(wl, active=np.full(wl.nq, wl.n_blocks, np.int32))
+    assert_ids_equal((ids, counts), oracle.topk_sort(s, wl.n_blocks, wl.block_size, wl.width), wl.name)
+    for i in (0, 131, 255):
+        ref = oracle.block_scores(q[i:i + 1], k, w[i:i + 1])[0]
+        check_selection_near_threshold(ids[i], counts[i], ref, wl.block_size, wl.width, f"C5 q{i}")
+
+
+def test_prompt_select_random_active_counts():
+    wl = synth.SelectWorkload("gpu/sel/active", nq=40, heads=16, n_blocks=40000, block_size=4, width=2048,
+                              call="prompt")
+    active = synth.integers("gpu/sel/active/n", wl.nq, 0, wl.n_blocks).astype(np.int32)
+    (q, k, w), s, ids, counts = run_select(wl, active=active)
+    assert_ids_equal((ids, counts), oracle.topk_sort(s, wl.n_blocks, 4, 2048, active), "active")

@@ -1,0 +1,173 @@
+"""GPU block top-k against the oracle: ids and counts bit-exact on every path.
+
+The GPU top-k is fed the very FP32 scores the oracle sorts, so any difference
+is a bug (Strata pull #2093 'sm_75: the prompt path's top-k with one full read
+of the scores', section Beschreibung, and Strata pull #3987, section Approach:
+every kernel there returns the reference's ids).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_block_scores_amd as qsa
+import synth
+from qsa_testutil import assert_ids_equal, device, gpu_topk, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+PATHS = {
+    "auto": None,
+    "split": dict(topk_path=qsa.PATH_SPLIT),
+    "split64": dict(topk_path=qsa.PATH_SPLIT, chunk_blocks=64),
+    "split516": dict(topk_path=qsa.PATH_SPLIT, chunk_blocks=516),
+    "oneread_lines": dict(topk_path=qsa.PATH_ONEREAD, sample=qsa.SAMPLE_LINES),
+    "oneread_stride": dict(topk_path=qsa.PATH_ONEREAD, sample=qsa.SAMPLE_STRIDE),
+    "fallback": dict(topk_path=qsa.PATH_ONEREAD, force_fallback=1),
+    "fallback64": dict(topk_path=qsa.PATH_ONEREAD, force_fallback=1, chunk_blocks=64),
+}
+
+
+def _opts(name):
+    kw = PATHS[name]
+    return None if kw is None else qsa.make_options(**kw)
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_hand_cases(path):
+    g = json.load(open(os.path.join(GOLDEN, "topk_hand.json")))
+    for case in g["cases"]:
+        keys = np.array([case["keys"]], np.float32)
+        call = "decode" if case["active"] is None else "prompt"
+        say(f"hand {case['name']} path={path}")
+        ids, counts = gpu_topk(keys, keys.shape[1], case["block_size"], case["width"], call,
+                               active=case["active"], options=_opts(path))
+        assert ids[0].tolist() == case["ids"], case["name"]
+        assert counts[0] == case["count"], case["name"]
+
+
+def _keys(tag, variant, nq, n_blocks, ld):
+    s = np.full((nq, ld), synth.PAD_VALUE, np.float32)
+    if variant == "normal":
+        s[:, :n_blocks] = synth.normal(tag, (nq, n_blocks))
+    elif variant == "q64":
+        s[:, :n_blocks] = synth.quantize64(synth.normal(tag, (nq, n_blocks)))
+    elif variant == "equal":
+        s[:, :n_blocks] = 1.0
+    elif variant == "few":  # few distinct values, both signed zeros, negatives
+        vals = np.array([-2.0, -0.0, 0.0, 0.5, 3.0], np.float32)
+        s[:, :n_blocks] = vals[synth.integers(tag, nq * n_blocks, 0, 4).reshape(nq, n_blocks)]
+    elif variant == "sorted":
+        s[:, :n_blocks] = np.arange(n_blocks, dtype=np.float32)[None, :] * 0.25
+    return s
+
+
+def _cases():
+    rng = np.random.default_rng(20261202)
+    variants = ["normal", "q64", "equal", "few", "sorted"]
+    sizes = [1, 2, 7, 64, 65, 333, 1000, 4104, 4105, 9000, 30000]
+    out = []
+    for i in range(72):
+        nb = int(sizes[i % len(sizes)])
+        bs = int(rng.choice([1, 2, 3, 4, 4, 4, 7]))
+        width = int(rng.choice([1, 5, 64, 100, 777, 2047, 2048]))
+        nq = int(rng.choice([1, 3, 5]))
+        variant = variants[i % len(variants)]
+        call = "prompt" if i % 3 else "decode"
+        path = list(PATHS)[i % len(PATHS)]
+        out.append(pytest.param(i, nb, bs, width, nq, variant, call, path,
+                                id=f"{i}-nb{nb}-bs{bs}-w{width}-nq{nq}-{variant}-{call}-{path}"))
+    return out
+
+
+@pytest.mark.parametrize("i,n_blocks,bs,width,nq,variant,call,path", _cases())
+def test_random_cases(i, n_blocks, bs, width, nq, variant, call, path):
+    ld = n_blocks + (i % 5)  # odd strides take the scalar-load path
+    s = _keys(f"gpu/topk/{i}", variant, nq, n_blocks, ld)
+    active = None
+    if call == "prompt":
+        active = synth.integers(f"gpu/topk/{i}/active", nq, -2, n_blocks + 3).astype(np.int32)
+        active[0] = n_blocks
+    say(f"case {i} nb={n_blocks} bs={bs} w={width} nq={nq} {variant} {call} {path}")
+    got = gpu_topk(s, n_blocks, bs, width, call, active=active, options=_opts(path))
+    exp = oracle.topk_sort(s, n_blocks, bs, width, active)
+    assert_ids_equal(got, exp, f"case {i}")
+
+
+@pytest.mark.parametrize("n_blocks", synth.C2_BLOCKS)
+def test_decode_contexts_full_size(n_blocks):
+    wl = synth.c2(n_blocks)
+    s = wl.scores()
+    exp = oracle.topk_sort(s, n_blocks, wl.block_size, wl.width)
+    for path in ("auto", "split64", "oneread_lines"):
+        say(f"C2 decode nb={n_blocks} path={path}")
+        got = gpu_topk(s, n_blocks, wl.block_size, wl.width, "decode", options=_opts(path))
+        assert_ids_equal(got, exp, f"C2 nb={n_blocks} {path}")
+
+
+@pytest.mark.parametrize("variant", ["continuous", "q64", "equal"])
+@pytest.mark.parametrize("n_blocks", synth.C4_BLOCKS)
+def test_prompt_contexts_full_size(n_blocks, variant):
+    wl = synth.c4(n_blocks, variant)
+    s = wl.scores()
+    active = np.full(wl.nq, n_blocks, np.int32)
+    rows = np.arange(0, wl.nq, 17)  # the oracle redoes 16 of the 256 queries
+    exp = oracle.topk_sort(s[rows], n_blocks, wl.block_size, wl.width, active[rows])
+    for path in ("auto", "split"):
+        say(f"C4 prompt nb={n_blocks} {variant} path={path}")
+        got = gpu_topk(s, n_blocks, wl.block_size, wl.width, "prompt", active=active, options=_opts(path))
+        assert_ids_equal(got, exp, f"C4 nb={n_blocks} {variant} {path}", rows=rows)
+        assert (got[1] == wl.width).all()
+
+
+def test_workspace_reused_across_calls_of_different_sizes():
+    dev = device()
+    need = max(qsa.topk_workspace_bytes(8, 20000, 4, 2048, "prompt"),
+               qsa.topk_workspace_bytes(8, 20000, 4, 2048, "decode"),
+               qsa.topk_workspace_bytes(8, 40000, 4, 2048, "prompt"))
+    ws = qsa.workspace(need, dev)
+    for j, (nq, nb, call) in enumerate([(8, 20000, "decode"), (3, 9000, "decode"), (8, 40000, "prompt"),
+                                        (5, 20000, "prompt"), (8, 20000, "decode"), (8, 40000, "prompt")]):
+        s = _keys(f"gpu/reuse/{j}", "normal", nq, nb, nb)
+        say(f"reuse call {j} nq={nq} nb={nb} {call}")
+        got = gpu_topk(s, nb, 4, 2048, call, ws=ws)
+        assert_ids_equal(got, oracle.topk_sort(s, nb, 4, 2048), f"reuse {j}")
+
+
+def test_two_streams_with_separate_workspaces():
+    dev = device()
+    a = _keys("gpu/streams/a", "normal", 4, 50000, 50000)
+    b = _keys("gpu/streams/b", "q64", 4, 50000, 50000)
+    sa, sb = to_dev(a), to_dev(b)
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    ws = [qsa.workspace(qsa.topk_workspace_bytes(4, 50000, 4, 2048, "prompt"), dev) for _ in streams]
+    torch.cuda.synchronize()
+    say("two streams")
+    outs = []
+    for s, st, w in ((sa, streams[0], ws[0]), (sb, streams[1], ws[1])):
+        with torch.cuda.stream(st):
+            outs.append(qsa.block_topk(s, 50000, 4, 2048, "prompt", ws=w, stream=st))
+    torch.cuda.synchronize()
+    for (ids, counts), src in zip(outs, (a, b)):
+        assert_ids_equal((ids.cpu().numpy(), counts.cpu().numpy()), oracle.topk_sort(src, 50000, 4, 2048),
+                         "streams")
+
+
+def test_misaligned_rows_and_empty_contexts():
+    dev = device()
+    base = _keys("gpu/misaligned", "normal", 3, 5001, 5003)
+    full = to_dev(np.concatenate([np.zeros((3, 1), np.float32), base], axis=1))
+    view = full[:, 1:]  # rows start 4 bytes past a 16-byte boundary
+    say("misaligned view")
+    ids, counts = qsa.block_topk(view, 5001, 4, 2048, "decode")
+    got = (ids.cpu().numpy(), counts.cpu().numpy())
+    assert_ids_equal(got, oracle.topk_sort(base, 5001, 4, 2048), "misaligned")
+    say("zero blocks")
+    s = to_dev(np.zeros((2, 4), np.float32))
+    ids, counts = qsa.block_topk(s, 0, 4, 16, "decode")
+    assert (ids.cpu().numpy() == -1).all() and (counts.cpu().numpy() == 0).all()
