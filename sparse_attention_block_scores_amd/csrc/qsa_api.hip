@@ -89,6 +89,8 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
         path = (call == QSA_PROMPT && n_blocks >= kOneReadMinBlocks && nq >= kOneReadMinQueries)
                    ? QSA_PATH_ONEREAD
                    : QSA_PATH_SPLIT;
+    if (path == QSA_PATH_ONEREAD && n_blocks > kOneReadMaxBatches * kOneReadBatch)
+        path = QSA_PATH_SPLIT;  // per-batch counts of longer rows do not fit the LDS table
     p.path = path;
 
     // Workspace: only the split keeps candidates in global memory.

@@ -32,6 +32,12 @@ __device__ __forceinline__ uint32_t key_of(float f)
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// The float with that image (inverse of key_of; -0.0 comes back as +0.0).
+__device__ __forceinline__ float float_of(uint32_t key)
+{
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x / kWave); }
 

@@ -30,6 +30,8 @@ namespace qsa {
 
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 struct QuerySel {
     int n_vis;      // visible blocks
     int wq;         // cells selected: min(width, n_vis * bs)
@@ -207,21 +209,27 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
 }
 
 // ------------------------------------------------------------------ one read
-// Each wave streams its own contiguous eighth of the row, F4 float4 loads per
-// lane and step, two steps in flight, and keeps its candidates in its own LDS
-// region; there is no workgroup barrier while the row streams.
+// The workgroup streams the row in batches of NW*STEP blocks; within a batch
+// wave w reads the w-th STEP-block slice, F4 float4 loads per lane, two
+// batches in flight. Each wave keeps its candidates in its own LDS region and
+// counts them per batch, so there is no workgroup barrier while the row
+// streams; at the end the per-(batch, wave) counts put them in block order.
 template <int NT, int F4, bool VEC>
 __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
 {
     constexpr int NW = NT / kWave;
-    constexpr int STEP = kWave * 4 * F4;       // blocks a wave reads per step
+    constexpr int STEP = kWave * 4 * F4;       // blocks a wave reads per batch
+    constexpr int BATCH = NW * STEP;           // blocks the workgroup reads per batch
     constexpr int WCAP = kOneReadCap / NW;     // candidates a wave may keep
     __shared__ __attribute__((aligned(16))) uint32_t s_wkey[kOneReadCap];  // sample, then per-wave candidates
     __shared__ __attribute__((aligned(16))) int32_t s_wblk[kOneReadCap];
     __shared__ __attribute__((aligned(16))) uint32_t s_ckey[kOneReadCap];  // candidates in block order
     __shared__ __attribute__((aligned(16))) int32_t s_cblk[kOneReadCap];
     __shared__ SelectShared<NT> sh;
-    __shared__ uint32_t s_wcnt[NW];
+    __shared__ uint32_t s_bcnt[kOneReadMaxBatches * NW];  // candidates per (batch, wave), batch-major
+    __shared__ uint32_t s_bsrc[kOneReadMaxBatches * NW];  // where they start in the wave's own list
+    __shared__ uint32_t s_bdst[kOneReadMaxBatches * NW];  // where they go in block order
+    __shared__ uint32_t s_wtot[NW];
 
     const TopkGeom g = a.g;
     const int q = blockIdx.x;
@@ -246,34 +254,31 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     const uint32_t ks = 2u * (uint32_t)qs.r / kSampleStride + 16u;
     const bool all_cells = (int64_t)n * g.bs <= (int64_t)qs.wq;
     const bool use_bound = !all_cells && !a.force_flag && (uint32_t)ns >= ks;
-
-    // This wave's blocks [w0, w1).
-    const int per_wave = ((n + NW - 1) / NW + 255) / 256 * 256;
-    const int w0 = min(n, wid * per_wave);
-    const int w1 = min(n, w0 + per_wave);
-    const int nsteps = (w1 - w0 + STEP - 1) / STEP;
+    const int nbatch = (n + BATCH - 1) / BATCH;  // <= kOneReadMaxBatches (the dispatch sees to it)
 
     // Every load below is unconditional: a lane with nothing to read re-reads
     // block 0 (the row has at least one visible block here) and the value is
     // ignored. A load under a branch makes the compiler lose count of the
     // loads in flight and wait for all of them before the next use.
-    auto load_step = [&](int st, float4 (&v)[F4]) {
+    auto load_batch = [&](int b, float4 (&v)[F4]) {
 #pragma unroll
         for (int j = 0; j < F4; ++j) {
-            const int i0 = w0 + st * STEP + j * 4 * kWave + 4 * lane;
+            const int i0 = b * BATCH + wid * STEP + j * 4 * kWave + 4 * lane;
             if constexpr (VEC) {
-                v[j] = *reinterpret_cast<const float4 *>(row + (i0 < w1 ? i0 : 0));
+                // Streamed once: nontemporal loads keep it from displacing cached data.
+                const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + (i0 < n ? i0 : 0)));
+                v[j] = make_float4(t[0], t[1], t[2], t[3]);
             } else {
-                v[j].x = row[i0 < w1 ? i0 : 0];
-                v[j].y = row[i0 + 1 < w1 ? i0 + 1 : 0];
-                v[j].z = row[i0 + 2 < w1 ? i0 + 2 : 0];
-                v[j].w = row[i0 + 3 < w1 ? i0 + 3 : 0];
+                v[j].x = row[i0 < n ? i0 : 0];
+                v[j].y = row[i0 + 1 < n ? i0 + 1 : 0];
+                v[j].z = row[i0 + 2 < n ? i0 + 2 : 0];
+                v[j].w = row[i0 + 3 < n ? i0 + 3 : 0];
             }
         }
     };
 
     // The sample goes into registers first (SPT per thread), then the first
-    // two steps of the stream are issued behind it.
+    // two batches of the stream are issued behind it.
     constexpr int SPT = kOneReadCap / NT;
     float smp[SPT];
 #pragma unroll
@@ -286,8 +291,8 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     }
     clear_hists<NT>(sh);
     float4 A[F4], B[F4];
-    load_step(0, A);  // in flight while the bound is found
-    load_step(1, B);
+    load_batch(0, A);  // two batches in flight while the bound is found
+    load_batch(1, B);
     if (use_bound) {
 #pragma unroll
         for (int u = 0; u < SPT; ++u) {
@@ -305,27 +310,25 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     lds_barrier();  // the sample is no longer read
 
     // One read: keep blocks with key >= bound, in block order, up to WCAP.
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    // key >= bound is tested as f >= float_of(bound): the key map preserves
+    // order and equates -0.0 with +0.0, exactly as float comparison does.
+    const float fbound = use_bound ? float_of(bound) : -__builtin_inff();
     uint32_t wcnt = 0;  // wave-uniform
     uint32_t *wkey = s_wkey + wid * WCAP;
     int32_t *wblk = s_wblk + wid * WCAP;
-    auto consume = [&](int st, const float4 (&v)[F4]) {
+    auto consume = [&](int b, const float4 (&v)[F4]) {
+        const int step0 = b * BATCH + wid * STEP;
+        const bool full = step0 + STEP <= n;  // wave-uniform
+        const uint32_t start = wcnt;
 #pragma unroll
         for (int j = 0; j < F4; ++j) {
-            const int i0 = w0 + st * STEP + j * 4 * kWave + 4 * lane;
+            const int i0 = step0 + j * 4 * kWave + 4 * lane;
             const float f[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-            uint32_t key[4];
             bool keep[4];
             uint32_t below = 0, step = 0;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const bool valid = i0 + s < w1;
-                key[s] = key_of(f[s]);
-                if (valid) {
-                    kmin = min(kmin, key[s]);
-                    kmax = max(kmax, key[s]);
-                }
-                keep[s] = valid && key[s] >= bound;
+                keep[s] = f[s] >= fbound && (full || i0 + s < n);
                 const uint64_t m = __ballot(keep[s]);
                 below += count_below(m);
                 step += (uint32_t)__popcll(m);
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             for (int s = 0; s < 4; ++s) {
                 if (keep[s]) {
                     if (pos < (uint32_t)WCAP) {
-                        wkey[pos] = key[s];
+                        wkey[pos] = key_of(f[s]);
                         wblk[pos] = i0 + s;
                     }
                     ++pos;
@@ -345,43 +348,65 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             }
             wcnt += step;
         }
+        if (lane == 0 && b < kOneReadMaxBatches) {
+            s_bcnt[b * NW + wid] = wcnt - start;
+            s_bsrc[b * NW + wid] = start;
+        }
     };
-    // Branch-free body (a step past the wave's range reads block 0 and is
-    // ignored); the last pair is peeled so no load is left in flight at the end.
-    int st = 0;
-    for (; st + 2 < nsteps; st += 2) {
-        consume(st, A);
-        load_step(st + 2, A);
-        consume(st + 1, B);
-        load_step(st + 3, B);
+    // Branch-free body (a batch past the row reads block 0 and is ignored);
+    // the last pair is peeled so no load is left in flight at the end.
+    int b = 0;
+    for (; b + 2 < nbatch; b += 2) {
+        consume(b, A);
+        load_batch(b + 2, A);
+        consume(b + 1, B);
+        load_batch(b + 3, B);
     }
-    consume(st, A);
-    consume(st + 1, B);
+    consume(b, A);
+    consume(b + 1, B);
     if (lane == 0)
-        s_wcnt[wid] = wcnt;
-    uint32_t row_min, row_max;
-    wg_minmax<NT>(kmin, kmax, sh, row_min, row_max);  // its barrier also publishes s_wcnt
+        s_wtot[wid] = wcnt;
+    lds_barrier();
 
-    uint32_t before = 0, total = 0;
+    // Totals and overflow.
+    uint32_t total = 0;
     bool over = false;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        const uint32_t c = s_wcnt[w];
-        before += w < wid ? c : 0u;
+        const uint32_t c = s_wtot[w];
         total += c;
         over = over || c > (uint32_t)WCAP;
     }
     if (!a.force_flag && !over && (uint64_t)total * (uint64_t)g.bs >= (uint64_t)qs.wq) {
-        for (int i = lane; i < (int)wcnt; i += kWave) {
-            s_ckey[before + i] = wkey[i];
-            s_cblk[before + i] = wblk[i];
+        // Destinations in block order: an exclusive scan over the (batch, wave)
+        // table, batch-major, 64 entries per wave step; wave 0 writes it.
+        const int E = nbatch * NW;
+        if (wid == 0) {
+            uint32_t carry = 0;
+            for (int e0 = 0; e0 < E; e0 += kWave) {
+                const int e = e0 + lane;
+                const uint32_t c = e < E ? s_bcnt[e] : 0u;
+                const uint32_t incl = wave_incl_sum(c);
+                if (e < E)
+                    s_bdst[e] = carry + incl - c;
+                carry += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+            }
+        }
+        lds_barrier();
+        for (int bb = 0; bb < nbatch; ++bb) {
+            const int e = bb * NW + wid;
+            const uint32_t cnt = s_bcnt[e], src = s_bsrc[e], dst = s_bdst[e];
+            for (uint32_t i = (uint32_t)lane; i < cnt; i += kWave) {
+                s_ckey[dst + i] = wkey[src + i];
+                s_cblk[dst + i] = wblk[src + i];
+            }
         }
         lds_barrier();
         select_cells<NT>(LdsKeys{s_ckey}, (int)total, qs, [&](int i) { return s_cblk[i]; }, g, q, sh);
         return;
     }
     // Flagged: the exact rule over the whole row, read from global memory.
-    select_cells<NT>(RowKeys{row, VEC}, n, qs, [&](int i) { return i; }, g, q, sh, true, row_min, row_max);
+    select_cells<NT>(RowKeys{row, VEC}, n, qs, [&](int i) { return i; }, g, q, sh);
 }
 
 // ------------------------------------------------------------------- utility
