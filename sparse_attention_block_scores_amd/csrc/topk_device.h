@@ -47,9 +47,10 @@ __device__ __forceinline__ uint64_t lanes_below()
     return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
+// Set bits of a wave mask in the lanes below this one (v_mbcnt).
 __device__ __forceinline__ uint32_t count_below(uint64_t mask)
 {
-    return (uint32_t)__popcll(mask & lanes_below());
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
 // ------------------------------------------------------------ wave scans

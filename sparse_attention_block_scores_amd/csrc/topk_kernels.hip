@@ -210,7 +210,7 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
 
 // ------------------------------------------------------------------ one read
 // The workgroup streams the row in batches of NW*STEP blocks; within a batch
-// wave w reads the w-th STEP-block slice, F4 float4 loads per lane, two
+// wave w reads the w-th STEP-block slice, F4 float4 loads per lane, three
 // batches in flight. Each wave keeps its candidates in its own LDS region and
 // counts them per batch, so there is no workgroup barrier while the row
 // streams; at the end the per-(batch, wave) counts put them in block order.
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     };
 
     // The sample goes into registers first (SPT per thread), then the first
-    // two batches of the stream are issued behind it.
+    // three batches of the stream are issued behind it.
     constexpr int SPT = kOneReadCap / NT;
     float smp[SPT];
 #pragma unroll
@@ -290,9 +290,10 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         smp[u] = row[b];
     }
     clear_hists<NT>(sh);
-    float4 A[F4], B[F4];
-    load_batch(0, A);  // two batches in flight while the bound is found
+    float4 A[F4], B[F4], C[F4];
+    load_batch(0, A);  // three batches in flight while the bound is found
     load_batch(1, B);
+    load_batch(2, C);
     if (use_bound) {
 #pragma unroll
         for (int u = 0; u < SPT; ++u) {
@@ -325,16 +326,37 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             const int i0 = step0 + j * 4 * kWave + 4 * lane;
             const float f[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
             bool keep[4];
-            uint32_t below = 0, step = 0;
+            uint64_t m[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 keep[s] = f[s] >= fbound && (full || i0 + s < n);
-                const uint64_t m = __ballot(keep[s]);
-                below += count_below(m);
-                step += (uint32_t)__popcll(m);
+                m[s] = __ballot(keep[s]);
             }
-            if (step == 0)
+            const uint64_t any = m[0] | m[1] | m[2] | m[3];
+            if (any == 0)
                 continue;
+            const uint64_t two = (m[0] & (m[1] | m[2] | m[3])) | (m[1] & (m[2] | m[3])) | (m[2] & m[3]);
+            if (two == 0) {
+                // Common case: no lane keeps more than one of its four keys, so
+                // a lane's slot is the number of keeping lanes below it.
+                if (keep[0] || keep[1] || keep[2] || keep[3]) {
+                    const int sel = keep[0] ? 0 : (keep[1] ? 1 : (keep[2] ? 2 : 3));
+                    const float x = keep[0] ? f[0] : (keep[1] ? f[1] : (keep[2] ? f[2] : f[3]));
+                    const uint32_t pos = wcnt + count_below(any);
+                    if (pos < (uint32_t)WCAP) {
+                        wkey[pos] = key_of(x);
+                        wblk[pos] = i0 + sel;
+                    }
+                }
+                wcnt += (uint32_t)__popcll(any);
+                continue;
+            }
+            uint32_t below = 0, step = 0;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                below += count_below(m[s]);
+                step += (uint32_t)__popcll(m[s]);
+            }
             uint32_t pos = wcnt + below;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -354,16 +376,19 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         }
     };
     // Branch-free body (a batch past the row reads block 0 and is ignored);
-    // the last pair is peeled so no load is left in flight at the end.
+    // the last three are peeled so no load is left in flight at the end.
     int b = 0;
-    for (; b + 2 < nbatch; b += 2) {
+    for (; b + 3 < nbatch; b += 3) {
         consume(b, A);
-        load_batch(b + 2, A);
+        load_batch(b + 3, A);
         consume(b + 1, B);
-        load_batch(b + 3, B);
+        load_batch(b + 4, B);
+        consume(b + 2, C);
+        load_batch(b + 5, C);
     }
     consume(b, A);
     consume(b + 1, B);
+    consume(b + 2, C);
     if (lane == 0)
         s_wtot[wid] = wcnt;
     lds_barrier();
