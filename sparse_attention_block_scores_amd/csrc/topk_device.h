@@ -39,7 +39,8 @@ __device__ __forceinline__ float float_of(uint32_t key)
 }
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
-__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x / kWave); }
+// Wave index in the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)); }
 
 __device__ __forceinline__ uint64_t lanes_below()
 {
@@ -271,29 +272,40 @@ __device__ __forceinline__ void wave_pick(const uint32_t *hist, uint32_t r, uint
     higher = (uint32_t)__builtin_amdgcn_readlane((int)my_higher, L);
 }
 
+// Shift of the first digit over a key range of the given span (span > 0).
+__device__ __forceinline__ int first_digit_shift(uint32_t span)
+{
+    const int bits = 32 - __clz(span);
+    return bits > kDigitBits ? bits - kDigitBits : 0;
+}
+
 // Rank-th largest key (1-based, 1 <= rank <= n) among keys 0..n-1 of src, and
 // the number of keys strictly above it. [kmin, kmax] must bound the keys.
 // All threads call. The histograms must be zero on entry and a barrier must
 // separate this call from any earlier one; they are zero again on return.
 // Each pass costs one barrier: every wave picks the digit itself, and the
 // histogram filled two passes earlier is cleared while the next one fills.
+// With first_filled the caller has already counted the first digit
+// ((k - kmin) >> first_digit_shift(kmax - kmin)) into hist[0], behind a
+// barrier; it must leave hist[0] zero when kmin == kmax.
 template <int NT, class Src>
 __device__ __forceinline__ void radix_select_range(const Src &src, int n, uint32_t rank, uint32_t kmin,
                                                    uint32_t kmax, SelectShared<NT> &sh, uint32_t &T,
-                                                   uint32_t &n_above)
+                                                   uint32_t &n_above, bool first_filled = false)
 {
     uint32_t lo = kmin, span = kmax - kmin, r = rank, above = 0;
     int p = 0;
     while (span != 0) {
-        const int bits = 32 - __clz(span);
-        const int s = bits > kDigitBits ? bits - kDigitBits : 0;
+        const int s = first_digit_shift(span);
         uint32_t *hist = sh.hist[p % 3];
-        for_each_key<NT>(src, n, [&](uint32_t k) {
-            const uint32_t sub = k - lo;
-            if (sub <= span)
-                hist_add(hist, sub >> s);
-        });
-        lds_barrier();
+        if (p != 0 || !first_filled) {
+            for_each_key<NT>(src, n, [&](uint32_t k) {
+                const uint32_t sub = k - lo;
+                if (sub <= span)
+                    hist_add(hist, sub >> s);
+            });
+            lds_barrier();
+        }
         uint32_t d, h;
         wave_pick(hist, r, d, h);
         clear_hist<NT>(sh, (p + 2) % 3);  // filled two passes ago; every wave has read it
@@ -382,10 +394,11 @@ __device__ __forceinline__ void ordered_take(const Src &src, int n, uint32_t T, 
     }
     lds_barrier();
     uint32_t ties_before = 0, taken_before = 0;
-    for (int v = 0; v < wid; ++v) {
-        const uint32_t t = sh.wave_ties[v];
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        const uint32_t t = v < wid ? sh.wave_ties[v] : 0u;
         const uint32_t left = tie_budget > ties_before ? tie_budget - ties_before : 0u;
-        taken_before += sh.wave_gts[v] + (t < left ? t : left);
+        taken_before += (v < wid ? sh.wave_gts[v] : 0u) + (t < left ? t : left);
         ties_before += t;
     }
     lds_barrier();

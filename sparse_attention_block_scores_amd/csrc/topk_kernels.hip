@@ -19,10 +19,11 @@
 //    LDS, in block order. If they hold at least the selection's cells, the
 //    threshold is >= LB and the rule over the candidates gives the exact
 //    selection. Otherwise (too few cells, or more candidates than the cap) the
-//    query takes the exact path over its whole row in the same workgroup; the
-//    key range found during the streaming pass seeds it, so equal keys finish
-//    without further histograms. Workgroups never talk to each other, so no
-//    device-scope fences are needed.
+//    query takes the exact path over its whole row in the same workgroup
+//    (equal keys need no histogram there: their range is empty). Workgroups
+//    never talk to each other, so no device-scope fences are needed.
+#include <type_traits>
+
 #include "qsa_internal.h"
 #include "topk_device.h"
 
@@ -84,12 +85,12 @@ __device__ __forceinline__ void write_cells(int32_t *out, uint32_t first, uint32
 template <int NT, class Src, class BlockAt>
 __device__ __forceinline__ void select_cells(const Src &src, int n, const QuerySel &qs, BlockAt block_at, const TopkGeom &g,
                              int q, SelectShared<NT> &sh, bool have_range = false, uint32_t kmin = 0,
-                             uint32_t kmax = 0)
+                             uint32_t kmax = 0, bool first_filled = false)
 {
     int32_t *out = g.ids + (int64_t)q * g.width;
     uint32_t T, above;
     if (have_range)
-        radix_select_range<NT>(src, n, (uint32_t)qs.r, kmin, kmax, sh, T, above);
+        radix_select_range<NT>(src, n, (uint32_t)qs.r, kmin, kmax, sh, T, above, first_filled);
     else
         radix_select<NT>(src, n, (uint32_t)qs.r, sh, T, above);
     const int bs = g.bs;
@@ -209,27 +210,90 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
 }
 
 // ------------------------------------------------------------------ one read
+// Lower bound for the one-read filter from a sample of the row (SPT values per
+// thread, sample index threadIdx.x + u*NT, valid below ns). The pages take the
+// KS-th largest sample key. Here the sample's value range is cut into 256
+// equal bins and the bound is the lower edge of the bin holding the KS-th
+// largest sample value; a bin that holds more than KS/2 samples is cut again,
+// at most three levels deep. Any bound gives the exact result (the kept blocks
+// either hold the selection or the row takes the exact path), so the bound
+// only steers how many blocks the stream keeps. Bins of equal value width
+// spread normal-like data evenly, where digits of the key bits would pile a
+// quarter of the sample onto one LDS counter.
+// Uses sh.hist[0..2] (zero on entry) and leaves them dirty; ends with a
+// barrier after the last read of them.
+template <int NT, int SPT>
+__device__ __forceinline__ float sample_bound(const float (&smp)[SPT], int ns, uint32_t ks, SelectShared<NT> &sh)
+{
+    bool in[SPT];
+    uint32_t klo = 0xFFFFFFFFu, khi = 0u;
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+        in[u] = (int)threadIdx.x + u * NT < ns;
+        const uint32_t k = key_of(smp[u]);
+        klo = in[u] ? min(klo, k) : klo;
+        khi = in[u] ? max(khi, k) : khi;
+    }
+    uint32_t mn, mx;
+    wg_minmax<NT>(klo, khi, sh, mn, mx);
+    float lo = float_of(mn), hi = float_of(mx);
+    uint32_t r = ks;
+    for (int level = 0; level < 3; ++level) {
+        // Halved operands keep the width finite for any finite range.
+        const float lh = 0.5f * lo, d2 = 0.5f * hi - lh;
+        const float inv = 256.0f / d2;
+        if (!(d2 > 0.0f) || !(inv < __builtin_inff()))
+            break;  // nothing left to cut
+        uint32_t *hist = sh.hist[level];
+        int bin[SPT];
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            bin[u] = min(255, max(0, (int)((0.5f * smp[u] - lh) * inv)));
+            if (in[u])
+                hist_add(hist, (uint32_t)bin[u]);
+        }
+        lds_barrier();
+        uint32_t b, h;
+        wave_pick(hist, r, b, h);
+        const uint32_t cnt = hist[b];
+        const float step = d2 * (1.0f / 256.0f);
+        lo = 2.0f * (lh + (float)b * step);
+        if (cnt <= ks / 2 || level == 2)
+            break;
+        hi = 2.0f * (lh + (float)(b + 1) * step);
+        r -= h;
+#pragma unroll
+        for (int u = 0; u < SPT; ++u)
+            in[u] = in[u] && bin[u] == (int)b;
+    }
+    lds_barrier();  // every wave is done reading the histograms
+    return lo;
+}
+
 // The workgroup streams the row in batches of NW*STEP blocks; within a batch
-// wave w reads the w-th STEP-block slice, F4 float4 loads per lane, three
-// batches in flight. Each wave keeps its candidates in its own LDS region and
-// counts them per batch, so there is no workgroup barrier while the row
-// streams; at the end the per-(batch, wave) counts put them in block order.
+// wave w reads the w-th STEP-block slice, F4 float4 loads per lane, with
+// kOneReadBuffers batches in flight. Each wave keeps its candidates (raw FP32
+// bits and block index) in its own LDS region and counts them per batch, so
+// there is no workgroup barrier while the row streams; at the end the
+// per-(batch, wave) counts put them in block order.
 template <int NT, int F4, bool VEC>
 __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
 {
     constexpr int NW = NT / kWave;
+    constexpr int NBUF = kOneReadBuffers;
     constexpr int STEP = kWave * 4 * F4;       // blocks a wave reads per batch
     constexpr int BATCH = NW * STEP;           // blocks the workgroup reads per batch
     constexpr int WCAP = kOneReadCap / NW;     // candidates a wave may keep
-    __shared__ __attribute__((aligned(16))) uint32_t s_wkey[kOneReadCap];  // sample, then per-wave candidates
+    static_assert(kOneReadMaxBatches <= kWave, "the compaction gives each batch a lane");
+    __shared__ __attribute__((aligned(16))) uint32_t s_wkey[kOneReadCap];  // per-wave candidates: FP32 bits
     __shared__ __attribute__((aligned(16))) int32_t s_wblk[kOneReadCap];
     __shared__ __attribute__((aligned(16))) uint32_t s_ckey[kOneReadCap];  // candidates in block order
     __shared__ __attribute__((aligned(16))) int32_t s_cblk[kOneReadCap];
     __shared__ SelectShared<NT> sh;
-    __shared__ uint32_t s_bcnt[kOneReadMaxBatches * NW];  // candidates per (batch, wave), batch-major
+    __shared__ __attribute__((aligned(16))) uint32_t s_bcnt[kOneReadMaxBatches * NW];  // per (batch, wave), batch-major
     __shared__ uint32_t s_bsrc[kOneReadMaxBatches * NW];  // where they start in the wave's own list
-    __shared__ uint32_t s_bdst[kOneReadMaxBatches * NW];  // where they go in block order
     __shared__ uint32_t s_wtot[NW];
+    __shared__ uint32_t s_wmax[NW];
 
     const TopkGeom g = a.g;
     const int q = blockIdx.x;
@@ -278,7 +342,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     };
 
     // The sample goes into registers first (SPT per thread), then the first
-    // three batches of the stream are issued behind it.
+    // NBUF batches of the stream are issued behind it.
     constexpr int SPT = kOneReadCap / NT;
     float smp[SPT];
 #pragma unroll
@@ -290,36 +354,26 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         smp[u] = row[b];
     }
     clear_hists<NT>(sh);
-    float4 A[F4], B[F4], C[F4];
-    load_batch(0, A);  // three batches in flight while the bound is found
-    load_batch(1, B);
-    load_batch(2, C);
-    if (use_bound) {
+    float4 buf[NBUF][F4];
 #pragma unroll
-        for (int u = 0; u < SPT; ++u) {
-            const int i = (int)threadIdx.x + u * NT;
-            if (i < ns)
-                s_wkey[i] = key_of(smp[u]);
-        }
-    }
+    for (int u = 0; u < NBUF; ++u)
+        load_batch(u, buf[u]);  // in flight while the bound is found
     lds_barrier();
-    uint32_t bound = 0;  // 0 keeps every block
-    if (use_bound) {
-        uint32_t above;
-        radix_select<NT>(LdsKeys{s_wkey}, ns, ks, sh, bound, above);
-    }
-    lds_barrier();  // the sample is no longer read
+    // One read: keep blocks with value >= fbound (every block without a
+    // bound), in block order, up to WCAP per wave. The key map preserves order
+    // and equates -0.0 with +0.0, exactly as float comparison does, so the
+    // kept keys are those >= key_of(fbound); keys must be finite, so the
+    // largest kept float has the largest key.
+    const float fbound = use_bound ? sample_bound<NT>(smp, ns, ks, sh) : -__builtin_inff();
+    clear_hists<NT>(sh);  // ordered before their next use by the barrier after the stream
 
-    // One read: keep blocks with key >= bound, in block order, up to WCAP.
-    // key >= bound is tested as f >= float_of(bound): the key map preserves
-    // order and equates -0.0 with +0.0, exactly as float comparison does.
-    const float fbound = use_bound ? float_of(bound) : -__builtin_inff();
-    uint32_t wcnt = 0;  // wave-uniform
+    uint32_t wcnt = 0;               // wave-uniform
+    float fmx = -__builtin_inff();   // largest value this lane kept
     uint32_t *wkey = s_wkey + wid * WCAP;
     int32_t *wblk = s_wblk + wid * WCAP;
-    auto consume = [&](int b, const float4 (&v)[F4]) {
+    auto consume = [&](int b, const float4 (&v)[F4], auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;  // every block of the slice is visible
         const int step0 = b * BATCH + wid * STEP;
-        const bool full = step0 + STEP <= n;  // wave-uniform
         const uint32_t start = wcnt;
 #pragma unroll
         for (int j = 0; j < F4; ++j) {
@@ -329,24 +383,25 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             uint64_t m[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                keep[s] = f[s] >= fbound && (full || i0 + s < n);
+                keep[s] = f[s] >= fbound && (FULL || i0 + s < n);
                 m[s] = __ballot(keep[s]);
             }
             const uint64_t any = m[0] | m[1] | m[2] | m[3];
             if (any == 0)
                 continue;
             const uint64_t two = (m[0] & (m[1] | m[2] | m[3])) | (m[1] & (m[2] | m[3])) | (m[2] & m[3]);
+            // A slot past the cap is clamped onto the last one: the wave's
+            // count then exceeds the cap and the row takes the exact path.
             if (two == 0) {
                 // Common case: no lane keeps more than one of its four keys, so
                 // a lane's slot is the number of keeping lanes below it.
                 if (keep[0] || keep[1] || keep[2] || keep[3]) {
-                    const int sel = keep[0] ? 0 : (keep[1] ? 1 : (keep[2] ? 2 : 3));
                     const float x = keep[0] ? f[0] : (keep[1] ? f[1] : (keep[2] ? f[2] : f[3]));
-                    const uint32_t pos = wcnt + count_below(any);
-                    if (pos < (uint32_t)WCAP) {
-                        wkey[pos] = key_of(x);
-                        wblk[pos] = i0 + sel;
-                    }
+                    const int sel = keep[0] ? 0 : (keep[1] ? 1 : (keep[2] ? 2 : 3));
+                    const uint32_t pos = min(wcnt + count_below(any), (uint32_t)(WCAP - 1));
+                    wkey[pos] = __float_as_uint(x);
+                    wblk[pos] = i0 + sel;
+                    fmx = x > fmx ? x : fmx;
                 }
                 wcnt += (uint32_t)__popcll(any);
                 continue;
@@ -361,10 +416,10 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 if (keep[s]) {
-                    if (pos < (uint32_t)WCAP) {
-                        wkey[pos] = key_of(f[s]);
-                        wblk[pos] = i0 + s;
-                    }
+                    const uint32_t p = min(pos, (uint32_t)(WCAP - 1));
+                    wkey[p] = __float_as_uint(f[s]);
+                    wblk[p] = i0 + s;
+                    fmx = f[s] > fmx ? f[s] : fmx;
                     ++pos;
                 }
             }
@@ -375,59 +430,102 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             s_bsrc[b * NW + wid] = start;
         }
     };
+    auto consume_batch = [&](int b, const float4 (&v)[F4]) {
+        if (b * BATCH + wid * STEP + STEP <= n)
+            consume(b, v, std::true_type{});
+        else
+            consume(b, v, std::false_type{});
+    };
     // Branch-free body (a batch past the row reads block 0 and is ignored);
-    // the last three are peeled so no load is left in flight at the end.
+    // the last NBUF are peeled so no load is left in flight at the end.
     int b = 0;
-    for (; b + 3 < nbatch; b += 3) {
-        consume(b, A);
-        load_batch(b + 3, A);
-        consume(b + 1, B);
-        load_batch(b + 4, B);
-        consume(b + 2, C);
-        load_batch(b + 5, C);
+    for (; b + NBUF < nbatch; b += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+            consume_batch(b + u, buf[u]);
+            load_batch(b + u + NBUF, buf[u]);
+        }
     }
-    consume(b, A);
-    consume(b + 1, B);
-    consume(b + 2, C);
-    if (lane == 0)
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u)
+        consume_batch(b + u, buf[u]);
+    const uint32_t wmax = wave_max(key_of(fmx));
+    if (lane == 0) {
         s_wtot[wid] = wcnt;
+        s_wmax[wid] = wmax;
+    }
     lds_barrier();
 
-    // Totals and overflow.
-    uint32_t total = 0;
+    // Totals, overflow and the largest candidate key.
+    uint32_t total = 0, kmax = 0;
     bool over = false;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         const uint32_t c = s_wtot[w];
         total += c;
         over = over || c > (uint32_t)WCAP;
+        kmax = max(kmax, s_wmax[w]);
     }
     if (!a.force_flag && !over && (uint64_t)total * (uint64_t)g.bs >= (uint64_t)qs.wq) {
-        // Destinations in block order: an exclusive scan over the (batch, wave)
-        // table, batch-major, 64 entries per wave step; wave 0 writes it.
-        const int E = nbatch * NW;
-        if (wid == 0) {
-            uint32_t carry = 0;
-            for (int e0 = 0; e0 < E; e0 += kWave) {
-                const int e = e0 + lane;
-                const uint32_t c = e < E ? s_bcnt[e] : 0u;
-                const uint32_t incl = wave_incl_sum(c);
-                if (e < E)
-                    s_bdst[e] = carry + incl - c;
-                carry += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        // Every candidate key lies in [kmin, kmax]; the copy into block order
+        // also counts the final selection's first digit.
+        const uint32_t kmin = use_bound ? key_of(fbound) : 0u;
+        const uint32_t span = kmax - kmin;
+        const int s0 = span != 0 ? first_digit_shift(span) : 0;
+        // Runs in block order are batch-major: lane bb works out how far this
+        // wave's run of batch bb moves from the wave's own list to block order
+        // and leaves it in the run's s_bsrc entry (read by this wave only); a
+        // candidate's batch follows from its block index.
+        {
+            uint32_t before = 0, btot = 0, src = 0;
+            if (lane < nbatch) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const uint32_t c = s_bcnt[lane * NW + w];
+                    btot += c;
+                    before += w < wid ? c : 0u;
+                }
+                src = s_bsrc[lane * NW + wid];
+            }
+            const uint32_t dst = wave_incl_sum(btot) - btot + before;
+            if (lane < nbatch)
+                s_bsrc[lane * NW + wid] = dst - src;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+        const uint32_t wtot = s_wtot[wid];
+        uint32_t *hist0 = sh.hist[0];
+        // Four items per lane per round, all reads issued before any write.
+        for (uint32_t i0 = (uint32_t)lane; i0 < wtot; i0 += 4 * kWave) {
+            int32_t blk[4];
+            uint32_t raw[4], shift[4];
+            bool ok[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                ok[u] = i0 + u * kWave < wtot;
+                const uint32_t i = ok[u] ? i0 + u * kWave : 0u;
+                blk[u] = wblk[i];
+                raw[u] = wkey[i];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                shift[u] = s_bsrc[(blk[u] / BATCH) * NW + wid];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (ok[u]) {
+                    const uint32_t k = key_of(__uint_as_float(raw[u]));
+                    const uint32_t d = i0 + u * kWave + shift[u];
+                    s_ckey[d] = k;
+                    s_cblk[d] = blk[u];
+                    if (span != 0)
+                        hist_add(hist0, (k - kmin) >> s0);
+                }
             }
         }
         lds_barrier();
-        for (int bb = 0; bb < nbatch; ++bb) {
-            const int e = bb * NW + wid;
-            const uint32_t cnt = s_bcnt[e], src = s_bsrc[e], dst = s_bdst[e];
-            for (uint32_t i = (uint32_t)lane; i < cnt; i += kWave) {
-                s_ckey[dst + i] = wkey[src + i];
-                s_cblk[dst + i] = wblk[src + i];
-            }
-        }
-        lds_barrier();
-        select_cells<NT>(LdsKeys{s_ckey}, (int)total, qs, [&](int i) { return s_cblk[i]; }, g, q, sh);
+        select_cells<NT>(LdsKeys{s_ckey}, (int)total, qs, [&](int i) { return s_cblk[i]; }, g, q, sh, true, kmin,
+                         kmax, true);
         return;
     }
     // Flagged: the exact rule over the whole row, read from global memory.
