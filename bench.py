@@ -10,6 +10,8 @@ are resident in HBM before the timed region starts.
 
 Prints ONE JSON line. Per-kernel times come from HIP events recorded on the
 stream the kernels run on (torch's current stream), around each entry point.
+The GPU raises its clock over the first ten or so calls of sustained matrix
+work, so the default warm-up is 20 steps (about 40 ms).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -37,7 +39,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode / top-k-only figures")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

@@ -46,8 +46,9 @@ struct ScoreGrid {
     int32_t xcd_map;
 };
 
+// Two workgroups per CU for 4-wave and 8-wave groups, one for 16 waves.
 template <int HP, int MR, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void scores_kernel(ScoreArgs a, ScoreGrid grid)
+__global__ __launch_bounds__(NW * 64, NW >= 16 ? 1 : 2) void scores_kernel(ScoreArgs a, ScoreGrid grid)
 {
     constexpr int NT = NW * 64;
     constexpr int ROWS = NW * MR * 32;
@@ -217,17 +218,17 @@ __global__ __launch_bounds__(NW * 64, 2) void scores_kernel(ScoreArgs a, ScoreGr
     }
 }
 
-template <int HP>
-hipError_t launch_hp(const ScoreArgs &a, hipStream_t s)
+template <int HP, int MR, int NW>
+hipError_t launch_cfg(const ScoreArgs &a, hipStream_t s)
 {
-    constexpr int MR = 2, NW = 4;
     constexpr int ROWS = NW * MR * 32;
+    constexpr int RESIDENT = NW >= 16 ? 256 : 512;  // workgroups that fit the chip at once
     ScoreGrid g;
     const int64_t rows = (int64_t)a.nq * HP;
     g.n_slabs = (int32_t)((rows + ROWS - 1) / ROWS);
     g.n_tiles = (a.n_blocks + kTileBlocks - 1) / kTileBlocks;
-    // About 512 resident workgroups (2 per CU) cover the chip once.
-    int groups = (int)((512 + g.n_slabs - 1) / g.n_slabs);
+    // About RESIDENT workgroups cover the chip once.
+    int groups = (int)((RESIDENT + g.n_slabs - 1) / g.n_slabs);
     groups = groups < 1 ? 1 : groups;
     groups = groups > g.n_tiles ? g.n_tiles : groups;
     g.tiles_per_group = (g.n_tiles + groups - 1) / groups;
@@ -239,6 +240,27 @@ hipError_t launch_hp(const ScoreArgs &a, hipStream_t s)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL((scores_kernel<HP, MR, NW>), dim3((unsigned)wgs), dim3(NW * 64), 0, s, a, g);
     return hipGetLastError();
+}
+
+// 64 heads: a wave holds a whole query (two 32-row tiles). Otherwise each
+// wave holds one 32-row tile (a quarter of the VGPRs, four waves per SIMD);
+// many rows take 16-wave workgroups, one per CU, which halves the key tiles
+// each CU stages and the key traffic from L2; few rows take 8-wave
+// workgroups, two per CU, so that more of them share the columns (as do
+// 1 or 2 heads).
+template <int HP>
+hipError_t launch_hp(const ScoreArgs &a, hipStream_t s)
+{
+    if constexpr (HP == 64) {
+        return launch_cfg<HP, 2, 4>(a, s);
+    } else {
+        const int64_t rows = (int64_t)a.nq * HP;
+        if constexpr (HP >= 4) {  // 1 or 2 heads: the epilogue's partial sums need more VGPRs
+            if (rows >= 16 * 512)
+                return launch_cfg<HP, 1, 16>(a, s);
+        }
+        return launch_cfg<HP, 1, 8>(a, s);
+    }
 }
 
 } // namespace
