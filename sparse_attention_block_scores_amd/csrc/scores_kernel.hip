@@ -46,9 +46,12 @@ struct ScoreGrid {
     int32_t xcd_map;
 };
 
-// Two workgroups per CU for 4-wave and 8-wave groups, one for 16 waves.
+// The second bound is the waves per SIMD the register budget must allow:
+// two 4-wave or two 8-wave workgroups per CU, or one 16-wave workgroup. With
+// 1 or 2 heads the epilogue keeps a partial sum per row and gets the larger
+// budget of one 8-wave workgroup per CU instead of spilling.
 template <int HP, int MR, int NW>
-__global__ __launch_bounds__(NW * 64, NW >= 16 ? 1 : 2) void scores_kernel(ScoreArgs a, ScoreGrid grid)
+__global__ __launch_bounds__(NW * 64, NW >= 8 && HP >= 4 ? 4 : 2) void scores_kernel(ScoreArgs a, ScoreGrid grid)
 {
     constexpr int NT = NW * 64;
     constexpr int ROWS = NW * MR * 32;

@@ -58,6 +58,23 @@ def test_shapes(heads, nq, n_blocks):
     assert (s[:, n_blocks:] == 7.0).all(), "columns past n_blocks were written"
 
 
+@pytest.mark.parametrize("heads,nq", [(3, 2731), (8, 1030), (13, 515), (31, 257)])
+def test_many_rows(heads, nq):
+    """8,192 or more padded (query, head) rows take the 16-wave workgroups
+    (one per CU); row counts here are not multiples of their 512-row slabs and
+    1,000 blocks end in a partial key tile."""
+    n_blocks = 1000
+    tag = f"gpu/scores/many/{heads}/{nq}"
+    q = synth.normal(tag + "/q", (nq, heads, 128))
+    k = synth.normal(tag + "/k", (n_blocks, 128))
+    w = synth.uniform01(tag + "/w", (nq, heads))
+    say(f"scores many rows heads={heads} nq={nq} nb={n_blocks}")
+    s = gpu_scores(q, k, w, ld=n_blocks + 1, fill=7.0)
+    ref = oracle.block_scores(q, k, w)
+    assert_scores_close(s[:, :n_blocks], ref, f"many rows h={heads} nq={nq}")
+    assert (s[:, n_blocks:] == 7.0).all(), "columns past n_blocks were written"
+
+
 def test_decode_select_shapes_full():
     for wl in (synth.c1(), synth.c3()):
         q, k, w = wl.tensors()
