@@ -25,6 +25,8 @@ constexpr int kOneReadCap = 4096;         // one-read candidate cap per query (b
 constexpr int kOneReadMinBlocks = 28672;  // prompt calls from this many blocks ...
 constexpr int kOneReadMinQueries = 64;    // ... and this many queries use the one-read path
 constexpr int kSampleStride = 32;
+constexpr int kFinalBits = 11;            // one-read final select: one digit of 2,048 bins
+constexpr int kFinalBins = 1 << kFinalBits;
 
 // Workspace layout of the split (byte offsets, 256-byte aligned).
 struct TopkLayout {

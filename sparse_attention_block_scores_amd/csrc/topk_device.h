@@ -237,14 +237,16 @@ __device__ __forceinline__ void wg_minmax(uint32_t lo, uint32_t hi, SelectShared
     lds_barrier();
 }
 
-// The bin of a histogram (highest bin first) that holds rank r, and the count
-// of everything in higher bins. Every wave computes it on its own: lane l owns
-// the kBins/64 bins just below the (kBins/64)*l highest.
+// The bin of a histogram of BINS bins (highest bin first) that holds rank r,
+// and the count of everything in higher bins. Every wave computes it on its
+// own: lane l owns the BINS/64 bins just below the (BINS/64)*l highest.
+template <int BINS = kBins>
 __device__ __forceinline__ void wave_pick(const uint32_t *hist, uint32_t r, uint32_t &bin, uint32_t &higher)
 {
-    constexpr int PL = kBins / kWave;
+    constexpr int PL = BINS / kWave;
+    static_assert(PL % 4 == 0, "16-byte reads of each lane's bins");
     const int lane = lane_id();
-    const int lo_bin = kBins - PL * (lane + 1);
+    const int lo_bin = BINS - PL * (lane + 1);
     uint32_t c[PL];
 #pragma unroll
     for (int i = 0; i < PL / 4; ++i) {
@@ -285,27 +287,22 @@ __device__ __forceinline__ int first_digit_shift(uint32_t span)
 // separate this call from any earlier one; they are zero again on return.
 // Each pass costs one barrier: every wave picks the digit itself, and the
 // histogram filled two passes earlier is cleared while the next one fills.
-// With first_filled the caller has already counted the first digit
-// ((k - kmin) >> first_digit_shift(kmax - kmin)) into hist[0], behind a
-// barrier; it must leave hist[0] zero when kmin == kmax.
 template <int NT, class Src>
 __device__ __forceinline__ void radix_select_range(const Src &src, int n, uint32_t rank, uint32_t kmin,
                                                    uint32_t kmax, SelectShared<NT> &sh, uint32_t &T,
-                                                   uint32_t &n_above, bool first_filled = false)
+                                                   uint32_t &n_above)
 {
     uint32_t lo = kmin, span = kmax - kmin, r = rank, above = 0;
     int p = 0;
     while (span != 0) {
         const int s = first_digit_shift(span);
         uint32_t *hist = sh.hist[p % 3];
-        if (p != 0 || !first_filled) {
-            for_each_key<NT>(src, n, [&](uint32_t k) {
-                const uint32_t sub = k - lo;
-                if (sub <= span)
-                    hist_add(hist, sub >> s);
-            });
-            lds_barrier();
-        }
+        for_each_key<NT>(src, n, [&](uint32_t k) {
+            const uint32_t sub = k - lo;
+            if (sub <= span)
+                hist_add(hist, sub >> s);
+        });
+        lds_barrier();
         uint32_t d, h;
         wave_pick(hist, r, d, h);
         clear_hist<NT>(sh, (p + 2) % 3);  // filled two passes ago; every wave has read it
@@ -321,6 +318,27 @@ __device__ __forceinline__ void radix_select_range(const Src &src, int n, uint32
     }
     T = lo;
     n_above = above;
+}
+
+// Within one wave: the rank-th largest (1-based, 1 <= rank <= c) of the c <= 64
+// keys in keys[0..c), and how many of them are strictly larger. Every lane
+// counts the keys above and at its own key against all c keys in turn.
+__device__ __forceinline__ void wave_rank_small(const uint32_t *keys, uint32_t c, uint32_t rank, uint32_t &T,
+                                                uint32_t &n_above)
+{
+    const int lane = lane_id();
+    const bool valid = lane < (int)c;
+    const uint32_t x = valid ? keys[lane] : 0u;
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t j = 0; j < c; ++j) {
+        const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, (int)j);
+        gt += y > x ? 1u : 0u;
+        ge += y >= x ? 1u : 0u;
+    }
+    const uint64_t hit = __ballot(valid && gt < rank && rank <= ge);
+    const int L = hit ? (int)__ffsll((unsigned long long)hit) - 1 : 0;
+    T = (uint32_t)__builtin_amdgcn_readlane((int)x, L);
+    n_above = (uint32_t)__builtin_amdgcn_readlane((int)gt, L);
 }
 
 // Min and max key of src[0..n).

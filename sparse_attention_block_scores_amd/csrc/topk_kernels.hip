@@ -79,20 +79,15 @@ __device__ __forceinline__ void write_cells(int32_t *out, uint32_t first, uint32
             out[first + j] = cell0 + (int32_t)j;
 }
 
-// Final selection over n candidate blocks (n >= qs.r) that contain the
-// query's whole selection, in ascending block order: writes the cells, the -1
-// tail and the count. Histograms must be zero on entry.
+// Writes a query's selection from n candidate blocks in ascending block order
+// that contain it, given T (the r-th largest candidate key) and the number of
+// candidates above T: the cells, the -1 tail and the count.
 template <int NT, class Src, class BlockAt>
-__device__ __forceinline__ void select_cells(const Src &src, int n, const QuerySel &qs, BlockAt block_at, const TopkGeom &g,
-                             int q, SelectShared<NT> &sh, bool have_range = false, uint32_t kmin = 0,
-                             uint32_t kmax = 0, bool first_filled = false)
+__device__ __forceinline__ void emit_selection(const Src &src, int n, const QuerySel &qs, BlockAt block_at,
+                                               const TopkGeom &g, int q, SelectShared<NT> &sh, uint32_t T,
+                                               uint32_t above)
 {
     int32_t *out = g.ids + (int64_t)q * g.width;
-    uint32_t T, above;
-    if (have_range)
-        radix_select_range<NT>(src, n, (uint32_t)qs.r, kmin, kmax, sh, T, above, first_filled);
-    else
-        radix_select<NT>(src, n, (uint32_t)qs.r, sh, T, above);
     const int bs = g.bs;
     const uint32_t limit = (uint32_t)qs.wq;
     ordered_take<NT>(src, n, T, (uint32_t)qs.r - above, (uint32_t)bs, (uint32_t)qs.last_unit, sh,
@@ -103,6 +98,18 @@ __device__ __forceinline__ void select_cells(const Src &src, int n, const QueryS
         out[p] = -1;
     if (g.counts && threadIdx.x == 0)
         g.counts[q] = qs.wq;
+}
+
+// Final selection over n candidate blocks (n >= qs.r) that contain the
+// query's whole selection, in ascending block order: writes the cells, the -1
+// tail and the count. Histograms must be zero on entry.
+template <int NT, class Src, class BlockAt>
+__device__ __forceinline__ void select_cells(const Src &src, int n, const QuerySel &qs, BlockAt block_at,
+                                             const TopkGeom &g, int q, SelectShared<NT> &sh)
+{
+    uint32_t T, above;
+    radix_select<NT>(src, n, (uint32_t)qs.r, sh, T, above);
+    emit_selection<NT>(src, n, qs, block_at, g, q, sh, T, above);
 }
 
 // Keys of blocks [b0, b0+n) of row q into LDS.
@@ -294,6 +301,10 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     __shared__ uint32_t s_bsrc[kOneReadMaxBatches * NW];  // where they start in the wave's own list
     __shared__ uint32_t s_wtot[NW];
     __shared__ uint32_t s_wmax[NW];
+    __shared__ __attribute__((aligned(16))) uint32_t s_fhist[kFinalBins];  // final select: fine bins ...
+    __shared__ __attribute__((aligned(16))) uint32_t s_chist[kBins];       // ... and 256 coarse ones (8 fine each)
+    __shared__ uint32_t s_small[kWave];                                    // keys of the chosen fine bin
+    __shared__ uint32_t s_small_n;
 
     const TopkGeom g = a.g;
     const int q = blockIdx.x;
@@ -354,6 +365,12 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         smp[u] = row[b];
     }
     clear_hists<NT>(sh);
+    for (int i = threadIdx.x; i < kFinalBins / 4; i += NT)
+        reinterpret_cast<uint4 *>(s_fhist)[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = threadIdx.x; i < kBins / 4; i += NT)
+        reinterpret_cast<uint4 *>(s_chist)[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (threadIdx.x == 0)
+        s_small_n = 0;
     float4 buf[NBUF][F4];
 #pragma unroll
     for (int u = 0; u < NBUF; ++u)
@@ -468,10 +485,11 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     }
     if (!a.force_flag && !over && (uint64_t)total * (uint64_t)g.bs >= (uint64_t)qs.wq) {
         // Every candidate key lies in [kmin, kmax]; the copy into block order
-        // also counts the final selection's first digit.
+        // also counts the top kFinalBits bits of (key - kmin) in s_fhist.
         const uint32_t kmin = use_bound ? key_of(fbound) : 0u;
         const uint32_t span = kmax - kmin;
-        const int s0 = span != 0 ? first_digit_shift(span) : 0;
+        const int fbits = span != 0 ? 32 - __clz(span) : 0;
+        const int sF = fbits > kFinalBits ? fbits - kFinalBits : 0;
         // Runs in block order are batch-major: lane bb works out how far this
         // wave's run of batch bb moves from the wave's own list to block order
         // and leaves it in the run's s_bsrc entry (read by this wave only); a
@@ -495,7 +513,6 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
         const uint32_t wtot = s_wtot[wid];
-        uint32_t *hist0 = sh.hist[0];
         // Four items per lane per round, all reads issued before any write.
         for (uint32_t i0 = (uint32_t)lane; i0 < wtot; i0 += 4 * kWave) {
             int32_t blk[4];
@@ -518,14 +535,68 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
                     const uint32_t d = i0 + u * kWave + shift[u];
                     s_ckey[d] = k;
                     s_cblk[d] = blk[u];
-                    if (span != 0)
-                        hist_add(hist0, (k - kmin) >> s0);
+                    if (span != 0) {
+                        const uint32_t fb = (k - kmin) >> sF;
+                        lds_add(&s_fhist[fb], 1u);
+                        lds_add(&s_chist[fb >> (kFinalBits - kDigitBits)], 1u);
+                    }
                 }
             }
         }
         lds_barrier();
-        select_cells<NT>(LdsKeys{s_ckey}, (int)total, qs, [&](int i) { return s_cblk[i]; }, g, q, sh, true, kmin,
-                         kmax, true);
+
+        // Threshold: the coarse bin holding rank r, then the fine bin among its
+        // eight; that usually holds a handful of keys, which one wave ranks
+        // exactly (every wave does so, which saves a barrier). A crowded fine
+        // bin goes on with radix digits.
+        uint32_t T = kmin, above = 0;
+        if (span != 0) {
+            constexpr int FPC = kFinalBins / kBins;  // fine bins per coarse bin
+            uint32_t cb, h;
+            wave_pick(s_chist, (uint32_t)qs.r, cb, h);
+            uint32_t f[FPC];
+#pragma unroll
+            for (int i = 0; i < FPC / 4; ++i) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(s_fhist + cb * FPC + 4 * i);
+                f[4 * i] = v.x; f[4 * i + 1] = v.y; f[4 * i + 2] = v.z; f[4 * i + 3] = v.w;
+            }
+            uint32_t b = cb * FPC, c = 0, cum = h;
+            bool found = false;
+#pragma unroll
+            for (int i = FPC - 1; i >= 0; --i) {
+                const bool here = !found && cum + f[i] >= (uint32_t)qs.r;
+                b = here ? cb * FPC + i : b;
+                c = here ? f[i] : c;
+                h = here ? cum : h;
+                found = found || here;
+                cum += f[i];
+            }
+            const uint32_t blo = kmin + (b << sF);
+            const uint32_t bspan = sF == 0 ? 0u : min(span - (b << sF), (1u << sF) - 1u);
+            const uint32_t r2 = (uint32_t)qs.r - h;
+            if (bspan == 0) {
+                T = blo;
+                above = h;
+            } else if (c <= (uint32_t)kWave) {
+                for_each_key<NT>(LdsKeys{s_ckey}, (int)total, [&](uint32_t k) {
+                    if (k - blo <= bspan) {
+                        const uint32_t pos =
+                            __hip_atomic_fetch_add(&s_small_n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                        if (pos < (uint32_t)kWave)
+                            s_small[pos] = k;
+                    }
+                });
+                lds_barrier();
+                uint32_t a2;
+                wave_rank_small(s_small, c, r2, T, a2);
+                above = h + a2;
+            } else {
+                uint32_t a2;
+                radix_select_range<NT>(LdsKeys{s_ckey}, (int)total, r2, blo, blo + bspan, sh, T, a2);
+                above = h + a2;
+            }
+        }
+        emit_selection<NT>(LdsKeys{s_ckey}, (int)total, qs, [&](int i) { return s_cblk[i]; }, g, q, sh, T, above);
         return;
     }
     // Flagged: the exact rule over the whole row, read from global memory.
