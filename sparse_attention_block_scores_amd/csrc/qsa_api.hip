@@ -170,6 +170,7 @@ qsa_status run_topk(const TopkGeom &g, const TopkPlan &plan, void *ws, hipStream
     sa.n_chunks = p.n_chunks;
     const int64_t stage_b = p.stage_b_lds ? plan.cand_stride : 0;
     sa.lds_words = (int32_t)(stage_b > p.chunk_blocks ? stage_b : p.chunk_blocks);
+    sa.blk_words = (int32_t)stage_b;
     return launch_split(sa, s) == hipSuccess ? QSA_OK : QSA_EHIP;
 }
 

@@ -20,13 +20,11 @@ constexpr int kOneReadMaxBatches = 64;    // the one-read path takes rows of up 
 constexpr int kChunkBound = 4104;         // split chunks: the fewest of at most this many blocks
 constexpr int kMinChunk = 64;
 constexpr int kMaxChunk = 15360;          // keeps a chunk's keys under 60 KB of LDS
-constexpr int kStageBLdsWords = 15360;    // stage B keeps up to this many candidate keys in LDS
+constexpr int kStageBLdsWords = 15360;    // stage B keeps up to this many candidates (keys and blocks) in LDS
 constexpr int kOneReadCap = 4096;         // one-read candidate cap per query (blocks)
 constexpr int kOneReadMinBlocks = 28672;  // prompt calls from this many blocks ...
 constexpr int kOneReadMinQueries = 64;    // ... and this many queries use the one-read path
 constexpr int kSampleStride = 32;
-constexpr int kFinalBits = 11;            // one-read final select: one digit of 2,048 bins
-constexpr int kFinalBins = 1 << kFinalBits;
 
 // Workspace layout of the split (byte offsets, 256-byte aligned).
 struct TopkLayout {
@@ -69,7 +67,8 @@ struct SplitArgs {
     int64_t cand_stride;
     int32_t chunk;
     int32_t n_chunks;
-    int32_t lds_words;      // dynamic LDS words available (>= chunk)
+    int32_t lds_words;      // dynamic LDS words for keys (>= chunk)
+    int32_t blk_words;      // dynamic LDS words after them for stage B's block ids (0: read from the workspace)
 };
 
 struct OneReadArgs {

@@ -188,22 +188,44 @@ __device__ __forceinline__ void for_each_key(const Src &src, int n, F f)
 // ------------------------------------------------------------ shared state
 constexpr int kDigitBits = 8;
 constexpr int kBins = 1 << kDigitBits;
+constexpr int kFineBits = 11;                        // fine bins: 2,048 ...
+constexpr int kFineBins = 1 << kFineBits;
+constexpr int kFinePerCoarse = kFineBins / kBins;    // ... in 256 coarse bins of 8
 
 template <int NT>
 struct SelectShared {
     static constexpr int NW = NT / kWave;
     alignas(16) uint32_t hist[3][kBins];  // rotating: fill one, pick from it, clear the one before
+    alignas(16) uint32_t fine[kFineBins];
+    alignas(16) uint32_t coarse[kBins];
+    uint32_t small[kWave];                // keys of one fine bin
+    uint32_t small_n;
     uint32_t red[2][NW];
     uint32_t wave_ties[NW];
     uint32_t wave_gts[NW];
 };
 
 template <int NT>
+__device__ __forceinline__ void clear_fine(SelectShared<NT> &sh)
+{
+    uint4 *f = reinterpret_cast<uint4 *>(sh.fine);
+    for (int i = threadIdx.x; i < kFineBins / 4; i += NT)
+        f[i] = make_uint4(0u, 0u, 0u, 0u);
+    uint4 *c = reinterpret_cast<uint4 *>(sh.coarse);
+    for (int i = threadIdx.x; i < kBins / 4; i += NT)
+        c[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Every histogram and counter of sh to zero (a barrier must follow).
+template <int NT>
 __device__ __forceinline__ void clear_hists(SelectShared<NT> &sh)
 {
     uint4 *h = reinterpret_cast<uint4 *>(&sh.hist[0][0]);
     for (int i = threadIdx.x; i < 3 * kBins / 4; i += NT)
         h[i] = make_uint4(0u, 0u, 0u, 0u);
+    clear_fine<NT>(sh);
+    if (threadIdx.x == 0)
+        sh.small_n = 0;
 }
 
 template <int NT>
@@ -274,6 +296,80 @@ __device__ __forceinline__ void wave_pick(const uint32_t *hist, uint32_t r, uint
     higher = (uint32_t)__builtin_amdgcn_readlane((int)my_higher, L);
 }
 
+// The fine bin holding rank r (1-based) by way of the coarse bins (fine bin f
+// lies in coarse bin f / kFinePerCoarse): its index, its count, and the count
+// of everything in higher fine bins. Every wave computes it on its own.
+template <int NT>
+__device__ __forceinline__ void pick_fine(const SelectShared<NT> &sh, uint32_t r, uint32_t &fb, uint32_t &c,
+                                          uint32_t &above)
+{
+    uint32_t cb, h;
+    wave_pick(sh.coarse, r, cb, h);
+    uint32_t f[kFinePerCoarse];
+#pragma unroll
+    for (int i = 0; i < kFinePerCoarse / 4; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(sh.fine + cb * kFinePerCoarse + 4 * i);
+        f[4 * i] = v.x; f[4 * i + 1] = v.y; f[4 * i + 2] = v.z; f[4 * i + 3] = v.w;
+    }
+    fb = cb * kFinePerCoarse;
+    c = 0;
+    above = h;
+    uint32_t cum = h;
+    bool found = false;
+#pragma unroll
+    for (int i = kFinePerCoarse - 1; i >= 0; --i) {
+        const bool here = !found && cum + f[i] >= r;
+        fb = here ? cb * kFinePerCoarse + i : fb;
+        c = here ? f[i] : c;
+        above = here ? cum : above;
+        found = found || here;
+        cum += f[i];
+    }
+}
+
+// Within one wave: the rank-th largest (1-based, 1 <= rank <= c) of the c <= 64
+// keys in keys[0..c), and how many of them are strictly larger. Every lane
+// counts the keys above and at its own key against all c keys in turn.
+__device__ __forceinline__ void wave_rank_small(const uint32_t *keys, uint32_t c, uint32_t rank, uint32_t &T,
+                                                uint32_t &n_above)
+{
+    const int lane = lane_id();
+    const bool valid = lane < (int)c;
+    const uint32_t x = valid ? keys[lane] : 0u;
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t j = 0; j < c; ++j) {
+        const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, (int)j);
+        gt += y > x ? 1u : 0u;
+        ge += y >= x ? 1u : 0u;
+    }
+    const uint64_t hit = __ballot(valid && gt < rank && rank <= ge);
+    const int L = hit ? (int)__ffsll((unsigned long long)hit) - 1 : 0;
+    T = (uint32_t)__builtin_amdgcn_readlane((int)x, L);
+    n_above = (uint32_t)__builtin_amdgcn_readlane((int)gt, L);
+}
+
+// The rank-th largest (1 <= rank <= c) of the c <= 64 keys of src for which
+// member(k) holds, and how many of them lie above it: the members are gathered
+// into sh.small in any order and one wave ranks them (every wave does, which
+// saves a barrier). sh.small_n is zero on entry and again after the call's
+// barrier.
+template <int NT, class Src, class Member>
+__device__ __forceinline__ void rank_members(const Src &src, int n, Member member, uint32_t c, uint32_t rank,
+                                             SelectShared<NT> &sh, uint32_t &T, uint32_t &n_above)
+{
+    for_each_key<NT>(src, n, [&](uint32_t k) {
+        if (member(k)) {
+            const uint32_t pos = __hip_atomic_fetch_add(&sh.small_n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (pos < (uint32_t)kWave)
+                sh.small[pos] = k;
+        }
+    });
+    lds_barrier();
+    if (threadIdx.x == 0)
+        sh.small_n = 0;
+    wave_rank_small(sh.small, c, rank, T, n_above);
+}
+
 // Shift of the first digit over a key range of the given span (span > 0).
 __device__ __forceinline__ int first_digit_shift(uint32_t span)
 {
@@ -320,27 +416,6 @@ __device__ __forceinline__ void radix_select_range(const Src &src, int n, uint32
     n_above = above;
 }
 
-// Within one wave: the rank-th largest (1-based, 1 <= rank <= c) of the c <= 64
-// keys in keys[0..c), and how many of them are strictly larger. Every lane
-// counts the keys above and at its own key against all c keys in turn.
-__device__ __forceinline__ void wave_rank_small(const uint32_t *keys, uint32_t c, uint32_t rank, uint32_t &T,
-                                                uint32_t &n_above)
-{
-    const int lane = lane_id();
-    const bool valid = lane < (int)c;
-    const uint32_t x = valid ? keys[lane] : 0u;
-    uint32_t gt = 0, ge = 0;
-    for (uint32_t j = 0; j < c; ++j) {
-        const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, (int)j);
-        gt += y > x ? 1u : 0u;
-        ge += y >= x ? 1u : 0u;
-    }
-    const uint64_t hit = __ballot(valid && gt < rank && rank <= ge);
-    const int L = hit ? (int)__ffsll((unsigned long long)hit) - 1 : 0;
-    T = (uint32_t)__builtin_amdgcn_readlane((int)x, L);
-    n_above = (uint32_t)__builtin_amdgcn_readlane((int)gt, L);
-}
-
 // Min and max key of src[0..n).
 template <int NT, class Src>
 __device__ __forceinline__ void key_range(const Src &src, int n, SelectShared<NT> &sh, uint32_t &mn, uint32_t &mx)
@@ -353,13 +428,72 @@ __device__ __forceinline__ void key_range(const Src &src, int n, SelectShared<NT
     wg_minmax<NT>(lo, hi, sh, mn, mx);
 }
 
+// Fine bin of a key among kFineBins bins of equal value width over
+// [lo, lo + 2*d2] (lh = lo/2, inv = kFineBins/d2; halved operands keep the
+// width finite for any finite range). Each step rounds monotonically, so the
+// bin never decreases as the key grows: a bin's keys form an interval of
+// keys. The explicit roundings keep every evaluation bit-identical.
+__device__ __forceinline__ uint32_t value_fine_bin(uint32_t k, float lh, float inv)
+{
+    const float t = __fmul_rn(__fsub_rn(__fmul_rn(0.5f, float_of(k)), lh), inv);
+    return (uint32_t)min(kFineBins - 1, max(0, (int)t));
+}
+
+// Rank-th largest key of src (see radix_select_range) without a known range.
+// Ranges of more than 2^16 keys take one pass of 2,048 fine bins (in 256
+// coarse ones) instead of 8-bit digits. Up to 2^27 keys (a few binades) the
+// fine bins are the top bits of (key - min); wider ranges, such as signed
+// normal-like keys spanning most binades, take bins of equal value width, as
+// key bits would put a large share of the keys into a few bins. The fine bin
+// that holds the rank usually holds a handful of keys, which one wave ranks
+// exactly; a crowded one is an interval of keys, which radix digits finish.
 template <int NT, class Src>
 __device__ __forceinline__ void radix_select(const Src &src, int n, uint32_t rank, SelectShared<NT> &sh,
                                              uint32_t &T, uint32_t &n_above)
 {
     uint32_t mn, mx;
     key_range<NT>(src, n, sh, mn, mx);
-    radix_select_range<NT>(src, n, rank, mn, mx, sh, T, n_above);
+    const uint32_t span = mx - mn;
+    const float lo = float_of(mn), hi = float_of(mx);
+    const float lh = 0.5f * lo, d2 = 0.5f * hi - lh;
+    const float inv = (float)kFineBins / d2;
+    const bool by_value = span >= (1u << 27) && d2 > 0.0f && inv < __builtin_inff();
+    if (span < (1u << 16) || (span >= (1u << 27) && !by_value)) {
+        radix_select_range<NT>(src, n, rank, mn, mx, sh, T, n_above);
+        return;
+    }
+    const int sF = (32 - __clz(span)) - kFineBits;  // >= 6 here
+    auto fine_bin = [&](uint32_t k) { return by_value ? value_fine_bin(k, lh, inv) : (k - mn) >> sF; };
+    for_each_key<NT>(src, n, [&](uint32_t k) {
+        const uint32_t fb = fine_bin(k);
+        lds_add(&sh.fine[fb], 1u);
+        lds_add(&sh.coarse[fb / kFinePerCoarse], 1u);
+    });
+    lds_barrier();
+    uint32_t fb, c, h;
+    pick_fine<NT>(sh, rank, fb, c, h);
+    uint32_t a2;
+    if (c <= (uint32_t)kWave) {
+        rank_members<NT>(src, n, [&](uint32_t k) { return fine_bin(k) == fb; }, c, rank - h, sh, T, a2);
+        clear_fine<NT>(sh);  // after rank_members' barrier: every wave has picked
+    } else {
+        // The bin's keys: an interval, exact from the bits or from a min/max pass.
+        uint32_t kmin_b = mn + (fb << sF), kmax_b = min(mx, kmin_b + ((1u << sF) - 1u));
+        if (by_value) {
+            uint32_t blo = 0xFFFFFFFFu, bhi = 0u;
+            for_each_key<NT>(src, n, [&](uint32_t k) {
+                const bool in = fine_bin(k) == fb;
+                blo = in ? min(blo, k) : blo;
+                bhi = in ? max(bhi, k) : bhi;
+            });
+            wg_minmax<NT>(blo, bhi, sh, kmin_b, kmax_b);
+        } else {
+            lds_barrier();  // every wave has picked before the bins are cleared
+        }
+        clear_fine<NT>(sh);
+        radix_select_range<NT>(src, n, rank - h, kmin_b, kmax_b, sh, T, a2);
+    }
+    n_above = h + a2;
 }
 
 // Walk items 0..n-1 in order and take every item with key > T plus the first

@@ -200,17 +200,22 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
     const int total = (nchq - 1) * cap_q + last_n;
     const uint32_t *gkey = a.cand_keys + (int64_t)q * a.cand_stride;
     const int32_t *gblk = a.cand_blocks + (int64_t)q * a.cand_stride;
-    auto blk = [&](int i) { return gblk[i]; };
-    if (total <= a.lds_words) {
+    if (total <= a.blk_words) {
+        // Keys and block ids both to LDS: the emit then reads no global memory.
+        int32_t *s_blks = reinterpret_cast<int32_t *>(s_keys + a.lds_words);
         const int n4 = total >> 2;
-        for (int i = threadIdx.x; i < n4; i += NT)
+        for (int i = threadIdx.x; i < n4; i += NT) {
             *reinterpret_cast<uint4 *>(s_keys + 4 * i) = *reinterpret_cast<const uint4 *>(gkey + 4 * i);
-        for (int i = (n4 << 2) + (int)threadIdx.x; i < total; i += NT)
+            *reinterpret_cast<int4 *>(s_blks + 4 * i) = *reinterpret_cast<const int4 *>(gblk + 4 * i);
+        }
+        for (int i = (n4 << 2) + (int)threadIdx.x; i < total; i += NT) {
             s_keys[i] = gkey[i];
+            s_blks[i] = gblk[i];
+        }
         lds_barrier();
-        select_cells<NT>(lds, total, qs, blk, g, q, sh);
+        select_cells<NT>(lds, total, qs, [&](int i) { return s_blks[i]; }, g, q, sh);
     } else {
-        select_cells<NT>(GlobalKeys{gkey}, total, qs, blk, g, q, sh);
+        select_cells<NT>(GlobalKeys{gkey}, total, qs, [&](int i) { return gblk[i]; }, g, q, sh);
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(&a.tickets[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -301,10 +306,6 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     __shared__ uint32_t s_bsrc[kOneReadMaxBatches * NW];  // where they start in the wave's own list
     __shared__ uint32_t s_wtot[NW];
     __shared__ uint32_t s_wmax[NW];
-    __shared__ __attribute__((aligned(16))) uint32_t s_fhist[kFinalBins];  // final select: fine bins ...
-    __shared__ __attribute__((aligned(16))) uint32_t s_chist[kBins];       // ... and 256 coarse ones (8 fine each)
-    __shared__ uint32_t s_small[kWave];                                    // keys of the chosen fine bin
-    __shared__ uint32_t s_small_n;
 
     const TopkGeom g = a.g;
     const int q = blockIdx.x;
@@ -365,12 +366,6 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         smp[u] = row[b];
     }
     clear_hists<NT>(sh);
-    for (int i = threadIdx.x; i < kFinalBins / 4; i += NT)
-        reinterpret_cast<uint4 *>(s_fhist)[i] = make_uint4(0u, 0u, 0u, 0u);
-    for (int i = threadIdx.x; i < kBins / 4; i += NT)
-        reinterpret_cast<uint4 *>(s_chist)[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (threadIdx.x == 0)
-        s_small_n = 0;
     float4 buf[NBUF][F4];
 #pragma unroll
     for (int u = 0; u < NBUF; ++u)
@@ -485,11 +480,12 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     }
     if (!a.force_flag && !over && (uint64_t)total * (uint64_t)g.bs >= (uint64_t)qs.wq) {
         // Every candidate key lies in [kmin, kmax]; the copy into block order
-        // also counts the top kFinalBits bits of (key - kmin) in s_fhist.
+        // also counts the top kFineBits bits of (key - kmin) into the fine
+        // bins and their coarse bins.
         const uint32_t kmin = use_bound ? key_of(fbound) : 0u;
         const uint32_t span = kmax - kmin;
         const int fbits = span != 0 ? 32 - __clz(span) : 0;
-        const int sF = fbits > kFinalBits ? fbits - kFinalBits : 0;
+        const int sF = fbits > kFineBits ? fbits - kFineBits : 0;
         // Runs in block order are batch-major: lane bb works out how far this
         // wave's run of batch bb moves from the wave's own list to block order
         // and leaves it in the run's s_bsrc entry (read by this wave only); a
@@ -537,64 +533,33 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
                     s_cblk[d] = blk[u];
                     if (span != 0) {
                         const uint32_t fb = (k - kmin) >> sF;
-                        lds_add(&s_fhist[fb], 1u);
-                        lds_add(&s_chist[fb >> (kFinalBits - kDigitBits)], 1u);
+                        lds_add(&sh.fine[fb], 1u);
+                        lds_add(&sh.coarse[fb / kFinePerCoarse], 1u);
                     }
                 }
             }
         }
         lds_barrier();
 
-        // Threshold: the coarse bin holding rank r, then the fine bin among its
-        // eight; that usually holds a handful of keys, which one wave ranks
-        // exactly (every wave does so, which saves a barrier). A crowded fine
-        // bin goes on with radix digits.
+        // Threshold: the fine bin holding rank r usually holds a handful of
+        // keys, which one wave ranks exactly; a crowded one goes on with radix
+        // digits over its keys.
         uint32_t T = kmin, above = 0;
         if (span != 0) {
-            constexpr int FPC = kFinalBins / kBins;  // fine bins per coarse bin
-            uint32_t cb, h;
-            wave_pick(s_chist, (uint32_t)qs.r, cb, h);
-            uint32_t f[FPC];
-#pragma unroll
-            for (int i = 0; i < FPC / 4; ++i) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(s_fhist + cb * FPC + 4 * i);
-                f[4 * i] = v.x; f[4 * i + 1] = v.y; f[4 * i + 2] = v.z; f[4 * i + 3] = v.w;
-            }
-            uint32_t b = cb * FPC, c = 0, cum = h;
-            bool found = false;
-#pragma unroll
-            for (int i = FPC - 1; i >= 0; --i) {
-                const bool here = !found && cum + f[i] >= (uint32_t)qs.r;
-                b = here ? cb * FPC + i : b;
-                c = here ? f[i] : c;
-                h = here ? cum : h;
-                found = found || here;
-                cum += f[i];
-            }
+            uint32_t b, c, h;
+            pick_fine<NT>(sh, (uint32_t)qs.r, b, c, h);
             const uint32_t blo = kmin + (b << sF);
             const uint32_t bspan = sF == 0 ? 0u : min(span - (b << sF), (1u << sF) - 1u);
             const uint32_t r2 = (uint32_t)qs.r - h;
-            if (bspan == 0) {
+            uint32_t a2 = 0;
+            if (bspan == 0)
                 T = blo;
-                above = h;
-            } else if (c <= (uint32_t)kWave) {
-                for_each_key<NT>(LdsKeys{s_ckey}, (int)total, [&](uint32_t k) {
-                    if (k - blo <= bspan) {
-                        const uint32_t pos =
-                            __hip_atomic_fetch_add(&s_small_n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                        if (pos < (uint32_t)kWave)
-                            s_small[pos] = k;
-                    }
-                });
-                lds_barrier();
-                uint32_t a2;
-                wave_rank_small(s_small, c, r2, T, a2);
-                above = h + a2;
-            } else {
-                uint32_t a2;
+            else if (c <= (uint32_t)kWave)
+                rank_members<NT>(LdsKeys{s_ckey}, (int)total, [&](uint32_t k) { return k - blo <= bspan; }, c, r2,
+                                 sh, T, a2);
+            else
                 radix_select_range<NT>(LdsKeys{s_ckey}, (int)total, r2, blo, blo + bspan, sh, T, a2);
-                above = h + a2;
-            }
+            above = h + a2;
         }
         emit_selection<NT>(LdsKeys{s_ckey}, (int)total, qs, [&](int i) { return s_cblk[i]; }, g, q, sh, T, above);
         return;
@@ -628,14 +593,14 @@ hipError_t launch_split(const SplitArgs &a, hipStream_t s)
     if (!lds_limit_raised) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&split_kernel<kSplitThreads>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 kStageBLdsWords * 4);
+                                                 2 * kStageBLdsWords * 4);
         if (e != hipSuccess)
             return e;
         lds_limit_raised = true;
     }
     const dim3 grid((unsigned)a.n_chunks, (unsigned)a.g.nq);
-    hipLaunchKernelGGL(split_kernel<kSplitThreads>, grid, dim3(kSplitThreads), (size_t)a.lds_words * 4, s,
-                       a);
+    hipLaunchKernelGGL(split_kernel<kSplitThreads>, grid, dim3(kSplitThreads),
+                       (size_t)(a.lds_words + a.blk_words) * 4, s, a);
     return hipGetLastError();
 }
 
