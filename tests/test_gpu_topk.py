@@ -64,12 +64,14 @@ def _keys(tag, variant, nq, n_blocks, ld):
         s[:, :n_blocks] = vals[synth.integers(tag, nq * n_blocks, 0, 4).reshape(nq, n_blocks)]
     elif variant == "sorted":
         s[:, :n_blocks] = np.arange(n_blocks, dtype=np.float32)[None, :] * 0.25
+    elif variant == "narrow":  # positive, within one binade, 64 levels: heavy ties
+        s[:, :n_blocks] = 1.0 + synth.integers(tag, nq * n_blocks, 0, 63).reshape(nq, n_blocks) / 64.0
     return s
 
 
 def _cases():
     rng = np.random.default_rng(20261202)
-    variants = ["normal", "q64", "equal", "few", "sorted"]
+    variants = ["normal", "q64", "equal", "few", "sorted", "narrow"]
     sizes = [1, 2, 7, 64, 65, 333, 1000, 4104, 4105, 9000, 30000]
     out = []
     for i in range(72):
@@ -97,6 +99,38 @@ def test_random_cases(i, n_blocks, bs, width, nq, variant, call, path):
     got = gpu_topk(s, n_blocks, bs, width, call, active=active, options=_opts(path))
     exp = oracle.topk_sort(s, n_blocks, bs, width, active)
     assert_ids_equal(got, exp, f"case {i}")
+
+
+def _branch_keys(kind, nq, n):
+    """Keys that steer the exact threshold select into each of its branches
+    (key ranges under 2^16 keys; key-bit or value-width fine bins; a fine bin
+    with a few keys or a crowded one)."""
+    tag = f"gpu/topk/branch/{kind}"
+    if kind == "tiny_span":  # consecutive floats from 1.0: the range is under 2^16 keys
+        k = synth.integers(tag, nq * n, 0, 60000).reshape(nq, n)
+        return (1.0 + k * 2.0 ** -23).astype(np.float32)
+    if kind == "bits_few":  # positive, a few binades: key-bit bins, few keys per bin
+        return (1.0 + np.abs(synth.normal(tag, (nq, n)))).astype(np.float32)
+    if kind == "bits_crowded":  # positive, one binade, 64 levels: key-bit bins, crowded
+        return (1.0 + synth.integers(tag, nq * n, 0, 63).reshape(nq, n) / 64.0).astype(np.float32)
+    if kind == "value_few":  # signed normal: value bins, few keys per bin
+        return synth.normal(tag, (nq, n))
+    if kind == "value_crowded":  # signed, 64 levels: value bins, crowded
+        return synth.quantize64(synth.normal(tag, (nq, n)))
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("path", ["split", "split516", "fallback"])
+@pytest.mark.parametrize("kind", ["tiny_span", "bits_few", "bits_crowded", "value_few", "value_crowded"])
+def test_threshold_select_branches(kind, path):
+    nq, n = 3, 20000
+    s = _branch_keys(kind, nq, n)
+    call = "prompt" if path == "fallback" else "decode"
+    active = np.full(nq, n, np.int32) if call == "prompt" else None
+    say(f"threshold branch {kind} path={path}")
+    for width in (2048, 40000):
+        got = gpu_topk(s, n, 4, width, call, active=active, options=_opts(path))
+        assert_ids_equal(got, oracle.topk_sort(s, n, 4, width, active), f"{kind} {path} w={width}")
 
 
 @pytest.mark.parametrize("n_blocks", synth.C2_BLOCKS)
