@@ -142,20 +142,26 @@ def secondary(torch, qsa, synth, dev, reps=50):
     out["decode_nq3_topk_us_by_cells"] = dec
     prm = {}
     for nb in synth.C4_BLOCKS:
-        t = synth.c4(nb)
-        host = t.scores()
-        # Four distinct score buffers (4 x 128 MiB) so that reads come from HBM,
-        # not from the 256 MB last-level cache.
-        bufs = [torch.from_numpy(host).to(dev) for _ in range(4)]
-        wsp = qsa.workspace(qsa.topk_workspace_bytes(t.nq, nb, 4, t.width, "prompt"), dev)
-        idp = torch.empty((t.nq, t.width), dtype=torch.int32, device=dev)
-        cp = torch.empty((t.nq,), dtype=torch.int32, device=dev)
-        us = time_us(lambda i: qsa.block_topk(bufs[i % 4], nb, 4, t.width, "prompt", ids=idp, counts=cp,
-                                              ws=wsp), n=40)
-        gbs = t.nq * nb * 4 / us / 1e3
-        prm[str(nb * 4)] = {"us": round(us, 2), "scores_GBps": round(gbs, 1),
-                            "hbm_frac": round(gbs / PEAK_HBM_GBS, 3)}
-        del bufs
+        entry = {}
+        for variant in ("continuous", "q64", "equal"):
+            t = synth.c4(nb, variant)
+            host = t.scores()
+            # Four distinct score buffers (4 x 128 MiB) so that reads come from HBM,
+            # not from the 256 MB last-level cache.
+            bufs = [torch.from_numpy(host).to(dev) for _ in range(4)]
+            wsp = qsa.workspace(qsa.topk_workspace_bytes(t.nq, nb, 4, t.width, "prompt"), dev)
+            idp = torch.empty((t.nq, t.width), dtype=torch.int32, device=dev)
+            cp = torch.empty((t.nq,), dtype=torch.int32, device=dev)
+            us = time_us(lambda i: qsa.block_topk(bufs[i % 4], nb, 4, t.width, "prompt", ids=idp, counts=cp,
+                                                  ws=wsp), n=40)
+            gbs = t.nq * nb * 4 / us / 1e3
+            if variant == "continuous":
+                entry.update({"us": round(us, 2), "scores_GBps": round(gbs, 1),
+                              "hbm_frac": round(gbs / PEAK_HBM_GBS, 3)})
+            else:  # 64-level keys; all-equal keys (every query takes the exact fallback)
+                entry[variant + "_us"] = round(us, 2)
+            del bufs
+        prm[str(nb * 4)] = entry
     out["prompt_nq256_topk_by_cells"] = prm
     return out
 

@@ -282,28 +282,32 @@ __device__ __forceinline__ float sample_bound(const float (&smp)[SPT], int ns, u
     return lo;
 }
 
-// The workgroup streams the row in batches of NW*STEP blocks; within a batch
-// wave w reads the w-th STEP-block slice, F4 float4 loads per lane, with
-// kOneReadBuffers batches in flight. Each wave keeps its candidates (raw FP32
-// bits and block index) in its own LDS region and counts them per batch, so
-// there is no workgroup barrier while the row streams; at the end the
-// per-(batch, wave) counts put them in block order.
+// The workgroup streams the row in slices of STEP blocks, F4 float4 loads per
+// lane and kOneReadBuffers slices in flight per wave. The first slices are
+// dealt out in order; after that a wave claims the next slice from an LDS
+// counter as it frees a buffer, so a wave whose loads come back early takes
+// more of the row and the waves finish together. Each wave keeps its
+// candidates (raw FP32 bits and block index) in its own LDS region and records
+// per slice how many it kept and where, so there is no workgroup barrier while
+// the row streams; at the end the per-slice counts put them in block order.
 template <int NT, int F4, bool VEC>
 __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
 {
     constexpr int NW = NT / kWave;
     constexpr int NBUF = kOneReadBuffers;
-    constexpr int STEP = kWave * 4 * F4;       // blocks a wave reads per batch
-    constexpr int BATCH = NW * STEP;           // blocks the workgroup reads per batch
-    constexpr int WCAP = kOneReadCap / NW;     // candidates a wave may keep
-    static_assert(kOneReadMaxBatches <= kWave, "the compaction gives each batch a lane");
+    constexpr int STEP = kWave * 4 * F4;                  // blocks per slice
+    constexpr int MAXS = kOneReadMaxBatches * NW;         // slices of the longest row taken here
+    constexpr int WCAP = kOneReadCap / NW;                // candidates a wave may keep
+    static_assert(kOneReadBatch == NW * STEP, "a batch is one slice per wave");
     __shared__ __attribute__((aligned(16))) uint32_t s_wkey[kOneReadCap];  // per-wave candidates: FP32 bits
     __shared__ __attribute__((aligned(16))) int32_t s_wblk[kOneReadCap];
     __shared__ __attribute__((aligned(16))) uint32_t s_ckey[kOneReadCap];  // candidates in block order
     __shared__ __attribute__((aligned(16))) int32_t s_cblk[kOneReadCap];
     __shared__ SelectShared<NT> sh;
-    __shared__ __attribute__((aligned(16))) uint32_t s_bcnt[kOneReadMaxBatches * NW];  // per (batch, wave), batch-major
-    __shared__ uint32_t s_bsrc[kOneReadMaxBatches * NW];  // where they start in the wave's own list
+    __shared__ uint32_t s_scnt[MAXS];   // per slice: candidates kept ...
+    __shared__ uint32_t s_ssrc[MAXS];   // ... where they start in the list of ...
+    __shared__ uint32_t s_swave[MAXS];  // ... this wave
+    __shared__ uint32_t s_next;         // next slice to claim
     __shared__ uint32_t s_wtot[NW];
     __shared__ uint32_t s_wmax[NW];
 
@@ -330,16 +334,16 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     const uint32_t ks = 2u * (uint32_t)qs.r / kSampleStride + 16u;
     const bool all_cells = (int64_t)n * g.bs <= (int64_t)qs.wq;
     const bool use_bound = !all_cells && !a.force_flag && (uint32_t)ns >= ks;
-    const int nbatch = (n + BATCH - 1) / BATCH;  // <= kOneReadMaxBatches (the dispatch sees to it)
+    const int nslices = (n + STEP - 1) / STEP;  // <= MAXS (the dispatch sees to it)
 
     // Every load below is unconditional: a lane with nothing to read re-reads
     // block 0 (the row has at least one visible block here) and the value is
     // ignored. A load under a branch makes the compiler lose count of the
     // loads in flight and wait for all of them before the next use.
-    auto load_batch = [&](int b, float4 (&v)[F4]) {
+    auto load_slice = [&](int sl, float4 (&v)[F4]) {
 #pragma unroll
         for (int j = 0; j < F4; ++j) {
-            const int i0 = b * BATCH + wid * STEP + j * 4 * kWave + 4 * lane;
+            const int i0 = sl * STEP + j * 4 * kWave + 4 * lane;
             if constexpr (VEC) {
                 // Streamed once: nontemporal loads keep it from displacing cached data.
                 const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + (i0 < n ? i0 : 0)));
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     };
 
     // The sample goes into registers first (SPT per thread), then the first
-    // NBUF batches of the stream are issued behind it.
+    // NBUF slices of every wave are issued behind it.
     constexpr int SPT = kOneReadCap / NT;
     float smp[SPT];
 #pragma unroll
@@ -367,9 +371,14 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     }
     clear_hists<NT>(sh);
     float4 buf[NBUF][F4];
+    int cs[NBUF];  // slice in each buffer (wave-uniform)
 #pragma unroll
-    for (int u = 0; u < NBUF; ++u)
-        load_batch(u, buf[u]);  // in flight while the bound is found
+    for (int u = 0; u < NBUF; ++u) {
+        cs[u] = u * NW + wid;
+        load_slice(cs[u], buf[u]);  // in flight while the bound is found
+    }
+    if (threadIdx.x == 0)
+        s_next = NBUF * NW;
     lds_barrier();
     // One read: keep blocks with value >= fbound (every block without a
     // bound), in block order, up to WCAP per wave. The key map preserves order
@@ -383,9 +392,9 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     float fmx = -__builtin_inff();   // largest value this lane kept
     uint32_t *wkey = s_wkey + wid * WCAP;
     int32_t *wblk = s_wblk + wid * WCAP;
-    auto consume = [&](int b, const float4 (&v)[F4], auto full_tag) {
+    auto consume = [&](int sl, const float4 (&v)[F4], auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;  // every block of the slice is visible
-        const int step0 = b * BATCH + wid * STEP;
+        const int step0 = sl * STEP;
         const uint32_t start = wcnt;
 #pragma unroll
         for (int j = 0; j < F4; ++j) {
@@ -437,30 +446,36 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             }
             wcnt += step;
         }
-        if (lane == 0 && b < kOneReadMaxBatches) {
-            s_bcnt[b * NW + wid] = wcnt - start;
-            s_bsrc[b * NW + wid] = start;
+        if (lane == 0) {
+            s_scnt[sl] = wcnt - start;
+            s_ssrc[sl] = start;
+            s_swave[sl] = (uint32_t)wid;
         }
     };
-    auto consume_batch = [&](int b, const float4 (&v)[F4]) {
-        if (b * BATCH + wid * STEP + STEP <= n)
-            consume(b, v, std::true_type{});
-        else
-            consume(b, v, std::false_type{});
-    };
-    // Branch-free body (a batch past the row reads block 0 and is ignored);
-    // the last NBUF are peeled so no load is left in flight at the end.
-    int b = 0;
-    for (; b + NBUF < nbatch; b += NBUF) {
+    // Rounds over the buffers until each holds a slice past the row. The next
+    // slice is claimed before the buffer is consumed (the claim's latency
+    // hides behind it); loads stay unconditional (a slice past the row reads
+    // block 0 and is not consumed).
+    for (;;) {
+        bool done = true;
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
-            consume_batch(b + u, buf[u]);
-            load_batch(b + u + NBUF, buf[u]);
+            uint32_t nxt = 0;
+            if (lane == 0)
+                nxt = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (cs[u] < nslices) {
+                if (cs[u] * STEP + STEP <= n)
+                    consume(cs[u], buf[u], std::true_type{});
+                else
+                    consume(cs[u], buf[u], std::false_type{});
+            }
+            cs[u] = __builtin_amdgcn_readfirstlane((int)nxt);
+            load_slice(cs[u], buf[u]);
+            done = done && cs[u] >= nslices;
         }
+        if (done)
+            break;
     }
-#pragma unroll
-    for (int u = 0; u < NBUF; ++u)
-        consume_batch(b + u, buf[u]);
     const uint32_t wmax = wave_max(key_of(fmx));
     if (lane == 0) {
         s_wtot[wid] = wcnt;
@@ -486,24 +501,22 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         const uint32_t span = kmax - kmin;
         const int fbits = span != 0 ? 32 - __clz(span) : 0;
         const int sF = fbits > kFineBits ? fbits - kFineBits : 0;
-        // Runs in block order are batch-major: lane bb works out how far this
-        // wave's run of batch bb moves from the wave's own list to block order
-        // and leaves it in the run's s_bsrc entry (read by this wave only); a
-        // candidate's batch follows from its block index.
+        // Slices in order are block order: every wave scans the slice counts
+        // itself and leaves, for each of its own slices, how far its run moves
+        // from the wave's list to block order in the slice's s_ssrc entry (no
+        // other wave touches those); a candidate's slice is its block / STEP.
         {
-            uint32_t before = 0, btot = 0, src = 0;
-            if (lane < nbatch) {
-#pragma unroll
-                for (int w = 0; w < NW; ++w) {
-                    const uint32_t c = s_bcnt[lane * NW + w];
-                    btot += c;
-                    before += w < wid ? c : 0u;
-                }
-                src = s_bsrc[lane * NW + wid];
+            uint32_t carry = 0;
+            for (int s0 = 0; s0 < nslices; s0 += kWave) {
+                const int sl = s0 + lane;
+                const bool ok = sl < nslices;
+                const uint32_t c = ok ? s_scnt[sl] : 0u;
+                const uint32_t incl = wave_incl_sum(c);
+                const bool mine = ok && s_swave[sl] == (uint32_t)wid;
+                if (mine)
+                    s_ssrc[sl] = carry + incl - c - s_ssrc[sl];
+                carry += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
             }
-            const uint32_t dst = wave_incl_sum(btot) - btot + before;
-            if (lane < nbatch)
-                s_bsrc[lane * NW + wid] = dst - src;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
         __builtin_amdgcn_wave_barrier();
@@ -523,7 +536,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                shift[u] = s_bsrc[(blk[u] / BATCH) * NW + wid];
+                shift[u] = s_ssrc[blk[u] / STEP];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 if (ok[u]) {
