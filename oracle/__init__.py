@@ -40,10 +40,10 @@ class Library:
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         lib.oracle_block_scores.argtypes = [P, P, P, P, i64, i32, i32, i32, i32]
         lib.oracle_block_scores_at.argtypes = [P, P, P, i32, i32, P, P, i32, P]
-        for name in ("oracle_topk_sort", "oracle_topk_rule"):
+        topk = ("oracle_topk_sort", "oracle_topk_rule", "oracle_topk_sort_cells", "oracle_topk_rule_cells")
+        for name in topk:
             getattr(lib, name).argtypes = [P, i64, i32, i32, i32, i32, P, P, P]
-        for name in ("oracle_block_scores", "oracle_block_scores_at",
-                     "oracle_topk_sort", "oracle_topk_rule"):
+        for name in ("oracle_block_scores", "oracle_block_scores_at") + topk:
             getattr(lib, name).restype = None
         self.lib = lib
         self.path = path
@@ -94,6 +94,15 @@ class Library:
         """The same selection by threshold / above / tie budget / ordered emit."""
         return self._topk("oracle_topk_rule", scores, n_blocks, block_size, width, active)
 
+    def topk_sort_cells(self, scores, n_blocks, block_size, width, cells):
+        """Full-sort selection with a visible cell count per query (the last
+        visible block may be partial)."""
+        return self._topk("oracle_topk_sort_cells", scores, n_blocks, block_size, width, cells)
+
+    def topk_rule_cells(self, scores, n_blocks, block_size, width, cells):
+        """Threshold-rule selection with a visible cell count per query."""
+        return self._topk("oracle_topk_rule_cells", scores, n_blocks, block_size, width, cells)
+
 
 def compile_source(source_text: str, out_path: str) -> str:
     """Compile a (possibly edited) copy of the oracle source; used by the
@@ -139,3 +148,11 @@ def topk_sort(scores, n_blocks, block_size, width, active=None):
 
 def topk_rule(scores, n_blocks, block_size, width, active=None):
     return _load().topk_rule(scores, n_blocks, block_size, width, active)
+
+
+def topk_sort_cells(scores, n_blocks, block_size, width, cells):
+    return _load().topk_sort_cells(scores, n_blocks, block_size, width, cells)
+
+
+def topk_rule_cells(scores, n_blocks, block_size, width, cells):
+    return _load().topk_rule_cells(scores, n_blocks, block_size, width, cells)

@@ -30,8 +30,12 @@
  *     32-bit image of the float keys), not by sorting, so that forms 2 and 3
  *     are two independent computations of one definition.
  *
- * Visible blocks: on a decode call every one of the n_blocks blocks; on a
- * prompt call the first min(max(active[q], 0), n_blocks) blocks of query q.
+ * Visible cells: on a decode call every cell of the n_blocks blocks; on a
+ * prompt call the cells of the first min(max(active[q], 0), n_blocks) blocks
+ * of query q. The *_cells entry points take a cell count per query instead,
+ * cells [0, min(max(cells[q], 0), n_blocks * block_size)), so the last visible
+ * block may hold fewer than block_size cells; every visible cell still carries
+ * its block's key.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -100,6 +104,18 @@ static int visible_blocks(int n_blocks, const int32_t *active, int iq)
     return a;
 }
 
+/* Visible cells of query iq: a cell count when `cells` is given, else whole
+ * visible blocks. */
+static int64_t visible_cells(int n_blocks, int block_size, const int32_t *active, const int32_t *cells, int iq)
+{
+    const int64_t all = (int64_t)n_blocks * block_size;
+    if (cells) {
+        int64_t c = cells[iq];
+        return c < 0 ? 0 : (c > all ? all : c);
+    }
+    return (int64_t)visible_blocks(n_blocks, active, iq) * block_size;
+}
+
 /* --------------------------------------------------- top-k by full sort */
 
 typedef struct {
@@ -123,14 +139,12 @@ static int by_int_asc(const void *pa, const void *pb)
     return (a > b) - (a < b);
 }
 
-EXPORT void oracle_topk_sort(const float *scores, int64_t ld, int nq, int n_blocks,
-                             int block_size, int width, const int32_t *active,
-                             int32_t *ids, int32_t *counts)
+static void topk_sort(const float *scores, int64_t ld, int nq, int n_blocks, int block_size, int width,
+                      const int32_t *active, const int32_t *vcells, int32_t *ids, int32_t *counts)
 {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int iq = 0; iq < nq; ++iq) {
-        const int nb = visible_blocks(n_blocks, active, iq);
-        const int64_t ncells = (int64_t)nb * block_size;
+        const int64_t ncells = visible_cells(n_blocks, block_size, active, vcells, iq);
         int32_t *out = ids + (int64_t)iq * width;
         cell_t *cells = (cell_t *)malloc((size_t)(ncells > 0 ? ncells : 1) * sizeof(cell_t));
         for (int64_t c = 0; c < ncells; ++c) {
@@ -150,10 +164,31 @@ EXPORT void oracle_topk_sort(const float *scores, int64_t ld, int nq, int n_bloc
     }
 }
 
+EXPORT void oracle_topk_sort(const float *scores, int64_t ld, int nq, int n_blocks,
+                             int block_size, int width, const int32_t *active,
+                             int32_t *ids, int32_t *counts)
+{
+    topk_sort(scores, ld, nq, n_blocks, block_size, width, active, NULL, ids, counts);
+}
+
+EXPORT void oracle_topk_sort_cells(const float *scores, int64_t ld, int nq, int n_blocks,
+                                   int block_size, int width, const int32_t *cells,
+                                   int32_t *ids, int32_t *counts)
+{
+    topk_sort(scores, ld, nq, n_blocks, block_size, width, NULL, cells, ids, counts);
+}
+
 /* ------------------------------------------- top-k by the threshold rule */
 
 /* Order-preserving image of a float in uint32: a > b  <=>  image(a) > image(b),
  * with -0.0 and +0.0 mapped to one value (they compare equal as floats). */
+/* Visible cells of block b when the first ncells cells are visible. */
+static int64_t cells_of(int b, int block_size, int64_t ncells)
+{
+    const int64_t rest = ncells - (int64_t)b * block_size;
+    return rest < block_size ? rest : block_size;
+}
+
 static uint32_t ordered_image(float f)
 {
     uint32_t bits;
@@ -163,14 +198,13 @@ static uint32_t ordered_image(float f)
     return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
 }
 
-EXPORT void oracle_topk_rule(const float *scores, int64_t ld, int nq, int n_blocks,
-                             int block_size, int width, const int32_t *active,
-                             int32_t *ids, int32_t *counts)
+static void topk_rule(const float *scores, int64_t ld, int nq, int n_blocks, int block_size, int width,
+                      const int32_t *active, const int32_t *vcells, int32_t *ids, int32_t *counts)
 {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int iq = 0; iq < nq; ++iq) {
-        const int nb = visible_blocks(n_blocks, active, iq);
-        const int64_t ncells = (int64_t)nb * block_size;
+        const int64_t ncells = visible_cells(n_blocks, block_size, active, vcells, iq);
+        const int nb = (int)((ncells + block_size - 1) / block_size);
         const float *row = scores + (int64_t)iq * ld;
         int32_t *out = ids + (int64_t)iq * width;
         const int64_t m = ncells < width ? ncells : width;
@@ -184,7 +218,7 @@ EXPORT void oracle_topk_rule(const float *scores, int64_t ld, int nq, int n_bloc
                 int64_t n_ge = 0;
                 for (int b = 0; b < nb; ++b)
                     if ((uint64_t)ordered_image(row[b]) >= mid)
-                        n_ge += block_size;
+                        n_ge += cells_of(b, block_size, ncells);
                 if (n_ge >= m)
                     lo = mid;
                 else
@@ -194,7 +228,7 @@ EXPORT void oracle_topk_rule(const float *scores, int64_t ld, int nq, int n_bloc
             int64_t above = 0;
             for (int b = 0; b < nb; ++b)
                 if (ordered_image(row[b]) > T)
-                    above += block_size;
+                    above += cells_of(b, block_size, ncells);
             int64_t budget = m - above;
             for (int64_t c = 0; c < ncells; ++c) {
                 uint32_t key = ordered_image(row[c / block_size]);
@@ -211,4 +245,18 @@ EXPORT void oracle_topk_rule(const float *scores, int64_t ld, int nq, int n_bloc
         if (counts)
             counts[iq] = (int32_t)written;
     }
+}
+
+EXPORT void oracle_topk_rule(const float *scores, int64_t ld, int nq, int n_blocks,
+                             int block_size, int width, const int32_t *active,
+                             int32_t *ids, int32_t *counts)
+{
+    topk_rule(scores, ld, nq, n_blocks, block_size, width, active, NULL, ids, counts);
+}
+
+EXPORT void oracle_topk_rule_cells(const float *scores, int64_t ld, int nq, int n_blocks,
+                                   int block_size, int width, const int32_t *cells,
+                                   int32_t *ids, int32_t *counts)
+{
+    topk_rule(scores, ld, nq, n_blocks, block_size, width, NULL, cells, ids, counts);
 }

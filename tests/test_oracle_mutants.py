@@ -30,6 +30,9 @@ TOPK_PINS = [
     lambda lib: T.test_increasing_keys_take_the_last_blocks(lib, "topk_sort", 4, 2047),
     lambda lib: T.test_increasing_keys_take_the_last_blocks(lib, "topk_rule", 4, 2047),
     lambda lib: T.test_invariants_on_prompt_like_rows(lib, "q64"),
+    lambda lib: T.test_cells_hand_cases(lib, "topk_sort_cells"),
+    lambda lib: T.test_cells_hand_cases(lib, "topk_rule_cells"),
+    lambda lib: T.test_cells_brute_force_tiny(lib, 3),
 ]
 
 # (name, original text, planted mistake, pins expected to notice)
@@ -66,6 +69,13 @@ MUTANTS = [
     ("signed zeros not merged", "    if (bits == 0x80000000u)\n        bits = 0u;", "", TOPK_PINS),
     ("tie budget one too many", "} else if (key == T && budget > 0) {",
      "} else if (key == T && budget >= 0) {", TOPK_PINS),
+    ("partial tail block counted whole", "    return rest < block_size ? rest : block_size;",
+     "    return block_size;", TOPK_PINS),
+    ("visible cell count ignored", "        return c < 0 ? 0 : (c > all ? all : c);",
+     "        return all;", TOPK_PINS),
+    ("visible cells rounded up to whole blocks", "        return c < 0 ? 0 : (c > all ? all : c);",
+     "        c = (c + block_size - 1) / block_size * block_size;\n        return c < 0 ? 0 : (c > all ? all : c);",
+     TOPK_PINS),
 ]
 
 

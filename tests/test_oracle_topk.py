@@ -151,3 +151,95 @@ def test_forms_agree_on_a_full_prompt_row(oracle_lib):
     a = oracle_lib.topk_sort(s, wl.n_blocks, 4, 2048)
     b = oracle_lib.topk_rule(s, wl.n_blocks, 4, 2048)
     assert (a[0] == b[0]).all() and (a[1] == 2048).all()
+
+
+# ------------------------------------------------- cell-granular visible length
+CELL_FORMS = ("topk_sort_cells", "topk_rule_cells")
+
+
+@pytest.mark.parametrize("form", CELL_FORMS)
+def test_cells_hand_cases(oracle_lib, form):
+    g = json.load(open(os.path.join(GOLDEN, "topk_cells_hand.json")))
+    for case in g["cases"]:
+        keys = np.array([case["keys"]], np.float32)
+        ids, counts = getattr(oracle_lib, form)(keys, keys.shape[1], case["block_size"], case["width"],
+                                                np.array([case["cells"]], np.int32))
+        assert ids[0].tolist() == case["ids"], case["name"]
+        assert counts[0] == case["count"], case["name"]
+
+
+def _brute_force_cells(keys, bs, ncells, width):
+    cells = [(float(keys[c // bs]), c) for c in range(ncells)]
+    m = min(width, len(cells))
+
+    def precedes(a, b):
+        return a[0] > b[0] or (a[0] == b[0] and a[1] < b[1])
+
+    found = []
+    for subset in itertools.combinations(range(len(cells)), m):
+        chosen = set(subset)
+        if all(precedes(cells[i], cells[j]) for i in chosen for j in range(len(cells)) if j not in chosen):
+            found.append(sorted(subset))
+    assert len(found) == 1
+    return found[0]
+
+
+@pytest.mark.parametrize("bs", [2, 3, 4])
+def test_cells_brute_force_tiny(oracle_lib, bs):
+    """Every visible length from one cell to all of them, partial tails included."""
+    values = np.array([-1.0, -0.0, 0.0, 1.0, 2.0], np.float32)
+    rng = np.random.default_rng(200 + bs)
+    n_cases = 0
+    for n_blocks in range(1, 4):
+        for _ in range(6):
+            keys = values[rng.integers(0, len(values), n_blocks)]
+            for ncells in range(1, n_blocks * bs + 1):
+                for width in range(1, ncells + 2):
+                    expect = _brute_force_cells(keys, bs, ncells, width)
+                    for form in CELL_FORMS:
+                        ids, counts = getattr(oracle_lib, form)(keys[None, :], n_blocks, bs, width,
+                                                                np.array([ncells], np.int32))
+                        assert counts[0] == len(expect), (form, keys, ncells, width)
+                        assert ids[0, : len(expect)].tolist() == expect, (form, keys, ncells, width)
+                        assert (ids[0, len(expect):] == -1).all()
+                    n_cases += 1
+    assert n_cases > 150
+
+
+@pytest.mark.parametrize("form,block_form", [("topk_sort_cells", "topk_sort"), ("topk_rule_cells", "topk_rule")])
+def test_cells_whole_blocks_reduce_to_active_blocks(oracle_lib, form, block_form):
+    """A visible length of whole blocks is the active-block selection."""
+    s = synth.normal("oracle/cells/whole", (6, 3000))
+    active = np.array([0, 1, 17, 999, 2500, 3000], np.int32)
+    for bs in (1, 4):
+        got = getattr(oracle_lib, form)(s, 3000, bs, 2048, active * bs)
+        exp = getattr(oracle_lib, block_form)(s, 3000, bs, 2048, active)
+        assert (got[0] == exp[0]).all() and (got[1] == exp[1]).all()
+
+
+@pytest.mark.parametrize("variant", ["normal", "q64"])
+def test_cells_invariants_and_forms_agree(oracle_lib, variant):
+    nq, nb, bs, width = 8, 4000, 4, 2048
+    s = synth.normal(f"oracle/cells/{variant}", (nq, nb))
+    if variant == "q64":
+        s = synth.quantize64(s)
+    cells = synth.integers(f"oracle/cells/{variant}/n", nq, 0, nb * bs).astype(np.int32)
+    cells[0] = nb * bs - 1  # partial tail of 3 cells
+    cells[1] = 5
+    ids, counts = oracle_lib.topk_sort_cells(s, nb, bs, width, cells)
+    ids2, counts2 = oracle_lib.topk_rule_cells(s, nb, bs, width, cells)
+    assert (ids == ids2).all() and (counts == counts2).all()
+    for q in range(nq):
+        m = min(width, int(cells[q]))
+        assert counts[q] == m
+        sel = ids[q, :m]
+        assert (np.diff(sel) > 0).all() and (sel < cells[q]).all() and (ids[q, m:] == -1).all()
+        key = s[q, np.arange(cells[q]) // bs]
+        chosen = np.zeros(cells[q], bool)
+        chosen[sel] = True
+        if 0 < m < cells[q]:
+            assert key[chosen].min() >= key[~chosen].max()
+            t = key[chosen].min()
+            tied = np.flatnonzero(key == t)
+            assert chosen[tied].tolist() == sorted(chosen[tied].tolist(), reverse=True)
+
