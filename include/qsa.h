@@ -23,7 +23,11 @@
  *
  * Calls. A decode call carries no active-block count: all n_blocks blocks are
  * visible to every query. A prompt call may carry a per-query active-block
- * count: query q sees blocks [0, min(max(active[q], 0), n_blocks)).
+ * count: query q sees blocks [0, min(max(active[q], 0), n_blocks)). The
+ * *_cells entry points take, for either call, a per-query count of visible
+ * CELLS that stays in device memory, so the last visible block may be partial
+ * and the length can change between calls without the host knowing it (the
+ * launches depend only on the host arguments, so a stream capture replays).
  *
  * Memory and streams. Every pointer argument except `opt` and `out` structs
  * is caller-owned DEVICE memory; the library never allocates, frees or keeps
@@ -158,6 +162,28 @@ qsa_status qsa_block_topk(const float *scores, int64_t ld_scores, int32_t nq,
                           const qsa_options *opt);
 
 /*
+ * qsa_block_topk_cells - qsa_block_topk with a cell-granular visible length
+ * read on the device, for decode and prompt calls alike. Strata pull #3987,
+ * section Approach, derives the split from the context length on the device;
+ * Strata pull #1091, section What, keeps a separate tail block, so a context
+ * need not end on a block boundary.
+ *
+ *   visible_cells  [nq] int32 device, or NULL (every cell visible): query q
+ *                  sees cells [0, min(max(visible_cells[q], 0),
+ *                  n_blocks * block_size)); every visible cell carries its
+ *                  block's score as its key, cells past the count do not
+ *                  exist for the selection.
+ *   cell_ids, counts, workspace, stream, opt: as qsa_block_topk (the same
+ *   workspace size); counts[q] = min(width, visible cells of q).
+ */
+qsa_status qsa_block_topk_cells(const float *scores, int64_t ld_scores, int32_t nq,
+                                int32_t n_blocks, int32_t block_size, int32_t width,
+                                qsa_call call, const int32_t *visible_cells,
+                                int32_t *cell_ids, int32_t *counts,
+                                void *workspace, size_t workspace_bytes, void *stream,
+                                const qsa_options *opt);
+
+/*
  * qsa_select - qsa_block_scores followed by qsa_block_topk on the scores it
  * wrote (`scores` is the caller's buffer and holds the scores afterwards).
  * Same argument rules as the two calls above.
@@ -169,6 +195,15 @@ qsa_status qsa_select(const float *q, const float *k, const float *w,
                       const int32_t *active_blocks, int32_t *cell_ids, int32_t *counts,
                       void *workspace, size_t workspace_bytes, void *stream,
                       const qsa_options *opt);
+
+/* qsa_select with the cell-granular visible length of qsa_block_topk_cells. */
+qsa_status qsa_select_cells(const float *q, const float *k, const float *w,
+                            int32_t n_heads, int32_t head_dim,
+                            float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks,
+                            int32_t block_size, int32_t width, qsa_call call,
+                            const int32_t *visible_cells, int32_t *cell_ids, int32_t *counts,
+                            void *workspace, size_t workspace_bytes, void *stream,
+                            const qsa_options *opt);
 
 /* Static text for a status code. */
 const char *qsa_status_str(qsa_status status);

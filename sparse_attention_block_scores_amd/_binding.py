@@ -84,8 +84,10 @@ def lib() -> ctypes.CDLL:
         L.qsa_workspace_init.argtypes = [P, sz, P]
         L.qsa_block_topk.argtypes = [P, i64, i32, i32, i32, i32, i32, P, P, P, P, sz, P, P]
         L.qsa_select.argtypes = [P, P, P, i32, i32, P, i64, i32, i32, i32, i32, i32, P, P, P, P, sz, P, P]
+        L.qsa_block_topk_cells.argtypes = L.qsa_block_topk.argtypes
+        L.qsa_select_cells.argtypes = L.qsa_select.argtypes
         for name in ("qsa_block_scores", "qsa_topk_plan_get", "qsa_workspace_init", "qsa_block_topk",
-                     "qsa_select"):
+                     "qsa_select", "qsa_block_topk_cells", "qsa_select_cells"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -198,37 +200,49 @@ def _topk_outputs(nq, width, device, ids, counts):
     return ids, counts
 
 
-def _active(active, nq):
+def _active(active, nq, name="active"):
     if active is None:
         return None
-    _dev(active, torch.int32, "active")
+    _dev(active, torch.int32, name)
     if tuple(active.shape) != (nq,) or not active.is_contiguous():
-        raise ValueError("active must be a contiguous [nq] int32 tensor")
+        raise ValueError(f"{name} must be a contiguous [nq] int32 tensor")
     return active
 
 
+def _lengths(active, cells, nq):
+    """(pointer to pass, which entry point): active blocks, or visible cells."""
+    if active is not None and cells is not None:
+        raise ValueError("pass active (blocks) or cells, not both")
+    if cells is not None:
+        return _active(cells, nq, "cells"), True
+    return _active(active, nq), False
+
+
 def block_topk(scores, n_blocks, block_size, width, call, active=None, ids=None, counts=None,
-               ws=None, options=None, stream=None):
-    """Selected cell ids [nq, width] (ascending, -1 tail) and counts [nq]."""
+               ws=None, options=None, stream=None, cells=None):
+    """Selected cell ids [nq, width] (ascending, -1 tail) and counts [nq].
+    `cells` ([nq] int32 on the device) gives a visible cell count per query
+    (qsa_block_topk_cells) instead of `active` blocks."""
     _dev(scores, torch.float32, "scores")
     if scores.dim() != 2 or scores.stride(1) != 1:
         raise ValueError("scores must be [nq, ld] with unit column stride")
     nq = scores.shape[0]
     code = _call_code(call)
-    active = _active(active, nq)
+    lengths, by_cells = _lengths(active, cells, nq)
     ids, counts = _topk_outputs(nq, width, scores.device, ids, counts)
     need = topk_workspace_bytes(nq, n_blocks, block_size, width, code, options)
     if ws is None:
         ws = workspace(need, scores.device, stream)
-    _check(lib().qsa_block_topk(_ptr(scores), scores.stride(0), nq, n_blocks, block_size, width, code,
-                                _ptr(active), _ptr(ids), _ptr(counts), _ptr(ws), ws.numel(),
-                                _stream(stream), _opt(options)), "qsa_block_topk")
+    name = "qsa_block_topk_cells" if by_cells else "qsa_block_topk"
+    _check(getattr(lib(), name)(_ptr(scores), scores.stride(0), nq, n_blocks, block_size, width, code,
+                                _ptr(lengths), _ptr(ids), _ptr(counts), _ptr(ws), ws.numel(),
+                                _stream(stream), _opt(options)), name)
     return ids, counts
 
 
 def select(q, k, w, block_size, width, call, scores=None, active=None, ids=None, counts=None,
-           ws=None, options=None, stream=None):
-    """Scores then top-k: returns (scores, ids, counts)."""
+           ws=None, options=None, stream=None, cells=None):
+    """Scores then top-k: returns (scores, ids, counts). `cells` as in block_topk."""
     for t, n in ((q, "q"), (k, "k"), (w, "w")):
         _dev(t, torch.float32, n)
         if not t.is_contiguous():
@@ -239,12 +253,13 @@ def select(q, k, w, block_size, width, call, scores=None, active=None, ids=None,
         scores = torch.empty((nq, n_blocks), dtype=torch.float32, device=q.device)
     _dev(scores, torch.float32, "scores")
     code = _call_code(call)
-    active = _active(active, nq)
+    lengths, by_cells = _lengths(active, cells, nq)
     ids, counts = _topk_outputs(nq, width, q.device, ids, counts)
     need = topk_workspace_bytes(nq, n_blocks, block_size, width, code, options)
     if ws is None:
         ws = workspace(need, q.device, stream)
-    _check(lib().qsa_select(_ptr(q), _ptr(k), _ptr(w), heads, head_dim, _ptr(scores), scores.stride(0), nq,
-                            n_blocks, block_size, width, code, _ptr(active), _ptr(ids), _ptr(counts),
-                            _ptr(ws), ws.numel(), _stream(stream), _opt(options)), "qsa_select")
+    name = "qsa_select_cells" if by_cells else "qsa_select"
+    _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(w), heads, head_dim, _ptr(scores), scores.stride(0), nq,
+                                n_blocks, block_size, width, code, _ptr(lengths), _ptr(ids), _ptr(counts),
+                                _ptr(ws), ws.numel(), _stream(stream), _opt(options)), name)
     return scores, ids, counts

@@ -71,7 +71,9 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
     }
     p.n_chunks = n_blocks > 0 ? (n_blocks + p.chunk_blocks - 1) / p.chunk_blocks : 1;
     p.split_threads = kSplitThreads;
-    const int64_t cap_c = p.r_blocks < p.chunk_blocks ? p.r_blocks : p.chunk_blocks;
+    // Room for one block more per chunk: a query whose last visible block is
+    // partial keeps r + 1 candidates per chunk (qsa_block_topk_cells).
+    const int64_t cap_c = p.r_blocks + 1 < p.chunk_blocks ? p.r_blocks + 1 : p.chunk_blocks;
     plan.cand_stride = ((int64_t)p.n_chunks * (cap_c > 0 ? cap_c : 1) + 3) / 4 * 4;
     p.stage_b_lds = plan.cand_stride <= kStageBLdsWords ? 1 : 0;
 
@@ -113,8 +115,8 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
 namespace {
 
 qsa_status check_topk_args(const float *scores, int64_t ld, int32_t nq, int32_t n_blocks,
-                           qsa_call call, const int32_t *active, const int32_t *ids,
-                           const int32_t *counts)
+                           qsa_call call, const int32_t *active, const int32_t *cells,
+                           const int32_t *ids, const int32_t *counts)
 {
     if (nq > 0 && (!scores || !ids))
         return QSA_EINVAL;
@@ -122,13 +124,15 @@ qsa_status check_topk_args(const float *scores, int64_t ld, int32_t nq, int32_t 
         return QSA_EINVAL;
     if (call == QSA_DECODE && active)
         return QSA_EINVAL;
-    if (!aligned(scores, 4) || !aligned(ids, 4) || !aligned(counts, 4) || !aligned(active, 4))
+    if (!aligned(scores, 4) || !aligned(ids, 4) || !aligned(counts, 4) || !aligned(active, 4) ||
+        !aligned(cells, 4))
         return QSA_EINVAL;
     return QSA_OK;
 }
 
 TopkGeom make_geom(const float *scores, int64_t ld, int32_t nq, int32_t n_blocks, int32_t bs,
-                   int32_t width, const int32_t *active, int32_t *ids, int32_t *counts)
+                   int32_t width, const int32_t *active, const int32_t *cells, int32_t *ids,
+                   int32_t *counts)
 {
     TopkGeom g;
     g.scores = scores;
@@ -138,6 +142,7 @@ TopkGeom make_geom(const float *scores, int64_t ld, int32_t nq, int32_t n_blocks
     g.bs = bs;
     g.width = width;
     g.active = active;
+    g.cells = cells;
     g.ids = ids;
     g.counts = counts;
     g.vec4 = (aligned(scores, 16) && ld % 4 == 0) ? 1 : 0;
@@ -196,6 +201,61 @@ qsa_status check_score_args(const float *q, const float *k, const float *w, cons
 } // namespace qsa
 
 using namespace qsa;
+
+namespace {
+
+qsa_status topk_call(const float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks, int32_t block_size,
+                     int32_t width, qsa_call call, const int32_t *active, const int32_t *cells,
+                     int32_t *cell_ids, int32_t *counts, void *workspace, size_t workspace_bytes,
+                     void *stream, const qsa_options *opt)
+{
+    TopkPlan plan;
+    qsa_status st = make_topk_plan(nq, n_blocks, block_size, width, call, opt, plan);
+    if (st != QSA_OK)
+        return st;
+    st = check_topk_args(scores, ld_scores, nq, n_blocks, call, active, cells, cell_ids, counts);
+    if (st != QSA_OK)
+        return st;
+    if (nq == 0)
+        return QSA_OK;
+    if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < plan.lay.bytes)
+        return QSA_EWORKSPACE;
+    const TopkGeom g = make_geom(scores, ld_scores, nq, n_blocks, block_size, width, active, cells, cell_ids,
+                                 counts);
+    return run_topk(g, plan, workspace, (hipStream_t)stream, opt);
+}
+
+qsa_status select_call(const float *q, const float *k, const float *w, int32_t n_heads, int32_t head_dim,
+                       float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks, int32_t block_size,
+                       int32_t width, qsa_call call, const int32_t *active, const int32_t *cells,
+                       int32_t *cell_ids, int32_t *counts, void *workspace, size_t workspace_bytes,
+                       void *stream, const qsa_options *opt)
+{
+    qsa_status st = check_score_args(q, k, w, scores, ld_scores, nq, n_heads, head_dim, n_blocks);
+    if (st != QSA_OK)
+        return st;
+    TopkPlan plan;
+    st = make_topk_plan(nq, n_blocks, block_size, width, call, opt, plan);
+    if (st != QSA_OK)
+        return st;
+    st = check_topk_args(scores, ld_scores, nq, n_blocks, call, active, cells, cell_ids, counts);
+    if (st != QSA_OK)
+        return st;
+    if (nq == 0)
+        return QSA_OK;
+    if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < plan.lay.bytes)
+        return QSA_EWORKSPACE;
+    if (n_blocks > 0) {
+        ScoreArgs a{q, k, w, scores, ld_scores, nq, n_heads, n_blocks};
+        if (launch_scores(a, (hipStream_t)stream) != hipSuccess)
+            return QSA_EHIP;
+    }
+    const TopkGeom g = make_geom(scores, ld_scores, nq, n_blocks, block_size, width, active, cells, cell_ids,
+                                 counts);
+    return run_topk(g, plan, workspace, (hipStream_t)stream, opt);
+}
+
+} // namespace
 
 extern "C" {
 
@@ -258,20 +318,18 @@ qsa_status qsa_block_topk(const float *scores, int64_t ld_scores, int32_t nq, in
                           void *workspace, size_t workspace_bytes, void *stream,
                           const qsa_options *opt)
 {
-    TopkPlan plan;
-    qsa_status st = make_topk_plan(nq, n_blocks, block_size, width, call, opt, plan);
-    if (st != QSA_OK)
-        return st;
-    st = check_topk_args(scores, ld_scores, nq, n_blocks, call, active_blocks, cell_ids, counts);
-    if (st != QSA_OK)
-        return st;
-    if (nq == 0)
-        return QSA_OK;
-    if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < plan.lay.bytes)
-        return QSA_EWORKSPACE;
-    const TopkGeom g = make_geom(scores, ld_scores, nq, n_blocks, block_size, width, active_blocks,
-                                 cell_ids, counts);
-    return run_topk(g, plan, workspace, (hipStream_t)stream, opt);
+    return topk_call(scores, ld_scores, nq, n_blocks, block_size, width, call, active_blocks, nullptr,
+                     cell_ids, counts, workspace, workspace_bytes, stream, opt);
+}
+
+qsa_status qsa_block_topk_cells(const float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks,
+                                int32_t block_size, int32_t width, qsa_call call,
+                                const int32_t *visible_cells, int32_t *cell_ids, int32_t *counts,
+                                void *workspace, size_t workspace_bytes, void *stream,
+                                const qsa_options *opt)
+{
+    return topk_call(scores, ld_scores, nq, n_blocks, block_size, width, call, nullptr, visible_cells,
+                     cell_ids, counts, workspace, workspace_bytes, stream, opt);
 }
 
 qsa_status qsa_select(const float *q, const float *k, const float *w, int32_t n_heads,
@@ -281,28 +339,19 @@ qsa_status qsa_select(const float *q, const float *k, const float *w, int32_t n_
                       void *workspace, size_t workspace_bytes, void *stream,
                       const qsa_options *opt)
 {
-    qsa_status st = check_score_args(q, k, w, scores, ld_scores, nq, n_heads, head_dim, n_blocks);
-    if (st != QSA_OK)
-        return st;
-    TopkPlan plan;
-    st = make_topk_plan(nq, n_blocks, block_size, width, call, opt, plan);
-    if (st != QSA_OK)
-        return st;
-    st = check_topk_args(scores, ld_scores, nq, n_blocks, call, active_blocks, cell_ids, counts);
-    if (st != QSA_OK)
-        return st;
-    if (nq == 0)
-        return QSA_OK;
-    if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < plan.lay.bytes)
-        return QSA_EWORKSPACE;
-    if (n_blocks > 0) {
-        ScoreArgs a{q, k, w, scores, ld_scores, nq, n_heads, n_blocks};
-        if (launch_scores(a, (hipStream_t)stream) != hipSuccess)
-            return QSA_EHIP;
-    }
-    const TopkGeom g = make_geom(scores, ld_scores, nq, n_blocks, block_size, width, active_blocks,
-                                 cell_ids, counts);
-    return run_topk(g, plan, workspace, (hipStream_t)stream, opt);
+    return select_call(q, k, w, n_heads, head_dim, scores, ld_scores, nq, n_blocks, block_size, width, call,
+                       active_blocks, nullptr, cell_ids, counts, workspace, workspace_bytes, stream, opt);
+}
+
+qsa_status qsa_select_cells(const float *q, const float *k, const float *w, int32_t n_heads,
+                            int32_t head_dim, float *scores, int64_t ld_scores, int32_t nq,
+                            int32_t n_blocks, int32_t block_size, int32_t width, qsa_call call,
+                            const int32_t *visible_cells, int32_t *cell_ids, int32_t *counts,
+                            void *workspace, size_t workspace_bytes, void *stream,
+                            const qsa_options *opt)
+{
+    return select_call(q, k, w, n_heads, head_dim, scores, ld_scores, nq, n_blocks, block_size, width, call,
+                       nullptr, visible_cells, cell_ids, counts, workspace, workspace_bytes, stream, opt);
 }
 
 } // extern "C"

@@ -52,7 +52,8 @@ struct TopkGeom {
     int32_t n_blocks;
     int32_t bs;
     int32_t width;
-    const int32_t *active;  // nullable
+    const int32_t *active;  // nullable: visible blocks per query
+    const int32_t *cells;   // nullable: visible cells per query (the last visible block may be partial)
     int32_t *ids;
     int32_t *counts;        // nullable
     int32_t vec4;           // rows are 16-byte aligned (float4 loads allowed)

@@ -416,6 +416,32 @@ __device__ __forceinline__ void radix_select_range(const Src &src, int n, uint32
     n_above = above;
 }
 
+// Sum over the workgroup of one value per thread (all threads call).
+template <int NT>
+__device__ __forceinline__ uint32_t wg_sum(uint32_t v, SelectShared<NT> &sh)
+{
+    constexpr int NW = NT / kWave;
+    v = wave_sum(v);
+    if (lane_id() == 0)
+        sh.red[0][wave_id()] = v;
+    lds_barrier();
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        t += sh.red[0][w];
+    lds_barrier();
+    return t;
+}
+
+// Number of keys of src[0..n) that are >= kp (all threads call).
+template <int NT, class Src>
+__device__ __forceinline__ uint32_t count_at_least(const Src &src, int n, uint32_t kp, SelectShared<NT> &sh)
+{
+    uint32_t c = 0;
+    for_each_key<NT>(src, n, [&](uint32_t k) { c += k >= kp ? 1u : 0u; });
+    return wg_sum<NT>(c, sh);
+}
+
 // Min and max key of src[0..n).
 template <int NT, class Src>
 __device__ __forceinline__ void key_range(const Src &src, int n, SelectShared<NT> &sh, uint32_t &mn, uint32_t &mx)

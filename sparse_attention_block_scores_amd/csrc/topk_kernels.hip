@@ -35,25 +35,56 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct QuerySel {
     int n_vis;      // visible blocks
-    int wq;         // cells selected: min(width, n_vis * bs)
-    int r;          // blocks the selection touches: ceil(wq / bs)
+    int wq;         // cells selected: min(width, visible cells)
+    int r;          // blocks the selection touches, every block taken whole
     int last_unit;  // cells of the last block in (key desc, block asc) order
+    int tail;       // cells of the last visible block when it is partial, else 0
 };
+
+// r and last_unit of a selection of w cells from whole blocks of bs cells.
+__device__ __forceinline__ void set_width(QuerySel &s, int w, int bs)
+{
+    s.r = (w + bs - 1) / bs;
+    s.last_unit = s.r > 0 ? w - bs * (s.r - 1) : 0;
+}
 
 __device__ __forceinline__ QuerySel query_sel(const TopkGeom &g, int q)
 {
     QuerySel s;
-    int nv = g.n_blocks;
-    if (g.active) {
-        const int a = g.active[q];
-        nv = a < 0 ? 0 : (a > g.n_blocks ? g.n_blocks : a);
+    int64_t cells;
+    if (g.cells) {
+        const int64_t all = (int64_t)g.n_blocks * g.bs;
+        const int64_t c = g.cells[q];
+        cells = c < 0 ? 0 : (c > all ? all : c);
+        s.n_vis = (int)((cells + g.bs - 1) / g.bs);
+        s.tail = (int)(cells % g.bs);
+    } else {
+        int nv = g.n_blocks;
+        if (g.active) {
+            const int a = g.active[q];
+            nv = a < 0 ? 0 : (a > g.n_blocks ? g.n_blocks : a);
+        }
+        s.n_vis = nv;
+        s.tail = 0;
+        cells = (int64_t)nv * g.bs;
     }
-    s.n_vis = nv;
-    const int64_t cells = (int64_t)nv * g.bs;
     s.wq = (int)(cells < g.width ? cells : (int64_t)g.width);
-    s.r = (s.wq + g.bs - 1) / g.bs;
-    s.last_unit = s.r > 0 ? s.wq - g.bs * (s.r - 1) : 0;
+    set_width(s, s.wq, g.bs);
     return s;
+}
+
+// A partial last visible block p (qs.tail cells). Counted as a whole block,
+// p is the last of the blocks with its key in (key desc, block asc) order, so
+// whole-block cells precede it exactly for the n_ge - 1 other blocks with key
+// >= key(p). If fewer than wq such cells precede it, p is taken, and the
+// selection is the whole-block selection of wq + bs - tail cells cut to its
+// first wq cells in cell order (p's cells past the visible ones are the
+// highest ids); otherwise p is not taken and the whole-block selection of wq
+// cells is the selection. Every emit writes at most qs.wq cells.
+__device__ __forceinline__ void widen_for_tail(QuerySel &qs, int bs, uint32_t n_ge)
+{
+    if (qs.tail != 0 && n_ge >= 1 && (int64_t)(n_ge - 1) * bs < qs.wq)
+        set_width(qs, qs.wq + bs - qs.tail, bs);
 }
 
 template <int NT>
@@ -149,7 +180,7 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
     const TopkGeom g = a.g;
     const int q = blockIdx.y;
     const int c = blockIdx.x;
-    const QuerySel qs = query_sel(g, q);
+    QuerySel qs = query_sel(g, q);
     if (qs.r == 0) {
         if (c == 0)
             write_empty<NT>(g, q);
@@ -166,19 +197,25 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
     const LdsKeys lds{s_keys};
 
     if (nchq == 1) {
+        if (qs.tail != 0)
+            widen_for_tail(qs, g.bs, count_at_least<NT>(lds, nc, s_keys[nc - 1], sh));
         select_cells<NT>(lds, nc, qs, [&](int i) { return b0 + i; }, g, q, sh);
         return;
     }
 
-    // Stage A: this chunk's top-r blocks in block order.
-    const int cap_q = min(qs.r, a.chunk);
+    // Stage A: this chunk's top-r_a blocks in block order. A query with a
+    // partial last block keeps one block more: its selection may take one
+    // more whole block (widen_for_tail), and with r_a = r + 1 the candidates
+    // decide exactly whether that block is taken (stage B).
+    const int r_a = qs.r + (qs.tail != 0 ? 1 : 0);
+    const int cap_q = min(r_a, a.chunk);
     uint32_t *ckey = a.cand_keys + (int64_t)q * a.cand_stride + (int64_t)c * cap_q;
     int32_t *cblk = a.cand_blocks + (int64_t)q * a.cand_stride + (int64_t)c * cap_q;
-    uint32_t T = 0, budget = (uint32_t)nc;  // a chunk no larger than r is kept whole
-    if (nc > qs.r) {
+    uint32_t T = 0, budget = (uint32_t)nc;  // a chunk no larger than r_a is kept whole
+    if (nc > r_a) {
         uint32_t above;
-        radix_select<NT>(lds, nc, (uint32_t)qs.r, sh, T, above);
-        budget = (uint32_t)qs.r - above;
+        radix_select<NT>(lds, nc, (uint32_t)r_a, sh, T, above);
+        budget = (uint32_t)r_a - above;
     }
     ordered_take<NT>(lds, nc, T, budget, 1u, 1u, sh, [&](int i, uint32_t pos, uint32_t) {
         if (pos < (uint32_t)cap_q) {
@@ -188,7 +225,7 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
     });
     if (threadIdx.x == 0) {
         uint32_t *m = a.meta + ((int64_t)q * a.n_chunks + c) * 2;
-        m[0] = (uint32_t)min(nc, qs.r);
+        m[0] = (uint32_t)min(nc, r_a);
         m[1] = T;
     }
     if (!last_to_arrive(&a.tickets[q], (uint32_t)nchq, s_flag))
@@ -196,10 +233,15 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
 
     // Stage B: candidates of all chunks, contiguous and in block order (every
     // chunk but the last is full).
-    const int last_n = min(qs.r, qs.n_vis - (nchq - 1) * a.chunk);
+    const int last_n = min(r_a, qs.n_vis - (nchq - 1) * a.chunk);
     const int total = (nchq - 1) * cap_q + last_n;
     const uint32_t *gkey = a.cand_keys + (int64_t)q * a.cand_stride;
     const int32_t *gblk = a.cand_blocks + (int64_t)q * a.cand_stride;
+    // A partial last block: count the candidates at or above its key. If it is
+    // taken, every block with key >= its key is among the top r_a of its chunk,
+    // so the count is exact; if it is not, the count still shows that (a chunk
+    // that drops such a block holds r_a candidates above it).
+    const uint32_t kp = qs.tail != 0 ? key_of(g.scores[(int64_t)q * g.ld + qs.n_vis - 1]) : 0u;
     if (total <= a.blk_words) {
         // Keys and block ids both to LDS: the emit then reads no global memory.
         int32_t *s_blks = reinterpret_cast<int32_t *>(s_keys + a.lds_words);
@@ -213,8 +255,12 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
             s_blks[i] = gblk[i];
         }
         lds_barrier();
+        if (qs.tail != 0)
+            widen_for_tail(qs, g.bs, count_at_least<NT>(lds, total, kp, sh));
         select_cells<NT>(lds, total, qs, [&](int i) { return s_blks[i]; }, g, q, sh);
     } else {
+        if (qs.tail != 0)
+            widen_for_tail(qs, g.bs, count_at_least<NT>(GlobalKeys{gkey}, total, kp, sh));
         select_cells<NT>(GlobalKeys{gkey}, total, qs, [&](int i) { return gblk[i]; }, g, q, sh);
     }
     if (threadIdx.x == 0)
@@ -308,12 +354,13 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     __shared__ uint32_t s_ssrc[MAXS];   // ... where they start in the list of ...
     __shared__ uint32_t s_swave[MAXS];  // ... this wave
     __shared__ uint32_t s_next;         // next slice to claim
+    __shared__ uint32_t s_gcnt[NW];     // candidates at or above a partial last block's key
     __shared__ uint32_t s_wtot[NW];
     __shared__ uint32_t s_wmax[NW];
 
     const TopkGeom g = a.g;
     const int q = blockIdx.x;
-    const QuerySel qs = query_sel(g, q);
+    QuerySel qs = query_sel(g, q);
     if (qs.r == 0) {
         write_empty<NT>(g, q);
         return;
@@ -321,6 +368,10 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     const int n = qs.n_vis;
     const float *row = g.scores + (int64_t)q * g.ld;
     const int lane = lane_id(), wid = wave_id();
+    // Key of a partial last block (see widen_for_tail), and the cells the
+    // candidates must hold in that case: the selection may take it whole.
+    const uint32_t kp = qs.tail != 0 ? key_of(row[n - 1]) : 0u;
+    const int64_t w_need = (int64_t)qs.wq + (qs.tail != 0 ? g.bs - qs.tail : 0);
 
     // Sample of the block keys for the bound.
     int ns;
@@ -493,7 +544,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         over = over || c > (uint32_t)WCAP;
         kmax = max(kmax, s_wmax[w]);
     }
-    if (!a.force_flag && !over && (uint64_t)total * (uint64_t)g.bs >= (uint64_t)qs.wq) {
+    if (!a.force_flag && !over && (int64_t)total * g.bs >= w_need) {
         // Every candidate key lies in [kmin, kmax]; the copy into block order
         // also counts the top kFineBits bits of (key - kmin) into the fine
         // bins and their coarse bins.
@@ -522,6 +573,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
         const uint32_t wtot = s_wtot[wid];
+        uint32_t gcnt = 0;
         // Four items per lane per round, all reads issued before any write.
         for (uint32_t i0 = (uint32_t)lane; i0 < wtot; i0 += 4 * kWave) {
             int32_t blk[4];
@@ -544,6 +596,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
                     const uint32_t d = i0 + u * kWave + shift[u];
                     s_ckey[d] = k;
                     s_cblk[d] = blk[u];
+                    gcnt += k >= kp ? 1u : 0u;
                     if (span != 0) {
                         const uint32_t fb = (k - kmin) >> sF;
                         lds_add(&sh.fine[fb], 1u);
@@ -552,7 +605,20 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
                 }
             }
         }
+        gcnt = wave_sum(gcnt);
+        if (lane == 0)
+            s_gcnt[wid] = gcnt;
         lds_barrier();
+        if (qs.tail != 0) {
+            // The partial last block is a candidate iff its key is >= kmin, and
+            // then every block at or above its key is one; if it is not, it is
+            // below the threshold (the candidates hold w_need cells).
+            uint32_t n_ge = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                n_ge += s_gcnt[w];
+            widen_for_tail(qs, g.bs, kp >= kmin ? n_ge : 0xFFFFFFFFu);
+        }
 
         // Threshold: the fine bin holding rank r usually holds a handful of
         // keys, which one wave ranks exactly; a crowded one goes on with radix
@@ -578,6 +644,8 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         return;
     }
     // Flagged: the exact rule over the whole row, read from global memory.
+    if (qs.tail != 0)
+        widen_for_tail(qs, g.bs, count_at_least<NT>(RowKeys{row, VEC}, n, kp, sh));
     select_cells<NT>(RowKeys{row, VEC}, n, qs, [&](int i) { return i; }, g, q, sh);
 }
 

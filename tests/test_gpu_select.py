@@ -54,3 +54,21 @@ def test_prompt_select_random_active_counts():
     active = synth.integers("gpu/sel/active/n", wl.nq, 0, wl.n_blocks).astype(np.int32)
     (q, k, w), s, ids, counts = run_select(wl, active=active)
     assert_ids_equal((ids, counts), oracle.topk_sort(s, wl.n_blocks, 4, 2048, active), "active")
+
+
+@pytest.mark.parametrize("make", [synth.c1, synth.c3])
+def test_decode_select_cells(make):
+    """qsa_select_cells: visible lengths that end inside a block."""
+    wl = make()
+    q, k, w = wl.tensors()
+    full = wl.n_blocks * wl.block_size
+    cells = np.array([full - 1 - (i % 3) - 97 * i for i in range(wl.nq)], np.int32)
+    say(f"select_cells {wl.name} nq={wl.nq} nb={wl.n_blocks}")
+    scores, ids, counts = qsa.select(to_dev(q), to_dev(k), to_dev(w), wl.block_size, wl.width, wl.call,
+                                     cells=to_dev(cells))
+    torch.cuda.synchronize()
+    s = scores.cpu().numpy()
+    got = (ids.cpu().numpy(), counts.cpu().numpy())
+    assert_ids_equal(got, oracle.topk_sort_cells(s, wl.n_blocks, wl.block_size, wl.width, cells),
+                     f"{wl.name} cells")
+    assert_scores_close(s, oracle.block_scores(q, k, w), wl.name)

@@ -205,3 +205,124 @@ def test_misaligned_rows_and_empty_contexts():
     s = to_dev(np.zeros((2, 4), np.float32))
     ids, counts = qsa.block_topk(s, 0, 4, 16, "decode")
     assert (ids.cpu().numpy() == -1).all() and (counts.cpu().numpy() == 0).all()
+
+
+# ------------------------------------------------- cell-granular visible length
+def gpu_topk_cells(scores, n_blocks, bs, width, call, cells, options=None, ws=None):
+    s = to_dev(scores)
+    c = to_dev(np.asarray(cells, np.int32))
+    ids, counts = qsa.block_topk(s, n_blocks, bs, width, call, cells=c, options=options, ws=ws)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), counts.cpu().numpy()
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_cells_hand_cases(path):
+    g = json.load(open(os.path.join(GOLDEN, "topk_cells_hand.json")))
+    for case in g["cases"]:
+        keys = np.array([case["keys"]], np.float32)
+        for call in ("decode", "prompt"):
+            if path.startswith(("oneread", "fallback")) and call == "decode":
+                continue
+            say(f"cells hand {case['name']} {call} path={path}")
+            ids, counts = gpu_topk_cells(keys, keys.shape[1], case["block_size"], case["width"], call,
+                                         [case["cells"]], options=_opts(path))
+            assert ids[0].tolist() == case["ids"], (case["name"], call)
+            assert counts[0] == case["count"], (case["name"], call)
+
+
+def _cells_cases():
+    rng = np.random.default_rng(20261203)
+    variants = ["normal", "q64", "equal", "few", "sorted", "narrow"]
+    sizes = [1, 2, 5, 64, 65, 333, 1000, 4104, 4105, 9000, 30000]
+    out = []
+    for i in range(48):
+        nb = int(sizes[i % len(sizes)])
+        bs = int(rng.choice([2, 3, 4, 4, 7]))
+        width = int(rng.choice([1, 5, 64, 777, 2048, 5000]))
+        nq = int(rng.choice([1, 3, 5]))
+        variant = variants[i % len(variants)]
+        call = "prompt" if i % 3 else "decode"
+        path = list(PATHS)[i % len(PATHS)]
+        if call == "decode" and path.startswith(("oneread", "fallback")):
+            path = "auto"
+        out.append(pytest.param(i, nb, bs, width, nq, variant, call, path,
+                                id=f"{i}-nb{nb}-bs{bs}-w{width}-nq{nq}-{variant}-{call}-{path}"))
+    return out
+
+
+@pytest.mark.parametrize("i,n_blocks,bs,width,nq,variant,call,path", _cells_cases())
+def test_cells_random_cases(i, n_blocks, bs, width, nq, variant, call, path):
+    ld = n_blocks + (i % 5)
+    s = _keys(f"gpu/topk/cells/{i}", variant, nq, n_blocks, ld)
+    full = n_blocks * bs
+    cells = synth.integers(f"gpu/topk/cells/{i}/n", nq, -3, full + 5).astype(np.int32)
+    cells[0] = max(full - 1, 0)  # a partial last block whenever bs > 1
+    say(f"cells case {i} nb={n_blocks} bs={bs} w={width} nq={nq} {variant} {call} {path}")
+    got = gpu_topk_cells(s, n_blocks, bs, width, call, cells, options=_opts(path))
+    exp = oracle.topk_sort_cells(s, n_blocks, bs, width, cells)
+    assert_ids_equal(got, exp, f"cells case {i}")
+
+
+@pytest.mark.parametrize("n_blocks", synth.C2_BLOCKS)
+def test_cells_decode_contexts_full_size(n_blocks):
+    """C2 rows cut one to three cells short of a block boundary, and at random."""
+    wl = synth.c2(n_blocks)
+    s = wl.scores()
+    full = n_blocks * wl.block_size
+    cells = np.array([full - 1, full - 3, full - 4 * 999 - 2], np.int32)
+    exp = oracle.topk_sort_cells(s, n_blocks, wl.block_size, wl.width, cells)
+    for path in ("auto", "split64"):
+        say(f"C2 cells nb={n_blocks} path={path}")
+        got = gpu_topk_cells(s, n_blocks, wl.block_size, wl.width, "decode", cells, options=_opts(path))
+        assert_ids_equal(got, exp, f"C2 cells nb={n_blocks} {path}")
+
+
+@pytest.mark.parametrize("variant", ["continuous", "q64"])
+def test_cells_prompt_full_size(variant):
+    n_blocks = 130048
+    wl = synth.c4(n_blocks, variant)
+    s = wl.scores()
+    full = n_blocks * wl.block_size
+    cells = synth.integers(f"gpu/topk/cells/c4/{variant}", wl.nq, full // 2, full).astype(np.int32)
+    cells[::3] = full - 1 - (np.arange(0, wl.nq, 3) % 3)  # partial last blocks
+    rows = np.arange(0, wl.nq, 17)
+    exp = oracle.topk_sort_cells(s[rows], n_blocks, wl.block_size, wl.width, cells[rows])
+    for path in ("auto", "split"):
+        say(f"C4 cells {variant} path={path}")
+        got = gpu_topk_cells(s, n_blocks, wl.block_size, wl.width, "prompt", cells, options=_opts(path))
+        assert_ids_equal(got, exp, f"C4 cells {variant} {path}", rows=rows)
+
+
+def test_cells_length_changes_between_graph_replays():
+    """The visible length lives on the device: one captured call, replayed
+    with new lengths written into the same buffer, follows every change."""
+    dev = device()
+    nq, nb, bs, width = 3, 20000, 4, 2048
+    s = to_dev(_keys("gpu/topk/cells/graph", "normal", nq, nb, nb))
+    host = s.cpu().numpy()
+    cells = torch.full((nq,), nb * bs, dtype=torch.int32, device=dev)
+    ws = qsa.workspace(qsa.topk_workspace_bytes(nq, nb, bs, width, "decode"), dev)
+    ids = torch.empty((nq, width), dtype=torch.int32, device=dev)
+    counts = torch.empty((nq,), dtype=torch.int32, device=dev)
+    say("cells graph: warm-up")
+    qsa.block_topk(s, nb, bs, width, "decode", ids=ids, counts=counts, ws=ws, cells=cells)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream(device=dev)
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            qsa.block_topk(s, nb, bs, width, "decode", ids=ids, counts=counts, ws=ws, cells=cells,
+                           stream=stream)
+    torch.cuda.synchronize()
+    for j, lengths in enumerate(([nb * bs, nb * bs - 1, 17], [79999, 40001, 2], [5, 0, 12345],
+                                 [nb * bs - 3, nb * bs - 2, nb * bs - 1])):
+        cells.copy_(torch.tensor(lengths, dtype=torch.int32))
+        torch.cuda.synchronize()
+        say(f"cells graph replay {j} lengths={lengths}")
+        graph.replay()
+        torch.cuda.synchronize()
+        exp = oracle.topk_sort_cells(host, nb, bs, width, np.array(lengths, np.int32))
+        assert_ids_equal((ids.cpu().numpy(), counts.cpu().numpy()), exp, f"graph replay {j}")
+
