@@ -405,6 +405,9 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
                 v[j].z = row[i0 + 2 < n ? i0 + 2 : 0];
                 v[j].w = row[i0 + 3 < n ? i0 + 3 : 0];
             }
+            // Issue order = use order: loads complete in order, so a load
+            // the scheduler moved ahead would make the first use wait for it.
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -424,10 +427,11 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     float4 buf[NBUF][F4];
     int cs[NBUF];  // slice in each buffer (wave-uniform)
 #pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
+    for (int u = 0; u < NBUF; ++u)
         cs[u] = u * NW + wid;
-        load_slice(cs[u], buf[u]);  // in flight while the bound is found
-    }
+    // Only the first slice goes out before the bound: a wave stalls while
+    // the memory queue is full, and the bound needs every wave.
+    load_slice(cs[0], buf[0]);
     if (threadIdx.x == 0)
         s_next = NBUF * NW;
     lds_barrier();
@@ -438,6 +442,9 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     // largest kept float has the largest key.
     const float fbound = use_bound ? sample_bound<NT>(smp, ns, ks, sh) : -__builtin_inff();
     clear_hists<NT>(sh);  // ordered before their next use by the barrier after the stream
+#pragma unroll
+    for (int u = 1; u < NBUF; ++u)
+        load_slice(cs[u], buf[u]);
 
     uint32_t wcnt = 0;               // wave-uniform
     float fmx = -__builtin_inff();   // largest value this lane kept
@@ -620,6 +627,26 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             widen_for_tail(qs, g.bs, kp >= kmin ? n_ge : 0xFFFFFFFFu);
         }
 
+        // Each thread holds the candidates [PER*t, PER*t + PER) of the block
+        // order in registers from here on: the threshold's gather and the
+        // emit both use them without another pass over the LDS.
+        constexpr int PER = kOneReadCap / NT;
+        static_assert(PER % 4 == 0, "16-byte reads of each thread's candidates");
+        uint32_t ck[PER];
+        int32_t cb[PER];
+        bool cv[PER];
+        const int c0 = (int)threadIdx.x * PER;
+#pragma unroll
+        for (int v = 0; v < PER / 4; ++v) {
+            const uint4 kk = *reinterpret_cast<const uint4 *>(s_ckey + c0 + 4 * v);
+            const int4 bb = *reinterpret_cast<const int4 *>(s_cblk + c0 + 4 * v);
+            ck[4 * v] = kk.x; ck[4 * v + 1] = kk.y; ck[4 * v + 2] = kk.z; ck[4 * v + 3] = kk.w;
+            cb[4 * v] = bb.x; cb[4 * v + 1] = bb.y; cb[4 * v + 2] = bb.z; cb[4 * v + 3] = bb.w;
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            cv[j] = c0 + j < (int)total;
+
         // Threshold: the fine bin holding rank r usually holds a handful of
         // keys, which one wave ranks exactly; a crowded one goes on with radix
         // digits over its keys.
@@ -631,16 +658,72 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             const uint32_t bspan = sF == 0 ? 0u : min(span - (b << sF), (1u << sF) - 1u);
             const uint32_t r2 = (uint32_t)qs.r - h;
             uint32_t a2 = 0;
-            if (bspan == 0)
+            if (bspan == 0) {
                 T = blo;
-            else if (c <= (uint32_t)kWave)
-                rank_members<NT>(LdsKeys{s_ckey}, (int)total, [&](uint32_t k) { return k - blo <= bspan; }, c, r2,
-                                 sh, T, a2);
-            else
+            } else if (c <= (uint32_t)kWave) {
+                // The bin's keys into sh.small, then one wave ranks them.
+#pragma unroll
+                for (int j = 0; j < PER; ++j) {
+                    if (cv[j] && ck[j] - blo <= bspan) {
+                        const uint32_t pos =
+                            __hip_atomic_fetch_add(&sh.small_n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                        if (pos < (uint32_t)kWave)
+                            sh.small[pos] = ck[j];
+                    }
+                }
+                lds_barrier();
+                wave_rank_small(sh.small, c, r2, T, a2);
+            } else {
                 radix_select_range<NT>(LdsKeys{s_ckey}, (int)total, r2, blo, blo + bspan, sh, T, a2);
+            }
             above = h + a2;
         }
-        emit_selection<NT>(LdsKeys{s_ckey}, (int)total, qs, [&](int i) { return s_cblk[i]; }, g, q, sh, T, above);
+
+        // Emit: one workgroup scan of (blocks above T, blocks equal to T) in
+        // block order gives every taken block its output slot: bs cells per
+        // taken block, except the last tie taken (rank budget - 1), which
+        // takes last_unit cells and moves every later block down.
+        const uint32_t budget = (uint32_t)qs.r - above;  // >= 1
+        uint32_t gt = 0, tie = 0;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            gt += cv[j] && ck[j] > T ? 1u : 0u;
+            tie += cv[j] && ck[j] == T ? 1u : 0u;
+        }
+        const uint32_t packed = gt | (tie << 16);  // both <= kOneReadCap < 2^16
+        const uint32_t incl = wave_incl_sum(packed);
+        if (lane == kWave - 1)
+            sh.red[0][wid] = incl;
+        lds_barrier();
+        uint32_t before = incl - packed;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            before += w < wid ? sh.red[0][w] : 0u;
+        uint32_t ties_before = before >> 16;
+        const uint32_t bs = (uint32_t)g.bs;
+        const uint32_t shortfall = bs - (uint32_t)qs.last_unit;
+        const uint32_t limit = (uint32_t)qs.wq;
+        int32_t *out = g.ids + (int64_t)q * g.width;
+        uint32_t pos = bs * ((before & 0xFFFFu) + min(ties_before, budget)) - (ties_before >= budget ? shortfall : 0u);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            uint32_t cells = 0;
+            if (cv[j] && ck[j] > T) {
+                cells = bs;
+            } else if (cv[j] && ck[j] == T) {
+                if (ties_before < budget)
+                    cells = ties_before == budget - 1u ? (uint32_t)qs.last_unit : bs;
+                ++ties_before;
+            }
+            if (cells != 0u) {
+                write_cells(out, pos, cells, cb[j] * (int32_t)bs, limit);
+                pos += cells;
+            }
+        }
+        for (int p = qs.wq + (int)threadIdx.x; p < g.width; p += NT)
+            out[p] = -1;
+        if (g.counts && threadIdx.x == 0)
+            g.counts[q] = qs.wq;
         return;
     }
     // Flagged: the exact rule over the whole row, read from global memory.
