@@ -91,7 +91,8 @@ typedef struct qsa_options {
     int32_t sample;         /* QSA_SAMPLE_* */
     int32_t force_fallback; /* ONEREAD: every query takes the exact fallback over its whole row */
     int32_t oneread_blocks; /* ONEREAD blocks streamed per batch: 0 or 16384 (others QSA_EUNSUPPORTED) */
-    int32_t reserved[3];    /* must be zero */
+    int32_t oneread_parts;  /* ONEREAD workgroups per query: 0 = auto, else 1..16 */
+    int32_t reserved[2];    /* must be zero */
 } qsa_options;
 
 /* The launch plan the top-k would use; exported so host code and tests can
@@ -104,7 +105,7 @@ typedef struct qsa_topk_plan {
     int32_t split_threads;   /* SPLIT workgroup size */
     int32_t stage_b_lds;     /* 1 if stage B keeps its candidates in LDS */
     int32_t oneread_blocks;  /* ONEREAD blocks streamed per batch */
-    int32_t oneread_groups;  /* ONEREAD workgroups per query (1) */
+    int32_t oneread_groups;  /* ONEREAD workgroups per query (parts of the row; >1 hands off in the workspace) */
     int32_t cap;             /* ONEREAD candidate cap per query (blocks) */
     int32_t sample_stride;   /* 32 */
     int32_t sample_mode;     /* QSA_SAMPLE_STRIDE or QSA_SAMPLE_LINES */

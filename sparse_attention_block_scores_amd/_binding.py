@@ -37,7 +37,8 @@ class Options(ctypes.Structure):
         ("sample", ctypes.c_int32),
         ("force_fallback", ctypes.c_int32),
         ("oneread_blocks", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 3),
+        ("oneread_parts", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 

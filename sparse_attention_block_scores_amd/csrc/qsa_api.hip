@@ -20,7 +20,7 @@ qsa_status check_options(const qsa_options *opt)
 {
     if (!opt)
         return QSA_OK;
-    for (int i = 0; i < 3; ++i)
+    for (int i = 0; i < 2; ++i)
         if (opt->reserved[i] != 0)
             return QSA_EINVAL;
     if (opt->topk_path < QSA_PATH_AUTO || opt->topk_path > QSA_PATH_ONEREAD)
@@ -34,6 +34,8 @@ qsa_status check_options(const qsa_options *opt)
         return QSA_EINVAL;
     if (opt->oneread_blocks != 0 && opt->oneread_blocks != kOneReadBatch)
         return QSA_EUNSUPPORTED;
+    if (opt->oneread_parts < 0 || opt->oneread_parts > kOneReadMaxParts)
+        return QSA_EINVAL;
     return QSA_OK;
 }
 
@@ -77,18 +79,26 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
     plan.cand_stride = ((int64_t)p.n_chunks * (cap_c > 0 ? cap_c : 1) + 3) / 4 * 4;
     p.stage_b_lds = plan.cand_stride <= kStageBLdsWords ? 1 : 0;
 
-    // One-read geometry: one workgroup per query streaming batches of blocks.
+    // One-read geometry: each query's row streams in batches of blocks, by
+    // one workgroup, or by several parts (one workgroup each) that hand their
+    // candidates to the last of them. Parts are opt-in: measured on MI355X,
+    // the hand-off (device-coherent stores, a ticket, one load round trip
+    // per part) costs about what the shorter stream saves at the decode
+    // contexts.
     p.oneread_blocks = kOneReadBatch;
-    p.oneread_groups = 1;
+    p.oneread_groups = (opt && opt->oneread_parts) ? opt->oneread_parts : 1;
     p.cap = kOneReadCap;
     p.sample_stride = kSampleStride;
     p.sample_mode = (opt && opt->sample) ? opt->sample : QSA_SAMPLE_LINES;
     p.ks = 2 * p.r_blocks / kSampleStride + 16;
 
-    // Dispatch.
+    // Dispatch (measured on MI355X; results never depend on it). A row that
+    // fits one chunk is selected in LDS by one workgroup. Longer rows take the
+    // one-read path while its candidates are a small share of the row (the
+    // bound keeps about 3r blocks); otherwise the split.
     int path = opt ? opt->topk_path : QSA_PATH_AUTO;
     if (path == QSA_PATH_AUTO)
-        path = (call == QSA_PROMPT && n_blocks >= kOneReadMinBlocks && nq >= kOneReadMinQueries)
+        path = (n_blocks > kChunkBound && (int64_t)n_blocks >= (int64_t)kOneReadMinRatio * p.r_blocks)
                    ? QSA_PATH_ONEREAD
                    : QSA_PATH_SPLIT;
     if (path == QSA_PATH_ONEREAD && n_blocks > kOneReadMaxBatches * kOneReadBatch)
@@ -101,9 +111,12 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
     if (path == QSA_PATH_SPLIT) {
         const size_t q = (size_t)(nq > 0 ? nq : 1);
         L.split_tickets = off; off = align_up(off + q * 4);
-        L.split_meta = off;    off = align_up(off + q * (size_t)p.n_chunks * 8);
         L.split_keys = off;    off = align_up(off + q * (size_t)plan.cand_stride * 4);
         L.split_blocks = off;  off = align_up(off + q * (size_t)plan.cand_stride * 4);
+    } else if (p.oneread_groups > 1) {
+        const size_t q = (size_t)(nq > 0 ? nq : 1);
+        L.part_tickets = off; off = align_up(off + q * 4);
+        L.part_slots = off;   off = align_up(off + q * (size_t)p.oneread_groups * kPartWords * 4);
     } else {
         off = kAlign;  // nothing is kept; a minimal non-empty workspace
     }
@@ -161,13 +174,15 @@ qsa_status run_topk(const TopkGeom &g, const TopkPlan &plan, void *ws, hipStream
         oa.g = g;
         oa.mode = p.sample_mode;
         oa.force_flag = (opt && opt->force_fallback) ? 1 : 0;
+        oa.parts = p.oneread_groups;
+        oa.part_tickets = p.oneread_groups > 1 ? at<uint32_t>(ws, plan.lay.part_tickets) : nullptr;
+        oa.part_ws = p.oneread_groups > 1 ? at<uint32_t>(ws, plan.lay.part_slots) : nullptr;
         return launch_oneread(oa, s) == hipSuccess ? QSA_OK : QSA_EHIP;
     }
     const TopkLayout &L = plan.lay;
     SplitArgs sa;
     sa.g = g;
     sa.tickets = at<uint32_t>(ws, L.split_tickets);
-    sa.meta = at<uint32_t>(ws, L.split_meta);
     sa.cand_keys = at<uint32_t>(ws, L.split_keys);
     sa.cand_blocks = at<int32_t>(ws, L.split_blocks);
     sa.cand_stride = plan.cand_stride;

@@ -22,16 +22,18 @@ constexpr int kMinChunk = 64;
 constexpr int kMaxChunk = 15360;          // keeps a chunk's keys under 60 KB of LDS
 constexpr int kStageBLdsWords = 15360;    // stage B keeps up to this many candidates (keys and blocks) in LDS
 constexpr int kOneReadCap = 4096;         // one-read candidate cap per query (blocks)
-constexpr int kOneReadMinBlocks = 28672;  // prompt calls from this many blocks ...
-constexpr int kOneReadMinQueries = 64;    // ... and this many queries use the one-read path
+constexpr int kPartWords = 4 + 2 * kOneReadCap;  // one-read hand-off slot per part (u32 words)
+constexpr int kOneReadMaxParts = 16;
+constexpr int kOneReadMinRatio = 16;      // one-read when n_blocks >= this many times r_blocks ...
 constexpr int kSampleStride = 32;
 
 // Workspace layout of the split (byte offsets, 256-byte aligned).
 struct TopkLayout {
     size_t split_tickets;   // u32 [nq]
-    size_t split_meta;      // u32 [nq][n_chunks][2] : {count, chunk threshold}
     size_t split_keys;      // u32 [nq][cand_stride]
     size_t split_blocks;    // i32 [nq][cand_stride]
+    size_t part_tickets;    // u32 [nq]             (one-read with several parts)
+    size_t part_slots;      // u32 [nq][parts][kPartWords]
     size_t bytes;
 };
 
@@ -62,7 +64,6 @@ struct TopkGeom {
 struct SplitArgs {
     TopkGeom g;
     uint32_t *tickets;
-    uint32_t *meta;
     uint32_t *cand_keys;
     int32_t *cand_blocks;
     int64_t cand_stride;
@@ -74,6 +75,9 @@ struct SplitArgs {
 
 struct OneReadArgs {
     TopkGeom g;
+    int32_t parts;          // workgroups per query (part = a range of slices)
+    uint32_t *part_tickets; // [nq], zero between calls (parts > 1)
+    uint32_t *part_ws;      // [nq][parts][kPartWords] hand-off slots (parts > 1)
     int32_t mode;           // QSA_SAMPLE_STRIDE / QSA_SAMPLE_LINES
     int32_t force_flag;     // take the exact path for every query
 };

@@ -33,6 +33,17 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Fourth word of a raw buffer resource on gfx9-family GPUs (32-bit data
+// format, no swizzle); with stride 0 a load at or past num_records bytes
+// returns zero without a memory access.
+constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy operand of a buffer load: sc1, device scope (the access a
+// relaxed device-scope atomic load makes).
+constexpr int kBufferDevice = 16;
+// Hand-off slot of one one-read part: {count, largest key, 2 unused}, then
+// kOneReadCap keys and kOneReadCap blocks (16-byte aligned sections).
+constexpr int kPartHeader = 4;
+
 struct QuerySel {
     int n_vis;      // visible blocks
     int wq;         // cells selected: min(width, visible cells)
@@ -219,15 +230,10 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
     }
     ordered_take<NT>(lds, nc, T, budget, 1u, 1u, sh, [&](int i, uint32_t pos, uint32_t) {
         if (pos < (uint32_t)cap_q) {
-            ckey[pos] = s_keys[i];
-            cblk[pos] = b0 + i;
+            store_dev(ckey + pos, s_keys[i]);
+            store_dev(reinterpret_cast<uint32_t *>(cblk) + pos, (uint32_t)(b0 + i));
         }
     });
-    if (threadIdx.x == 0) {
-        uint32_t *m = a.meta + ((int64_t)q * a.n_chunks + c) * 2;
-        m[0] = (uint32_t)min(nc, r_a);
-        m[1] = T;
-    }
     if (!last_to_arrive(&a.tickets[q], (uint32_t)nchq, s_flag))
         return;
 
@@ -245,14 +251,22 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
     if (total <= a.blk_words) {
         // Keys and block ids both to LDS: the emit then reads no global memory.
         int32_t *s_blks = reinterpret_cast<int32_t *>(s_keys + a.lds_words);
+        // Device-coherent 16-byte loads (a buffer resource with the sc1
+        // cache policy, the same access as load_dev) of both arrays.
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(gkey), (short)0, total * 4, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rb =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(gblk), (short)0, total * 4, kBufferWord3);
         const int n4 = total >> 2;
         for (int i = threadIdx.x; i < n4; i += NT) {
-            *reinterpret_cast<uint4 *>(s_keys + 4 * i) = *reinterpret_cast<const uint4 *>(gkey + 4 * i);
-            *reinterpret_cast<int4 *>(s_blks + 4 * i) = *reinterpret_cast<const int4 *>(gblk + 4 * i);
+            *reinterpret_cast<uint4 *>(s_keys + 4 * i) =
+                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * i, 0, kBufferDevice));
+            *reinterpret_cast<uint4 *>(s_blks + 4 * i) =
+                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * i, 0, kBufferDevice));
         }
         for (int i = (n4 << 2) + (int)threadIdx.x; i < total; i += NT) {
-            s_keys[i] = gkey[i];
-            s_blks[i] = gblk[i];
+            s_keys[i] = load_dev(gkey + i);
+            s_blks[i] = (int32_t)load_dev(reinterpret_cast<const uint32_t *>(gblk) + i);
         }
         lds_barrier();
         if (qs.tail != 0)
@@ -260,8 +274,10 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
         select_cells<NT>(lds, total, qs, [&](int i) { return s_blks[i]; }, g, q, sh);
     } else {
         if (qs.tail != 0)
-            widen_for_tail(qs, g.bs, count_at_least<NT>(GlobalKeys{gkey}, total, kp, sh));
-        select_cells<NT>(GlobalKeys{gkey}, total, qs, [&](int i) { return gblk[i]; }, g, q, sh);
+            widen_for_tail(qs, g.bs, count_at_least<NT>(DevKeys{gkey}, total, kp, sh));
+        select_cells<NT>(DevKeys{gkey}, total, qs,
+                         [&](int i) { return (int32_t)load_dev(reinterpret_cast<const uint32_t *>(gblk) + i); }, g,
+                         q, sh);
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(&a.tickets[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -357,12 +373,15 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     __shared__ uint32_t s_gcnt[NW];     // candidates at or above a partial last block's key
     __shared__ uint32_t s_wtot[NW];
     __shared__ uint32_t s_wmax[NW];
+    __shared__ uint32_t s_flag[1];
 
     const TopkGeom g = a.g;
-    const int q = blockIdx.x;
+    const int q = blockIdx.x / a.parts;
+    const int part = blockIdx.x - q * a.parts;
     QuerySel qs = query_sel(g, q);
     if (qs.r == 0) {
-        write_empty<NT>(g, q);
+        if (part == 0)
+            write_empty<NT>(g, q);
         return;
     }
     const int n = qs.n_vis;
@@ -385,7 +404,20 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     const uint32_t ks = 2u * (uint32_t)qs.r / kSampleStride + 16u;
     const bool all_cells = (int64_t)n * g.bs <= (int64_t)qs.wq;
     const bool use_bound = !all_cells && !a.force_flag && (uint32_t)ns >= ks;
-    const int nslices = (n + STEP - 1) / STEP;  // <= MAXS (the dispatch sees to it)
+    // Parts: the row's slices split evenly over the workgroups of the query
+    // (a query without a bound is one part). Each part streams its own range
+    // behind the same bound and hands its candidates to the part that
+    // finishes last, which selects over all of them.
+    const int rslices = (n + STEP - 1) / STEP;
+    const int sper0 = (rslices + min(a.parts, rslices) - 1) / min(a.parts, rslices);
+    const int sper = use_bound ? sper0 : rslices;
+    const int nparts = (rslices + sper - 1) / sper;
+    if (part >= nparts)
+        return;
+    const int p0 = part * sper * STEP;                  // first block of this part
+    const int np = min(n, (part + 1) * sper * STEP) - p0;  // blocks of this part
+    const float *prow = row + p0;
+    const int nslices = (np + STEP - 1) / STEP;  // <= MAXS (the dispatch sees to it)
 
     // Every load below is unconditional: a lane with nothing to read re-reads
     // block 0 (the row has at least one visible block here) and the value is
@@ -397,13 +429,13 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             const int i0 = sl * STEP + j * 4 * kWave + 4 * lane;
             if constexpr (VEC) {
                 // Streamed once: nontemporal loads keep it from displacing cached data.
-                const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + (i0 < n ? i0 : 0)));
+                const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(prow + (i0 < np ? i0 : 0)));
                 v[j] = make_float4(t[0], t[1], t[2], t[3]);
             } else {
-                v[j].x = row[i0 < n ? i0 : 0];
-                v[j].y = row[i0 + 1 < n ? i0 + 1 : 0];
-                v[j].z = row[i0 + 2 < n ? i0 + 2 : 0];
-                v[j].w = row[i0 + 3 < n ? i0 + 3 : 0];
+                v[j].x = prow[i0 < np ? i0 : 0];
+                v[j].y = prow[i0 + 1 < np ? i0 + 1 : 0];
+                v[j].z = prow[i0 + 2 < np ? i0 + 2 : 0];
+                v[j].w = prow[i0 + 3 < np ? i0 + 3 : 0];
             }
             // Issue order = use order: loads complete in order, so a load
             // the scheduler moved ahead would make the first use wait for it.
@@ -462,7 +494,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             uint64_t m[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                keep[s] = f[s] >= fbound && (FULL || i0 + s < n);
+                keep[s] = f[s] >= fbound && (FULL || i0 + s < np);
                 m[s] = __ballot(keep[s]);
             }
             const uint64_t any = m[0] | m[1] | m[2] | m[3];
@@ -479,7 +511,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
                     const int sel = keep[0] ? 0 : (keep[1] ? 1 : (keep[2] ? 2 : 3));
                     const uint32_t pos = min(wcnt + count_below(any), (uint32_t)(WCAP - 1));
                     wkey[pos] = __float_as_uint(x);
-                    wblk[pos] = i0 + sel;
+                    wblk[pos] = p0 + i0 + sel;
                     fmx = x > fmx ? x : fmx;
                 }
                 wcnt += (uint32_t)__popcll(any);
@@ -497,7 +529,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
                 if (keep[s]) {
                     const uint32_t p = min(pos, (uint32_t)(WCAP - 1));
                     wkey[p] = __float_as_uint(f[s]);
-                    wblk[p] = i0 + s;
+                    wblk[p] = p0 + i0 + s;
                     fmx = f[s] > fmx ? f[s] : fmx;
                     ++pos;
                 }
@@ -522,7 +554,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             if (lane == 0)
                 nxt = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             if (cs[u] < nslices) {
-                if (cs[u] * STEP + STEP <= n)
+                if (cs[u] * STEP + STEP <= np)
                     consume(cs[u], buf[u], std::true_type{});
                 else
                     consume(cs[u], buf[u], std::false_type{});
@@ -551,14 +583,19 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         over = over || c > (uint32_t)WCAP;
         kmax = max(kmax, s_wmax[w]);
     }
-    if (!a.force_flag && !over && (int64_t)total * g.bs >= w_need) {
-        // Every candidate key lies in [kmin, kmax]; the copy into block order
-        // also counts the top kFineBits bits of (key - kmin) into the fine
-        // bins and their coarse bins.
-        const uint32_t kmin = use_bound ? key_of(fbound) : 0u;
-        const uint32_t span = kmax - kmin;
-        const int fbits = span != 0 ? 32 - __clz(span) : 0;
-        const int sF = fbits > kFineBits ? fbits - kFineBits : 0;
+    const bool multi = nparts > 1;
+    bool ok = !a.force_flag && !over && (multi || (int64_t)total * g.bs >= w_need);
+    // Every candidate key lies in [kmin, kmax]; the fine bins take the top
+    // kFineBits bits of (key - kmin) (with one part, counted during the copy
+    // into block order; with several, after the merge).
+    const uint32_t kmin = use_bound ? key_of(fbound) : 0u;
+    uint32_t span = kmax - kmin;
+    auto fine_shift = [](uint32_t sp) {
+        const int fbits = sp != 0 ? 32 - __clz(sp) : 0;
+        return fbits > kFineBits ? fbits - kFineBits : 0;
+    };
+    int sF = fine_shift(span);
+    if (ok) {
         // Slices in order are block order: every wave scans the slice counts
         // itself and leaves, for each of its own slices, how far its run moves
         // from the wave's list to block order in the slice's s_ssrc entry (no
@@ -595,7 +632,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                shift[u] = s_ssrc[blk[u] / STEP];
+                shift[u] = s_ssrc[(blk[u] - p0) / STEP];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 if (ok[u]) {
@@ -604,7 +641,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
                     s_ckey[d] = k;
                     s_cblk[d] = blk[u];
                     gcnt += k >= kp ? 1u : 0u;
-                    if (span != 0) {
+                    if (!multi && span != 0) {
                         const uint32_t fb = (k - kmin) >> sF;
                         lds_add(&sh.fine[fb], 1u);
                         lds_add(&sh.coarse[fb / kFinePerCoarse], 1u);
@@ -616,6 +653,68 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         if (lane == 0)
             s_gcnt[wid] = gcnt;
         lds_barrier();
+    }
+    if (multi) {
+        // Publish this part's candidates (or an overflow mark) with
+        // device-coherent stores; the part that arrives last merges them in
+        // part order, which is block order.
+        uint32_t *slot = a.part_ws + ((int64_t)q * a.parts + part) * kPartWords;
+        if (ok) {
+            for (int i = threadIdx.x; i < (int)total; i += NT) {
+                store_dev(slot + kPartHeader + i, s_ckey[i]);
+                store_dev(slot + kPartHeader + kOneReadCap + i, (uint32_t)s_cblk[i]);
+            }
+        }
+        if (threadIdx.x == 0) {
+            store_dev(slot, ok ? total : 0xFFFFFFFFu);
+            store_dev(slot + 1, kmax);
+        }
+        if (!last_to_arrive(&a.part_tickets[q], (uint32_t)nparts, s_flag))
+            return;
+        if (threadIdx.x == 0)
+            store_dev(&a.part_tickets[q], 0u);  // zero again for the next call
+        const uint32_t *base = a.part_ws + (int64_t)q * a.parts * kPartWords;
+        total = 0;
+        kmax = 0;
+        ok = true;
+        for (int j = 0; j < nparts; ++j) {
+            const uint32_t c = load_dev(base + (int64_t)j * kPartWords);
+            ok = ok && c != 0xFFFFFFFFu;
+            total += ok ? c : 0u;
+            kmax = max(kmax, load_dev(base + (int64_t)j * kPartWords + 1));
+        }
+        ok = ok && total <= (uint32_t)kOneReadCap && (int64_t)total * g.bs >= w_need;
+        if (ok) {
+            uint32_t o = 0;
+            for (int j = 0; j < nparts; ++j) {
+                const uint32_t *src = base + (int64_t)j * kPartWords;
+                const int c = (int)load_dev(src);
+                for (int i = threadIdx.x; i < c; i += NT) {
+                    s_ckey[o + i] = load_dev(src + kPartHeader + i);
+                    s_cblk[o + i] = (int32_t)load_dev(src + kPartHeader + kOneReadCap + i);
+                }
+                o += (uint32_t)c;
+            }
+            lds_barrier();
+            span = kmax - kmin;
+            sF = fine_shift(span);
+            uint32_t gcnt = 0;
+            for (int i = threadIdx.x; i < (int)total; i += NT) {
+                const uint32_t k = s_ckey[i];
+                gcnt += k >= kp ? 1u : 0u;
+                if (span != 0) {
+                    const uint32_t fb = (k - kmin) >> sF;
+                    lds_add(&sh.fine[fb], 1u);
+                    lds_add(&sh.coarse[fb / kFinePerCoarse], 1u);
+                }
+            }
+            gcnt = wave_sum(gcnt);
+            if (lane == 0)
+                s_gcnt[wid] = gcnt;
+            lds_barrier();
+        }
+    }
+    if (ok) {
         if (qs.tail != 0) {
             // The partial last block is a candidate iff its key is >= kmin, and
             // then every block at or above its key is one; if it is not, it is
@@ -726,7 +825,8 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             g.counts[q] = qs.wq;
         return;
     }
-    // Flagged: the exact rule over the whole row, read from global memory.
+    // Flagged: the exact rule over the whole row, read from global memory (the
+    // histograms are still zero: no histogram pass ran).
     if (qs.tail != 0)
         widen_for_tail(qs, g.bs, count_at_least<NT>(RowKeys{row, VEC}, n, kp, sh));
     select_cells<NT>(RowKeys{row, VEC}, n, qs, [&](int i) { return i; }, g, q, sh);
@@ -770,12 +870,12 @@ hipError_t launch_split(const SplitArgs &a, hipStream_t s)
 
 hipError_t launch_oneread(const OneReadArgs &a, hipStream_t s)
 {
+    const dim3 grid((unsigned)(a.g.nq * a.parts));
     if (a.g.vec4)
-        hipLaunchKernelGGL((oneread_kernel<kOneReadThreads, kOneReadF4, true>), dim3((unsigned)a.g.nq),
-                           dim3(kOneReadThreads), 0, s, a);
+        hipLaunchKernelGGL((oneread_kernel<kOneReadThreads, kOneReadF4, true>), grid, dim3(kOneReadThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((oneread_kernel<kOneReadThreads, kOneReadF4, false>), dim3((unsigned)a.g.nq),
-                           dim3(kOneReadThreads), 0, s, a);
+        hipLaunchKernelGGL((oneread_kernel<kOneReadThreads, kOneReadF4, false>), grid, dim3(kOneReadThreads), 0, s,
+                           a);
     return hipGetLastError();
 }
 

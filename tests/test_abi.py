@@ -33,21 +33,38 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         B.lib()
 
 
-def test_dispatch_decode_uses_split_with_page_chunks():
-    p = qsa.topk_plan(3, 64512, 4, 2048, "decode")
+def test_split_geometry_with_page_chunks():
+    p = qsa.topk_plan(3, 64512, 4, 2048, "decode", qsa.make_options(topk_path=qsa.PATH_SPLIT))
     assert p["path"] == qsa.PATH_SPLIT
     assert p["r_blocks"] == 512
     assert p["n_chunks"] == 16 and p["chunk_blocks"] == 4032  # fewest chunks of <= 4,104 blocks
     assert p["stage_b_lds"] == 1
 
 
-def test_dispatch_prompt_threshold_and_ks():
+def test_dispatch_rule():
+    # One chunk: the split's single workgroup; longer rows where the bound
+    # keeps a small share of the blocks (n >= 16 r): one-read; else the split.
+    assert qsa.topk_plan(3, 4104, 4, 2048, "decode")["path"] == qsa.PATH_SPLIT
+    assert qsa.topk_plan(3, 8191, 4, 2048, "decode")["path"] == qsa.PATH_SPLIT
+    assert qsa.topk_plan(3, 8192, 4, 2048, "decode")["path"] == qsa.PATH_ONEREAD
+    assert qsa.topk_plan(3, 4105, 4, 256, "decode")["path"] == qsa.PATH_ONEREAD
+    for nq, call in ((3, "decode"), (16, "decode"), (16, "prompt"), (256, "prompt")):
+        assert qsa.topk_plan(nq, 32768, 4, 2048, call)["path"] == qsa.PATH_ONEREAD
+
+
+def test_oneread_parts_are_opt_in():
+    assert qsa.topk_plan(3, 64512, 4, 2048, "decode")["oneread_groups"] == 1
+    o = qsa.make_options(oneread_parts=4)
+    p = qsa.topk_plan(3, 64512, 4, 2048, "decode", o)
+    assert p["path"] == qsa.PATH_ONEREAD and p["oneread_groups"] == 4
+    assert qsa.topk_workspace_bytes(256, 130048, 4, 2048, "prompt") <= 256
+    assert qsa.topk_workspace_bytes(3, 64512, 4, 2048, "decode", o) >= 3 * 4 * (4 + 2 * 4096) * 4
+
+
+def test_prompt_ks_and_cap():
     big = qsa.topk_plan(256, 32768, 4, 2048, "prompt")
-    small = qsa.topk_plan(256, 28671, 4, 2048, "prompt")
-    assert big["path"] == qsa.PATH_ONEREAD and small["path"] == qsa.PATH_SPLIT
     assert big["ks"] == 2 * 512 // 32 + 16 == 48
     assert big["cap"] == 4096 and big["sample_stride"] == 32
-    assert qsa.topk_plan(16, 32768, 4, 2048, "prompt")["path"] == qsa.PATH_SPLIT  # few queries
 
 
 def test_forced_paths_and_workspace_growth():
@@ -80,7 +97,9 @@ def test_width_larger_than_context():
     (dict(topk_path=7), B.QSA_EINVAL),
     (dict(sample=9), B.QSA_EINVAL),
     (dict(oneread_blocks=2048), B.QSA_EUNSUPPORTED),
-    (dict(reserved=(1, 0, 0)), B.QSA_EINVAL),
+    (dict(reserved=(1, 0)), B.QSA_EINVAL),
+    (dict(oneread_parts=17), B.QSA_EINVAL),
+    (dict(oneread_parts=-1), B.QSA_EINVAL),
 ])
 def test_bad_options_rejected(kw, status):
     with pytest.raises(B.QSAError) as e:

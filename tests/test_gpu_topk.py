@@ -30,6 +30,9 @@ PATHS = {
     "oneread_stride": dict(topk_path=qsa.PATH_ONEREAD, sample=qsa.SAMPLE_STRIDE),
     "fallback": dict(topk_path=qsa.PATH_ONEREAD, force_fallback=1),
     "fallback64": dict(topk_path=qsa.PATH_ONEREAD, force_fallback=1, chunk_blocks=64),
+    "parts2": dict(topk_path=qsa.PATH_ONEREAD, oneread_parts=2),
+    "parts5": dict(topk_path=qsa.PATH_ONEREAD, oneread_parts=5),
+    "parts16": dict(topk_path=qsa.PATH_ONEREAD, oneread_parts=16, sample=qsa.SAMPLE_STRIDE),
 }
 
 
@@ -138,7 +141,7 @@ def test_decode_contexts_full_size(n_blocks):
     wl = synth.c2(n_blocks)
     s = wl.scores()
     exp = oracle.topk_sort(s, n_blocks, wl.block_size, wl.width)
-    for path in ("auto", "split64", "oneread_lines"):
+    for path in ("auto", "split", "split64", "oneread_lines", "parts2", "parts16"):
         say(f"C2 decode nb={n_blocks} path={path}")
         got = gpu_topk(s, n_blocks, wl.block_size, wl.width, "decode", options=_opts(path))
         assert_ids_equal(got, exp, f"C2 nb={n_blocks} {path}")
@@ -152,7 +155,7 @@ def test_prompt_contexts_full_size(n_blocks, variant):
     active = np.full(wl.nq, n_blocks, np.int32)
     rows = np.arange(0, wl.nq, 17)  # the oracle redoes 16 of the 256 queries
     exp = oracle.topk_sort(s[rows], n_blocks, wl.block_size, wl.width, active[rows])
-    for path in ("auto", "split"):
+    for path in ("auto", "split", "parts5"):
         say(f"C4 prompt nb={n_blocks} {variant} path={path}")
         got = gpu_topk(s, n_blocks, wl.block_size, wl.width, "prompt", active=active, options=_opts(path))
         assert_ids_equal(got, exp, f"C4 nb={n_blocks} {variant} {path}", rows=rows)
@@ -222,8 +225,6 @@ def test_cells_hand_cases(path):
     for case in g["cases"]:
         keys = np.array([case["keys"]], np.float32)
         for call in ("decode", "prompt"):
-            if path.startswith(("oneread", "fallback")) and call == "decode":
-                continue
             say(f"cells hand {case['name']} {call} path={path}")
             ids, counts = gpu_topk_cells(keys, keys.shape[1], case["block_size"], case["width"], call,
                                          [case["cells"]], options=_opts(path))
@@ -244,8 +245,6 @@ def _cells_cases():
         variant = variants[i % len(variants)]
         call = "prompt" if i % 3 else "decode"
         path = list(PATHS)[i % len(PATHS)]
-        if call == "decode" and path.startswith(("oneread", "fallback")):
-            path = "auto"
         out.append(pytest.param(i, nb, bs, width, nq, variant, call, path,
                                 id=f"{i}-nb{nb}-bs{bs}-w{width}-nq{nq}-{variant}-{call}-{path}"))
     return out
@@ -272,7 +271,7 @@ def test_cells_decode_contexts_full_size(n_blocks):
     full = n_blocks * wl.block_size
     cells = np.array([full - 1, full - 3, full - 4 * 999 - 2], np.int32)
     exp = oracle.topk_sort_cells(s, n_blocks, wl.block_size, wl.width, cells)
-    for path in ("auto", "split64"):
+    for path in ("auto", "split", "split64", "parts5"):
         say(f"C2 cells nb={n_blocks} path={path}")
         got = gpu_topk_cells(s, n_blocks, wl.block_size, wl.width, "decode", cells, options=_opts(path))
         assert_ids_equal(got, exp, f"C2 cells nb={n_blocks} {path}")
@@ -288,7 +287,7 @@ def test_cells_prompt_full_size(variant):
     cells[::3] = full - 1 - (np.arange(0, wl.nq, 3) % 3)  # partial last blocks
     rows = np.arange(0, wl.nq, 17)
     exp = oracle.topk_sort_cells(s[rows], n_blocks, wl.block_size, wl.width, cells[rows])
-    for path in ("auto", "split"):
+    for path in ("auto", "split", "parts2"):
         say(f"C4 cells {variant} path={path}")
         got = gpu_topk_cells(s, n_blocks, wl.block_size, wl.width, "prompt", cells, options=_opts(path))
         assert_ids_equal(got, exp, f"C4 cells {variant} {path}", rows=rows)
