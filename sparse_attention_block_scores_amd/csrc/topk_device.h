@@ -647,6 +647,87 @@ __device__ __forceinline__ void ordered_take(const Src &src, int n, uint32_t T, 
     }
 }
 
+// ordered_take for n <= PER * NT items, with one workgroup exchange: thread
+// t holds items [PER*t, PER*t + PER) in registers, and one scan of (items
+// above T, items equal to T) over the workgroup gives every taken item its
+// slot. Same contract as ordered_take. Uses sh.red[0] until the caller's next
+// barrier.
+template <int NT, int PER, class Src, class Emit>
+__device__ __forceinline__ void take_in_order(const Src &src, int n, uint32_t T, uint32_t tie_budget,
+                                              uint32_t unit, uint32_t last_unit, SelectShared<NT> &sh, Emit emit)
+{
+    static_assert(PER % 4 == 0, "16-byte loads of each thread's items");
+    constexpr int NW = NT / kWave;
+    const int lane = lane_id(), wid = wave_id();
+    const int c0 = (int)threadIdx.x * PER;
+    const bool vec = vector_ok(src);
+    uint32_t k[PER];
+    bool v[PER];
+#pragma unroll
+    for (int u = 0; u < PER / 4; ++u) {
+        const int i = c0 + 4 * u;
+        if (vec && i + 3 < n) {
+            const uint4 x = src.load4(i);
+            k[4 * u] = x.x; k[4 * u + 1] = x.y; k[4 * u + 2] = x.z; k[4 * u + 3] = x.w;
+            v[4 * u] = v[4 * u + 1] = v[4 * u + 2] = v[4 * u + 3] = true;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[4 * u + j] = i + j < n;
+                k[4 * u + j] = v[4 * u + j] ? src.load1(i + j) : 0u;
+            }
+        }
+    }
+    uint32_t gt = 0, tie = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        gt += v[j] && k[j] > T ? 1u : 0u;
+        tie += v[j] && k[j] == T ? 1u : 0u;
+    }
+    const uint32_t packed = gt | (tie << 16);  // both < 2^16 (n <= PER * NT)
+    const uint32_t incl = wave_incl_sum(packed);
+    if (lane == kWave - 1)
+        sh.red[0][wid] = incl;
+    lds_barrier();
+    uint32_t before = incl - packed;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        before += w < wid ? sh.red[0][w] : 0u;
+    uint32_t ties_before = before >> 16;
+    const uint32_t shortfall = unit - last_unit;
+    uint32_t first = unit * ((before & 0xFFFFu) + min(ties_before, tie_budget)) -
+                     (ties_before >= tie_budget ? shortfall : 0u);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        uint32_t w = 0;
+        if (v[j] && k[j] > T) {
+            w = unit;
+        } else if (v[j] && k[j] == T) {
+            if (ties_before < tie_budget)
+                w = ties_before == tie_budget - 1u ? last_unit : unit;
+            ++ties_before;
+        }
+        if (w != 0u) {
+            emit(c0 + j, first, w);
+            first += w;
+        }
+    }
+}
+
+// The ordered take for any n: in registers up to 16 items per thread, else
+// walked in ranges (ordered_take).
+template <int NT, class Src, class Emit>
+__device__ __forceinline__ void take_ordered(const Src &src, int n, uint32_t T, uint32_t tie_budget, uint32_t unit,
+                                             uint32_t last_unit, SelectShared<NT> &sh, Emit emit)
+{
+    if (n <= 8 * NT)
+        take_in_order<NT, 8>(src, n, T, tie_budget, unit, last_unit, sh, emit);
+    else if (n <= 16 * NT)
+        take_in_order<NT, 16>(src, n, T, tie_budget, unit, last_unit, sh, emit);
+    else
+        ordered_take<NT>(src, n, T, tie_budget, unit, last_unit, sh, emit);
+}
+
 // ------------------------------------------------------------ hand-off
 // Workgroups of one launch hand data to the last of them through global
 // memory without device-scope fences. On gfx950 each XCD has its own L2, and

@@ -132,7 +132,7 @@ __device__ __forceinline__ void emit_selection(const Src &src, int n, const Quer
     int32_t *out = g.ids + (int64_t)q * g.width;
     const int bs = g.bs;
     const uint32_t limit = (uint32_t)qs.wq;
-    ordered_take<NT>(src, n, T, (uint32_t)qs.r - above, (uint32_t)bs, (uint32_t)qs.last_unit, sh,
+    take_ordered<NT>(src, n, T, (uint32_t)qs.r - above, (uint32_t)bs, (uint32_t)qs.last_unit, sh,
                      [&](int i, uint32_t first, uint32_t cnt) {
                          write_cells(out, first, cnt, block_at(i) * bs, limit);
                      });
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
         radix_select<NT>(lds, nc, (uint32_t)r_a, sh, T, above);
         budget = (uint32_t)r_a - above;
     }
-    ordered_take<NT>(lds, nc, T, budget, 1u, 1u, sh, [&](int i, uint32_t pos, uint32_t) {
+    take_ordered<NT>(lds, nc, T, budget, 1u, 1u, sh, [&](int i, uint32_t pos, uint32_t) {
         if (pos < (uint32_t)cap_q) {
             store_dev(ckey + pos, s_keys[i]);
             store_dev(reinterpret_cast<uint32_t *>(cblk) + pos, (uint32_t)(b0 + i));
