@@ -104,14 +104,42 @@ def cpu_baseline(wl, q, k, w, budget_s=12.0):
     }
 
 
+def graph_us(torch, dev, fn, n):
+    """Mean GPU time of fn(i) for i < n, captured once in a HIP graph and
+    replayed, so host-side call overhead does not enter small latencies."""
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n):
+                fn(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / n * 1000.0
+
+
 def secondary(torch, qsa, synth, dev, reps=50):
-    """Decode-call latency at each context and top-k-only prompt figures."""
+    """Decode-call latency at each context and top-k-only prompt figures.
+    Every figure is the mean over a HIP graph of back-to-back calls on
+    torch's current stream (the library is capture-safe: no allocation, no
+    host synchronisation, no memset nodes)."""
     out = {}
 
     def time_us(fn, n=reps):
-        for _ in range(3):
-            fn(0)
-        return timed_loop(torch, n, fn) / n * 1000.0
+        return graph_us(torch, dev, lambda i: fn(i), n)
+
+    cur = torch.cuda.current_stream
 
     wl = synth.c1()
     q, k, w = [torch.from_numpy(x).to(dev) for x in wl.tensors()]
@@ -120,7 +148,8 @@ def secondary(torch, qsa, synth, dev, reps=50):
     ids = torch.empty((wl.nq, wl.width), dtype=torch.int32, device=dev)
     cnt = torch.empty((wl.nq,), dtype=torch.int32, device=dev)
     out["decode_nq3_select_us"] = round(time_us(lambda i: qsa.select(q, k, w, 4, wl.width, "decode", scores=s,
-                                                                      ids=ids, counts=cnt, ws=ws)), 2)
+                                                                      ids=ids, counts=cnt, ws=ws,
+                                                                      stream=cur())), 2)
     wl3 = synth.c3()
     q3, k3, w3 = [torch.from_numpy(x).to(dev) for x in wl3.tensors()]
     ws3 = qsa.workspace(qsa.topk_workspace_bytes(wl3.nq, wl3.n_blocks, 4, wl3.width, "decode"), dev)
@@ -129,17 +158,21 @@ def secondary(torch, qsa, synth, dev, reps=50):
     cnt3 = torch.empty((wl3.nq,), dtype=torch.int32, device=dev)
     out["decode_nq16_select_us"] = round(time_us(lambda i: qsa.select(q3, k3, w3, 4, wl3.width, "decode",
                                                                        scores=s3, ids=ids3, counts=cnt3,
-                                                                       ws=ws3)), 2)
-    dec = {}
+                                                                       ws=ws3, stream=cur())), 2)
+    dec, dec_split = {}, {}
+    split = qsa.make_options(topk_path=qsa.PATH_SPLIT)
     for nb in synth.C2_BLOCKS:
         t = synth.c2(nb)
         sc = torch.from_numpy(t.scores()).to(dev)
-        wsd = qsa.workspace(qsa.topk_workspace_bytes(t.nq, nb, 4, t.width, "decode"), dev)
         idd = torch.empty((t.nq, t.width), dtype=torch.int32, device=dev)
         cd = torch.empty((t.nq,), dtype=torch.int32, device=dev)
-        dec[str(nb * 4)] = round(time_us(lambda i: qsa.block_topk(sc, nb, 4, t.width, "decode", ids=idd,
-                                                                  counts=cd, ws=wsd)), 2)
-    out["decode_nq3_topk_us_by_cells"] = dec
+        for table, opt in ((dec, None), (dec_split, split)):
+            wsd = qsa.workspace(qsa.topk_workspace_bytes(t.nq, nb, 4, t.width, "decode", opt), dev)
+            table[str(nb * 4)] = round(time_us(lambda i: qsa.block_topk(sc, nb, 4, t.width, "decode", ids=idd,
+                                                                        counts=cd, ws=wsd, options=opt,
+                                                                        stream=cur())), 2)
+    out["decode_nq3_topk_us_by_cells"] = dec              # the dispatch's choice (one-read for these rows)
+    out["decode_nq3_topk_split_us_by_cells"] = dec_split  # the multi-workgroup chunked split, forced
     prm = {}
     for nb in synth.C4_BLOCKS:
         entry = {}
@@ -153,7 +186,7 @@ def secondary(torch, qsa, synth, dev, reps=50):
             idp = torch.empty((t.nq, t.width), dtype=torch.int32, device=dev)
             cp = torch.empty((t.nq,), dtype=torch.int32, device=dev)
             us = time_us(lambda i: qsa.block_topk(bufs[i % 4], nb, 4, t.width, "prompt", ids=idp, counts=cp,
-                                                  ws=wsp), n=40)
+                                                  ws=wsp, stream=cur()), n=40)
             gbs = t.nq * nb * 4 / us / 1e3
             if variant == "continuous":
                 entry.update({"us": round(us, 2), "scores_GBps": round(gbs, 1),
