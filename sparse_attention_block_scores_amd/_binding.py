@@ -38,7 +38,8 @@ class Options(ctypes.Structure):
         ("force_fallback", ctypes.c_int32),
         ("oneread_blocks", ctypes.c_int32),
         ("oneread_parts", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 2),
+        ("fused_select", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 1),
     ]
 
 

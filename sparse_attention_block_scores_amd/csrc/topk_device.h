@@ -728,6 +728,20 @@ __device__ __forceinline__ void take_ordered(const Src &src, int n, uint32_t T, 
         ordered_take<NT>(src, n, T, tie_budget, unit, last_unit, sh, emit);
 }
 
+// Cells of one taken block: `cnt` consecutive ids from cell0 at out[first],
+// none at or past `limit`.
+__device__ __forceinline__ void write_cells(int32_t *out, uint32_t first, uint32_t cnt, int32_t cell0,
+                                            uint32_t limit)
+{
+    if (cnt == 4 && (first & 3u) == 0 && first + 4 <= limit) {
+        *reinterpret_cast<int4 *>(out + first) = make_int4(cell0, cell0 + 1, cell0 + 2, cell0 + 3);
+        return;
+    }
+    for (uint32_t j = 0; j < cnt; ++j)
+        if (first + j < limit)
+            out[first + j] = cell0 + (int32_t)j;
+}
+
 // ------------------------------------------------------------ hand-off
 // Workgroups of one launch hand data to the last of them through global
 // memory without device-scope fences. On gfx950 each XCD has its own L2, and
@@ -737,6 +751,14 @@ __device__ __forceinline__ void take_ordered(const Src &src, int n, uint32_t T, 
 // coherent: stores write through to the device level and loads read it.
 // Every thread waits for its own stores to complete before the ticket, so the
 // ticket is counted only after the data is there.
+
+// Fourth word of a raw buffer resource on gfx9-family GPUs (32-bit data
+// format, no swizzle); with stride 0 a load at or past num_records bytes
+// returns zero without a memory access.
+constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy operand of a buffer load: sc1, device scope (the access a
+// relaxed device-scope atomic load makes).
+constexpr int kBufferDevice = 16;
 
 // Device-coherent store / load of one 32-bit word.
 __device__ __forceinline__ void store_dev(uint32_t *p, uint32_t v)

@@ -33,13 +33,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Fourth word of a raw buffer resource on gfx9-family GPUs (32-bit data
-// format, no swizzle); with stride 0 a load at or past num_records bytes
-// returns zero without a memory access.
-constexpr int kBufferWord3 = 0x00020000;
-// Cache-policy operand of a buffer load: sc1, device scope (the access a
-// relaxed device-scope atomic load makes).
-constexpr int kBufferDevice = 16;
+
 // Hand-off slot of one one-read part: {count, largest key, 2 unused}, then
 // kOneReadCap keys and kOneReadCap blocks (16-byte aligned sections).
 constexpr int kPartHeader = 4;
@@ -106,19 +100,6 @@ __device__ __forceinline__ void write_empty(const TopkGeom &g, int q)
         out[p] = -1;
     if (g.counts && threadIdx.x == 0)
         g.counts[q] = 0;
-}
-
-// Cells of one taken block: `cnt` consecutive ids from block*bs at out[first].
-__device__ __forceinline__ void write_cells(int32_t *out, uint32_t first, uint32_t cnt, int32_t cell0,
-                                            uint32_t limit)
-{
-    if (cnt == 4 && (first & 3u) == 0 && first + 4 <= limit) {
-        *reinterpret_cast<int4 *>(out + first) = make_int4(cell0, cell0 + 1, cell0 + 2, cell0 + 3);
-        return;
-    }
-    for (uint32_t j = 0; j < cnt; ++j)
-        if (first + j < limit)
-            out[first + j] = cell0 + (int32_t)j;
 }
 
 // Writes a query's selection from n candidate blocks in ascending block order
