@@ -31,7 +31,8 @@ if ROOT not in sys.path:
 METRIC = "qsa_select µs/call (score+top-k) decode nq=3 & prompt nq=256; % HBM/MFMA peak"
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
-SCORER_SOURCE = os.path.join(ROOT, "sparse_attention_block_scores_amd", "csrc", "scores_kernel.hip")
+SCORER_SOURCES = [os.path.join(ROOT, "sparse_attention_block_scores_amd", "csrc", f)
+                  for f in ("scores_kernel.hip", "scores_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scores_kernel_c5_traffic.json")
 
 
@@ -47,8 +48,11 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def event_pairs_mean_us(pairs) -> float:
@@ -62,7 +66,7 @@ def measured_traffic(per_launch_flops_unit):
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != source_digest(SCORER_SOURCE):
+    if t.get("kernel_source_sha256_16") != source_digest(SCORER_SOURCES):
         return None
     return t.get("hbm_bytes_per_launch")
 
