@@ -13,8 +13,8 @@ namespace qsa {
 // ---------------------------------------------------------------- top-k
 constexpr int kSplitThreads = 512;        // workgroup of the exact split kernel
 constexpr int kOneReadThreads = 512;      // one workgroup per query on the one-read path
-constexpr int kOneReadF4 = 8;             // float4 loads per lane and batch
-constexpr int kOneReadBuffers = 3;        // batches in flight per lane
+constexpr int kOneReadF4 = 4;             // float4 loads per lane and slice
+constexpr int kOneReadBuffers = 4;        // slices in flight per lane
 constexpr int kOneReadBatch = kOneReadThreads * kOneReadF4 * 4;  // blocks streamed per batch
 constexpr int kOneReadMaxBatches = 64;    // the one-read path takes rows of up to 64 batches
 constexpr int kChunkBound = 4104;         // split chunks: the fewest of at most this many blocks
