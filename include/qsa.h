@@ -90,7 +90,7 @@ typedef struct qsa_options {
     int32_t chunk_blocks;   /* SPLIT chunk size in blocks: 0 = auto, else 64..15360, multiple of 4 */
     int32_t sample;         /* QSA_SAMPLE_* */
     int32_t force_fallback; /* ONEREAD: every query takes the exact fallback over its whole row */
-    int32_t oneread_blocks; /* ONEREAD blocks streamed per batch: 0 or 8192 (others QSA_EUNSUPPORTED) */
+    int32_t oneread_blocks; /* ONEREAD blocks streamed per batch: 0 or 16384 (others QSA_EUNSUPPORTED) */
     int32_t oneread_parts;  /* ONEREAD workgroups per query: 0 = auto, else 1..16 */
     int32_t fused_select;   /* qsa_select, decode calls of up to 1,024 blocks, 16 queries and 32 heads,
                                no length array: 1 = scores and top-k in one launch (the default, 0,

@@ -12,16 +12,17 @@ namespace qsa {
 
 // ---------------------------------------------------------------- top-k
 constexpr int kSplitThreads = 512;        // workgroup of the exact split kernel
-constexpr int kOneReadThreads = 512;      // one workgroup per query on the one-read path
+constexpr int kOneReadThreads = 1024;     // one workgroup per query on the one-read path
 constexpr int kOneReadF4 = 4;             // float4 loads per lane and slice
-constexpr int kOneReadBuffers = 4;        // slices in flight per lane
+constexpr int kOneReadBuffers = 2;        // slices in flight per lane
 constexpr int kOneReadBatch = kOneReadThreads * kOneReadF4 * 4;  // blocks streamed per batch
 constexpr int kOneReadMaxBatches = 64;    // the one-read path takes rows of up to 64 batches
 constexpr int kChunkBound = 4104;         // split chunks: the fewest of at most this many blocks
 constexpr int kMinChunk = 64;
 constexpr int kMaxChunk = 15360;          // keeps a chunk's keys under 60 KB of LDS
 constexpr int kStageBLdsWords = 15360;    // stage B keeps up to this many candidates (keys and blocks) in LDS
-constexpr int kOneReadCap = 4096;         // one-read candidate cap per query (blocks)
+constexpr int kOneReadCap = 8192;         // one-read candidate cap per query (blocks)
+constexpr int kOneReadSample = 4096;      // one-read sample: at most this many keys
 constexpr int kPartWords = 4 + 2 * kOneReadCap;  // one-read hand-off slot per part (u32 words)
 constexpr int kOneReadMaxParts = 16;
 constexpr int kOneReadMinRatio = 16;      // one-read when n_blocks >= this many times r_blocks ...

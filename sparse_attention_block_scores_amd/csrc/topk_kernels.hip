@@ -381,7 +381,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         const int full = n / 1024, rem = n % 1024;
         ns = full * kSampleStride + min(rem, kSampleStride);
     }
-    ns = min(ns, kOneReadCap);
+    ns = min(ns, kOneReadSample);
     const uint32_t ks = 2u * (uint32_t)qs.r / kSampleStride + 16u;
     const bool all_cells = (int64_t)n * g.bs <= (int64_t)qs.wq;
     const bool use_bound = !all_cells && !a.force_flag && (uint32_t)ns >= ks;
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
 
     // The sample goes into registers first (SPT per thread), then the first
     // NBUF slices of every wave are issued behind it.
-    constexpr int SPT = kOneReadCap / NT;
+    constexpr int SPT = kOneReadSample / NT;
     float smp[SPT];
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
@@ -707,25 +707,29 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             widen_for_tail(qs, g.bs, kp >= kmin ? n_ge : 0xFFFFFFFFu);
         }
 
-        // Each thread holds the candidates [PER*t, PER*t + PER) of the block
-        // order in registers from here on: the threshold's gather and the
-        // emit both use them without another pass over the LDS.
+        // Each thread holds the candidates [per*t, per*t + per) of the block
+        // order in registers from here on (per = ceil(total / NT), at most
+        // PER; slots j >= per are skipped as a whole): the threshold's gather
+        // and the emit both use them without another pass over the LDS, and
+        // the candidates are spread over every wave.
         constexpr int PER = kOneReadCap / NT;
-        static_assert(PER % 4 == 0, "16-byte reads of each thread's candidates");
+        const int per = ((int)total + NT - 1) / NT;
         uint32_t ck[PER];
         int32_t cb[PER];
         bool cv[PER];
-        const int c0 = (int)threadIdx.x * PER;
+        const int c0 = (int)threadIdx.x * per;
 #pragma unroll
-        for (int v = 0; v < PER / 4; ++v) {
-            const uint4 kk = *reinterpret_cast<const uint4 *>(s_ckey + c0 + 4 * v);
-            const int4 bb = *reinterpret_cast<const int4 *>(s_cblk + c0 + 4 * v);
-            ck[4 * v] = kk.x; ck[4 * v + 1] = kk.y; ck[4 * v + 2] = kk.z; ck[4 * v + 3] = kk.w;
-            cb[4 * v] = bb.x; cb[4 * v + 1] = bb.y; cb[4 * v + 2] = bb.z; cb[4 * v + 3] = bb.w;
+        for (int j = 0; j < PER; ++j) {
+            cv[j] = false;
+            ck[j] = 0;
+            cb[j] = 0;
+            if (j < per) {  // workgroup-uniform
+                cv[j] = c0 + j < (int)total;
+                const int i = cv[j] ? c0 + j : 0;
+                ck[j] = s_ckey[i];
+                cb[j] = s_cblk[i];
+            }
         }
-#pragma unroll
-        for (int j = 0; j < PER; ++j)
-            cv[j] = c0 + j < (int)total;
 
         // Threshold: the fine bin holding rank r usually holds a handful of
         // keys, which one wave ranks exactly; a crowded one goes on with radix
@@ -744,7 +748,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
                 // The bin's keys into sh.small, then one wave ranks them.
 #pragma unroll
                 for (int j = 0; j < PER; ++j) {
-                    if (cv[j] && ck[j] - blo <= bspan) {
+                    if (j < per && cv[j] && ck[j] - blo <= bspan) {
                         const uint32_t pos =
                             __hip_atomic_fetch_add(&sh.small_n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                         if (pos < (uint32_t)kWave)
@@ -767,8 +771,10 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         uint32_t gt = 0, tie = 0;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            gt += cv[j] && ck[j] > T ? 1u : 0u;
-            tie += cv[j] && ck[j] == T ? 1u : 0u;
+            if (j < per) {  // workgroup-uniform
+                gt += cv[j] && ck[j] > T ? 1u : 0u;
+                tie += cv[j] && ck[j] == T ? 1u : 0u;
+            }
         }
         const uint32_t packed = gt | (tie << 16);  // both <= kOneReadCap < 2^16
         const uint32_t incl = wave_incl_sum(packed);
@@ -787,6 +793,8 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         uint32_t pos = bs * ((before & 0xFFFFu) + min(ties_before, budget)) - (ties_before >= budget ? shortfall : 0u);
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
+            if (j >= per)  // workgroup-uniform
+                break;
             uint32_t cells = 0;
             if (cv[j] && ck[j] > T) {
                 cells = bs;
