@@ -132,6 +132,25 @@ qsa_status qsa_block_scores(const float *q, const float *k, const float *w,
                             int32_t nq, int32_t n_heads, int32_t head_dim,
                             int32_t n_blocks, void *stream);
 
+/*
+ * qsa_block_scores_bf16 - step 1 with BF16 q and k (a low-precision variant
+ * the pages mention for the scorer; Strata pull #1091, section What).
+ *
+ *   q       [nq][n_heads][head_dim] bfloat16 (raw 16-bit IEEE bfloat16
+ *           values), row-major, 16-byte aligned
+ *   k       [n_blocks][head_dim]    bfloat16, row-major, 16-byte aligned
+ *   w, scores, shapes, limits and errors as qsa_block_scores; in addition
+ *   ld_scores must be below 2^24 (else QSA_EUNSUPPORTED).
+ *   Products of BF16 values on the BF16 matrix cores, exact in FP32, with
+ *   FP32 accumulation: the scores of the BF16-rounded inputs. Ids selected
+ *   from them agree with the FP32 path's only within the rounding of the
+ *   inputs.
+ */
+qsa_status qsa_block_scores_bf16(const void *q, const void *k, const float *w,
+                                 float *scores, int64_t ld_scores,
+                                 int32_t nq, int32_t n_heads, int32_t head_dim,
+                                 int32_t n_blocks, void *stream);
+
 /* Bytes of workspace qsa_block_topk / qsa_select need for these sizes and
  * options (0 if the arguments are invalid). */
 size_t qsa_topk_workspace_bytes(int32_t nq, int32_t n_blocks, int32_t block_size,

@@ -6,6 +6,6 @@ the indexer block scorer (FP32 matrix cores) and the per-query block top-k
 the thin Python binding over libqsa.so.
 """
 from ._binding import (DECODE, PATH_AUTO, PATH_ONEREAD, PATH_SPLIT, PROMPT, SAMPLE_AUTO,  # noqa: F401
-                       SAMPLE_LINES, SAMPLE_STRIDE, Options, QSAError, block_scores, block_topk,
+                       SAMPLE_LINES, SAMPLE_STRIDE, Options, QSAError, block_scores, block_scores_bf16, block_topk,
                        declared_functions, lib, make_options, select, status_str, topk_plan,
                        topk_workspace_bytes, workspace)

@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
         L.qsa_status_str.argtypes = [i32]
         L.qsa_status_str.restype = ctypes.c_char_p
         L.qsa_block_scores.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P]
+        L.qsa_block_scores_bf16.argtypes = L.qsa_block_scores.argtypes
         L.qsa_topk_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, P]
         L.qsa_topk_workspace_bytes.restype = sz
         L.qsa_topk_plan_get.argtypes = [i32, i32, i32, i32, i32, P, P]
@@ -88,7 +89,7 @@ def lib() -> ctypes.CDLL:
         L.qsa_select.argtypes = [P, P, P, i32, i32, P, i64, i32, i32, i32, i32, i32, P, P, P, P, sz, P, P]
         L.qsa_block_topk_cells.argtypes = L.qsa_block_topk.argtypes
         L.qsa_select_cells.argtypes = L.qsa_select.argtypes
-        for name in ("qsa_block_scores", "qsa_topk_plan_get", "qsa_workspace_init", "qsa_block_topk",
+        for name in ("qsa_block_scores", "qsa_block_scores_bf16", "qsa_topk_plan_get", "qsa_workspace_init", "qsa_block_topk",
                      "qsa_select", "qsa_block_topk_cells", "qsa_select_cells"):
             getattr(L, name).restype = i32
         _lib = L
@@ -188,6 +189,25 @@ def block_scores(q, k, w, scores=None, stream=None):
         raise ValueError("scores must be [nq, ld] with unit column stride")
     _check(lib().qsa_block_scores(_ptr(q), _ptr(k), _ptr(w), _ptr(scores), scores.stride(0), nq, heads,
                                   head_dim, n_blocks, _stream(stream)), "qsa_block_scores")
+    return scores
+
+
+def block_scores_bf16(q, k, w, scores=None, stream=None):
+    """block_scores with bfloat16 q [nq, heads, 128] and k [n_blocks, 128] (FP32 w and scores)."""
+    _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(w, torch.float32, "w")
+    if not (q.is_contiguous() and k.is_contiguous() and w.is_contiguous()):
+        raise ValueError("q, k and w must be contiguous")
+    nq, heads, head_dim = q.shape
+    n_blocks = k.shape[0]
+    if k.shape[1] != head_dim or tuple(w.shape) != (nq, heads):
+        raise ValueError("shape mismatch between q, k and w")
+    if scores is None:
+        scores = torch.empty((nq, n_blocks), dtype=torch.float32, device=q.device)
+    _dev(scores, torch.float32, "scores")
+    if scores.dim() != 2 or scores.shape[0] != nq or scores.stride(1) != 1:
+        raise ValueError("scores must be [nq, ld] with unit column stride")
+    _check(lib().qsa_block_scores_bf16(_ptr(q), _ptr(k), _ptr(w), _ptr(scores), scores.stride(0), nq, heads,
+                                       head_dim, n_blocks, _stream(stream)), "qsa_block_scores_bf16")
     return scores
 
 

@@ -343,6 +343,24 @@ qsa_status qsa_block_scores(const float *q, const float *k, const float *w, floa
     return launch_scores(a, (hipStream_t)stream) == hipSuccess ? QSA_OK : QSA_EHIP;
 }
 
+qsa_status qsa_block_scores_bf16(const void *q, const void *k, const float *w, float *scores,
+                                 int64_t ld_scores, int32_t nq, int32_t n_heads, int32_t head_dim,
+                                 int32_t n_blocks, void *stream)
+{
+    // The FP32 checks apply unchanged: the same shapes, 16-byte aligned rows.
+    const qsa_status st = check_score_args(static_cast<const float *>(q), static_cast<const float *>(k), w, scores,
+                                           ld_scores, nq, n_heads, head_dim, n_blocks);
+    if (st != QSA_OK)
+        return st;
+    if (ld_scores >= (int64_t)1 << 24)
+        return QSA_EUNSUPPORTED;  // the kernel addresses 32 score rows with 31-bit offsets
+    if (nq == 0 || n_blocks == 0)
+        return QSA_OK;
+    ScoreArgs a{static_cast<const float *>(q), static_cast<const float *>(k), w, scores, ld_scores, nq, n_heads,
+                n_blocks};
+    return launch_scores_bf16(a, (hipStream_t)stream) == hipSuccess ? QSA_OK : QSA_EHIP;
+}
+
 qsa_status qsa_block_topk(const float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks,
                           int32_t block_size, int32_t width, qsa_call call,
                           const int32_t *active_blocks, int32_t *cell_ids, int32_t *counts,

@@ -100,6 +100,8 @@ struct ScoreArgs {
 };
 
 hipError_t launch_scores(const ScoreArgs &a, hipStream_t s);
+// The same with q and k holding BF16 values (ScoreArgs' q and k point at them).
+hipError_t launch_scores_bf16(const ScoreArgs &a, hipStream_t s);
 
 // Fused small decode-call selection (scores and top-k in one launch).
 constexpr int kFusedMaxBlocks = 1024;  // 16 keys per lane in the selecting wave

@@ -43,6 +43,90 @@ struct ScoreLds {
     float w[ROWS];
 };
 
+// max(x, 0) for a finite x, as an integer max of its bit pattern: negative
+// values (and -0.0) have the sign bit set, so they compare below 0 and give
+// +0.0; one instruction, where a float max would first quiet the operand.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// x of this lane plus x of the lane 32 away (lanes l and l ^ 32 get the same
+// sum): one cross-half swap of two copies.
+__device__ __forceinline__ float half_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Epilogue of one key tile: relu, weight, head sum, store. acc[m] holds the
+// 32x32 dot products of this wave's row tile m (rows 8*(v/4) + 4*(lane/32) +
+// v%4 of column lane%32 in register v, the layout of every 32x32 matrix-core
+// product); wgt(m, v) is the weight of acc[m][v]'s row; blk is the block of
+// this lane's column.
+template <int HP, int MR, bool MASKED = false, class Weight, class Store>
+__device__ __forceinline__ void score_epilogue(const f32x16 (&acc)[MR], const ScoreArgs &a, int row0, int wv,
+                                               int half, int blk, Weight wgt, Store store)
+{
+    const bool col_ok = blk < a.n_blocks;
+    // MASKED: every lane calls store(qi, blk, s, ok, qb) (qb: the first
+    // query of the row tile, wave-uniform) and the store itself drops the
+    // lanes whose ok is false; else only valid lanes call store(qi, blk, s).
+    auto emit = [&](int qi, float x, bool ok, int qb) {
+        if constexpr (MASKED)
+            store(qi, blk, x, ok, qb);
+        else if (ok)
+            store(qi, blk, x);
+    };
+    if constexpr (HP == 64) {
+        float s = 0.f;
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                s += wgt(m, v) * relu(acc[m][v]);
+            }
+        s = half_sum(s);
+        const int qi = (row0 + wv * MR * 32) / 64;
+        emit(qi, s, half == 0 && col_ok && qi < a.nq, qi);
+    } else {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            const int tile_row = (wv * MR + m) * 32;  // slab row of this tile's row 0
+            const int q0 = (row0 + tile_row) / HP;    // first query of the tile
+            if constexpr (HP >= 8) {
+                constexpr int SLOTS = 32 / HP;
+                float part[SLOTS];
+#pragma unroll
+                for (int s = 0; s < SLOTS; ++s)
+                    part[s] = 0.f;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    part[(8 * (v >> 2)) / HP] += wgt(m, v) * relu(acc[m][v]);
+#pragma unroll
+                for (int s = 0; s < SLOTS; ++s) {
+                    const float tot = half_sum(part[s]);
+                    const int qi = q0 + s;
+                    emit(qi, tot, half == 0 && col_ok && qi < a.nq, q0);
+                }
+            } else {
+                // HP <= 4: a lane's rows cover whole queries; no exchange.
+                constexpr int LS = 32 / HP;  // local slot index space
+                float part[LS];
+#pragma unroll
+                for (int s = 0; s < LS; ++s)
+                    part[s] = 0.f;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    part[(8 * (v >> 2)) / HP + (v & 3) / HP] += wgt(m, v) * relu(acc[m][v]);
+#pragma unroll
+                for (int v = 0; v < 16; v += HP) {
+                    const int s = (8 * (v >> 2)) / HP + (v & 3) / HP;
+                    const int qi = q0 + s + (4 * half) / HP;
+                    emit(qi, part[s], col_ok && qi < a.nq, q0);
+                }
+            }
+        }
+    }
+}
+
 // Scores of key tiles [t0, t1) for the NW*MR*32 padded rows from row0: q rows
 // of this wave into VGPRs, weights into LDS, then every tile through the
 // MFMAs and the epilogue; store(qi, blk, score) receives each score. All
@@ -134,72 +218,182 @@ __device__ __forceinline__ void score_tiles(const ScoreArgs &a, int row0, int t0
                         acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[m][4 * u + e], bv[e], acc[m], 0, 0, 0);
             }
 
-            // Epilogue: relu, weight, head sum, store.
-            const int blk = t * kTileBlocks + li;
-            const bool col_ok = blk < a.n_blocks;
-            if constexpr (HP == 64) {
-                float s = 0.f;
-#pragma unroll
-                for (int m = 0; m < MR; ++m)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int row = (wv * MR + m) * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-                        s += sm.w[row] * fmaxf(acc[m][v], 0.f);
-                    }
-                s += __shfl_xor(s, 32, 64);
-                const int qi = (row0 + wv * MR * 32) / 64;
-                if (half == 0 && col_ok && qi < a.nq)
-                    store(qi, blk, s);
-            } else {
-#pragma unroll
-                for (int m = 0; m < MR; ++m) {
-                    const int tile_row = (wv * MR + m) * 32;  // slab row of this tile's row 0
-                    const int q0 = (row0 + tile_row) / HP;    // first query of the tile
-                    if constexpr (HP >= 8) {
-                        constexpr int SLOTS = 32 / HP;
-                        float part[SLOTS];
-#pragma unroll
-                        for (int s = 0; s < SLOTS; ++s)
-                            part[s] = 0.f;
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int row = 8 * (v >> 2) + 4 * half + (v & 3);
-                            part[(8 * (v >> 2)) / HP] += sm.w[tile_row + row] * fmaxf(acc[m][v], 0.f);
-                        }
-#pragma unroll
-                        for (int s = 0; s < SLOTS; ++s) {
-                            const float tot = part[s] + __shfl_xor(part[s], 32, 64);
-                            const int qi = q0 + s;
-                            if (half == 0 && col_ok && qi < a.nq)
-                                store(qi, blk, tot);
-                        }
-                    } else {
-                        // HP <= 4: a lane's rows cover whole queries; no exchange.
-                        constexpr int LS = 32 / HP;  // local slot index space
-                        float part[LS];
-#pragma unroll
-                        for (int s = 0; s < LS; ++s)
-                            part[s] = 0.f;
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int row = 8 * (v >> 2) + 4 * half + (v & 3);
-                            part[(8 * (v >> 2)) / HP + (v & 3) / HP] += sm.w[tile_row + row] * fmaxf(acc[m][v], 0.f);
-                        }
-#pragma unroll
-                        for (int v = 0; v < 16; v += HP) {
-                            const int s = (8 * (v >> 2)) / HP + (v & 3) / HP;
-                            const int qi = q0 + s + (4 * half) / HP;
-                            if (col_ok && qi < a.nq)
-                                store(qi, blk, part[s]);
-                        }
-                    }
-                }
-            }
+            score_epilogue<HP, MR>(
+                acc, a, row0, wv, half, t * kTileBlocks + li,
+                [&](int m, int v) { return sm.w[(wv * MR + m) * 32 + 8 * (v >> 2) + 4 * half + (v & 3)]; }, store);
         }
 
         if (t + 1 < t1)
             store_tile(sm.k[cur ^ 1]);
         __syncthreads();
+    }
+}
+
+
+// ------------------------------------------------------------ BF16 inputs
+// The same scores from BF16 q and k (16-bit IEEE bfloat16 bit patterns) on
+// the BF16 matrix cores: v_mfma_f32_32x32x16_bf16 takes 8 consecutive
+// k-indices per lane, so step u of the 8 steps contracts k-indices 8u..8u+7
+// (lanes 0-31) and 64+8u..64+8u+7 (lanes 32-63): every lane again reads 64
+// consecutive values of its own q row and key row. Products of two BF16
+// values are exact in FP32 and accumulate in FP32; the epilogue is the FP32
+// path's. In ScoreArgs, q and k then point at BF16 data.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int kLdsRowH = 136;  // BF16 values per staged key row (128 + 8 pad: 272-byte rows)
+// Fourth word of a raw buffer resource on gfx9-family GPUs (32-bit data
+// format, no swizzle); with stride 0 an access at or past num_records bytes
+// is dropped (stores) or reads zero (loads).
+constexpr int kScoreBufferWord3 = 0x00020000;
+
+template <int ROWS>
+struct ScoreLdsH {
+    __attribute__((aligned(16))) uint16_t k[2][kTileBlocks * kLdsRowH];
+    float w[ROWS];
+};
+
+template <int HP, int MR, int NW, class Store>
+__device__ __forceinline__ void score_tiles_bf16(const ScoreArgs &a, int row0, int t0, int t1,
+                                                 ScoreLdsH<NW * MR * 32> &sm, Store store)
+{
+    constexpr int NT = NW * 64;
+    constexpr int ROWS = NW * MR * 32;
+    static_assert(HP <= 32 || (HP == 64 && MR == 2), "64 heads need both row tiles of a wave");
+    const uint16_t *qh = reinterpret_cast<const uint16_t *>(a.q);
+    const uint16_t *kh = reinterpret_cast<const uint16_t *>(a.k);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int li = lane & 31, half = lane >> 5;
+    const bool live = __builtin_amdgcn_readfirstlane(row0 + wv * MR * 32) < a.nq * HP;  // wave-uniform
+
+    // q rows of this wave -> VGPRs (A operand): 64 BF16 values per lane.
+    bf16x8 qa[MR][8];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        const int R = row0 + (wv * MR + m) * 32 + li;
+        const int qi = R / HP, h = R % HP;
+        const bool ok = qi < a.nq && h < a.heads;
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            qh + ((int64_t)(ok ? qi : 0) * a.heads + (ok ? h : 0)) * kHeadDim + 64 * half);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint4 v = ok ? src[u] : make_uint4(0u, 0u, 0u, 0u);
+            qa[m][u] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    for (int r = tid; r < ROWS; r += NT) {
+        const int R = row0 + r;
+        const int qi = R / HP, h = R % HP;
+        sm.w[r] = (qi < a.nq && h < a.heads) ? a.w[(int64_t)qi * a.heads + h] : 0.f;
+    }
+
+    // Key tile t -> registers: 8 KB per tile, CH bytes per thread. The loads
+    // are unconditional (a block past the end re-reads the last block, and
+    // its scores are never stored): a load under a branch would make the
+    // compiler wait for every load in flight before the next use.
+    constexpr int CH = kTileBlocks * kHeadDim * 2 / NT;  // bytes per thread: 32, 16 or 8 (256-1,024 threads)
+    static_assert(CH == 16 || CH == 8 || CH == 32, "a tile splits into 8, 16 or 32 bytes per thread");
+    constexpr int PS = CH < 16 ? CH : 16;                // bytes per load
+    constexpr int GPT = CH / PS;                         // loads per thread
+    constexpr int PPR = kHeadDim * 2 / PS;               // pieces per key row
+    uint4 pre[GPT];
+    auto load_tile = [&](int t) {
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) {
+            const int piece = tid * GPT + i;
+            const int blk = min(t * kTileBlocks + piece / PPR, a.n_blocks - 1);
+            const char *src = reinterpret_cast<const char *>(kh + (int64_t)blk * kHeadDim) + (piece % PPR) * PS;
+            if constexpr (PS == 8) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(src);
+                pre[i] = make_uint4(v.x, v.y, 0u, 0u);
+            } else {
+                pre[i] = *reinterpret_cast<const uint4 *>(src);
+            }
+        }
+    };
+    auto store_tile = [&](uint16_t *dst) {
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) {
+            const int piece = tid * GPT + i;
+            char *d = reinterpret_cast<char *>(dst + (piece / PPR) * kLdsRowH) + (piece % PPR) * PS;
+            if constexpr (PS == 8)
+                *reinterpret_cast<uint2 *>(d) = make_uint2(pre[i].x, pre[i].y);
+            else
+                *reinterpret_cast<uint4 *>(d) = pre[i];
+        }
+    };
+
+    // Key tiles come in PF deep: tile t + PF is loaded while tile t is
+    // scored, so the load latency hides behind PF - 1 tiles of matrix-core
+    // work (a tile is only 8 steps here), and the barrier between tiles
+    // orders LDS only, leaving the loads in flight. The loop body has no
+    // branch around a memory access, so the compiler waits for exactly the
+    // load a step needs: slots past the last tile score the last tile again
+    // with every store dropped, loads of tiles past the end re-read the last
+    // one, and waves whose rows are all padding score zero rows (their
+    // stores are dropped too).
+    constexpr int PF = 2;
+    uint4 ring[PF][GPT];
+    auto load_into = [&](int t, uint4 (&dst)[GPT]) {
+        load_tile(min(t, t1 - 1));
+#pragma unroll
+        for (int i = 0; i < GPT; ++i)
+            dst[i] = pre[i];
+    };
+    auto store_from = [&](const uint4 (&src)[GPT], uint16_t *dst) {
+#pragma unroll
+        for (int i = 0; i < GPT; ++i)
+            pre[i] = src[i];
+        store_tile(dst);
+    };
+#pragma unroll
+    for (int d = 0; d < PF; ++d)
+        load_into(t0 + d, ring[d]);
+    store_from(ring[0], sm.k[0]);
+    __syncthreads();
+
+    // The q rows and the first tiles were loaded above; nothing of the
+    // prologue is waited for inside the loop.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // This wave's weights, once, in registers.
+    float wr[MR][16];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            wr[m][v] = sm.w[(wv * MR + m) * 32 + 8 * (v >> 2) + 4 * half + (v & 3)];
+    (void)live;
+
+    for (int tb = t0; tb < t1; tb += PF) {
+#pragma unroll
+        for (int d = 0; d < PF; ++d) {
+            const int t = tb + d;
+            const int cur = d & 1;  // (t - t0) & 1, as PF is even
+            f32x16 acc[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[m][v] = 0.f;
+            const uint16_t *kb = &sm.k[cur][li * kLdsRowH + 64 * half];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(kb + 8 * u));
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+                    acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[m][u], b, acc[m], 0, 0, 0);
+            }
+            // A slot past the last tile: its column test fails for every lane.
+            const int blk = t < t1 ? t * kTileBlocks + li : a.n_blocks;
+            score_epilogue<HP, MR, true>(acc, a, row0, wv, half, blk, [&](int m, int v) { return wr[m][v]; },
+                                         store);
+            // Tile t + 1 (in ring slot (d + 1) % PF) into the other LDS buffer;
+            // tile t + PF into the slot tile t came from.
+            store_from(ring[(d + 1) % PF], sm.k[cur ^ 1]);
+            load_into(t + PF, ring[d]);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        }
     }
 }
 

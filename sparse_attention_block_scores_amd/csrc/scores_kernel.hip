@@ -1,4 +1,5 @@
-// scores_kernel.hip - indexer block scores on FP32 matrix cores (gfx950).
+// scores_kernel.hip - indexer block scores on the matrix cores (gfx950):
+// FP32 inputs on the FP32 matrix cores, or BF16 inputs on the BF16 ones.
 //
 // The contraction, its layout on the matrix cores and the epilogue are in
 // scores_device.h. This kernel owns the grid:
@@ -7,6 +8,8 @@
 //  * Grid: slabs x column groups. Workgroup ids go round-robin over the 8
 //    XCDs; ids are mapped so that all slabs of one column group run on the
 //    same XCD and share its L2 for the key tiles.
+#include <type_traits>
+
 #include "scores_device.h"
 
 namespace qsa {
@@ -25,11 +28,12 @@ struct ScoreGrid {
 // two 4-wave or two 8-wave workgroups per CU, or one 16-wave workgroup. With
 // 1 or 2 heads the epilogue keeps a partial sum per row and gets the larger
 // budget of one 8-wave workgroup per CU instead of spilling.
-template <int HP, int MR, int NW>
+template <int HP, int MR, int NW, bool BF16>
 __global__ __launch_bounds__(NW * 64, NW >= 8 && HP >= 4 ? 4 : 2) void scores_kernel(ScoreArgs a, ScoreGrid grid)
 {
     constexpr int ROWS = NW * MR * 32;
-    __shared__ ScoreLds<ROWS> sm;
+    using Lds = typename std::conditional<BF16, ScoreLdsH<ROWS>, ScoreLds<ROWS>>::type;
+    __shared__ Lds sm;
 
     int slab, grp;
     {
@@ -47,11 +51,31 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 && HP >= 4 ? 4 : 2) void scores_ke
     const int t1 = min(t0 + grid.tiles_per_group, grid.n_tiles);
     if (t0 >= t1)
         return;
-    score_tiles<HP, MR, NW>(a, slab * ROWS, t0, t1, sm,
-                            [&](int qi, int blk, float s) { a.scores[(int64_t)qi * a.ld + blk] = s; });
+    if constexpr (BF16) {
+        // Unconditional buffer stores: a lane with nothing to store gets an
+        // offset past the resource's end, which the hardware drops. (A store
+        // under a branch would make the compiler wait for every memory access
+        // in flight before the next tile's loads are used.) The resource
+        // spans the score rows of the tile's queries; ld < 2^24 keeps its
+        // size and every offset below 2^31.
+        auto store = [&](int qi, int blk, float s, bool ok, int qb) {
+            // A tile of padding rows (qb >= nq) gets an empty resource: every
+            // store of it is dropped, and its base stays inside the matrix.
+            const bool any = qb < a.nq;
+            const int rows = any ? min(a.nq - qb, 32) : 0;
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                a.scores + (int64_t)(any ? qb : 0) * a.ld, (short)0, rows * (int)a.ld * 4, kScoreBufferWord3);
+            const int off = ok ? ((qi - qb) * (int)a.ld + blk) * 4 : (int)0x80000000;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), r, off, 0, 0);
+        };
+        score_tiles_bf16<HP, MR, NW>(a, slab * ROWS, t0, t1, sm, store);
+    } else {
+        score_tiles<HP, MR, NW>(a, slab * ROWS, t0, t1, sm,
+                                [&](int qi, int blk, float s) { a.scores[(int64_t)qi * a.ld + blk] = s; });
+    }
 }
 
-template <int HP, int MR, int NW>
+template <int HP, int MR, int NW, bool BF16>
 hipError_t launch_cfg(const ScoreArgs &a, hipStream_t s)
 {
     constexpr int ROWS = NW * MR * 32;
@@ -71,7 +95,7 @@ hipError_t launch_cfg(const ScoreArgs &a, hipStream_t s)
     const int64_t wgs = (int64_t)g.n_slabs * groups;
     if (wgs > 0x7fffffff)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((scores_kernel<HP, MR, NW>), dim3((unsigned)wgs), dim3(NW * 64), 0, s, a, g);
+    hipLaunchKernelGGL((scores_kernel<HP, MR, NW, BF16>), dim3((unsigned)wgs), dim3(NW * 64), 0, s, a, g);
     return hipGetLastError();
 }
 
@@ -81,34 +105,39 @@ hipError_t launch_cfg(const ScoreArgs &a, hipStream_t s)
 // each CU stages and the key traffic from L2; few rows take 8-wave
 // workgroups, two per CU, so that more of them share the columns (as do
 // 1 or 2 heads).
-template <int HP>
+template <int HP, bool BF16>
 hipError_t launch_hp(const ScoreArgs &a, hipStream_t s)
 {
     if constexpr (HP == 64) {
-        return launch_cfg<HP, 2, 4>(a, s);
+        return launch_cfg<HP, 2, 4, BF16>(a, s);
     } else {
         const int64_t rows = (int64_t)a.nq * HP;
         if constexpr (HP >= 4) {  // 1 or 2 heads: the epilogue's partial sums need more VGPRs
             if (rows >= 16 * 512)
-                return launch_cfg<HP, 1, 16>(a, s);
+                return launch_cfg<HP, 1, 16, BF16>(a, s);
         }
-        return launch_cfg<HP, 1, 8>(a, s);
+        return launch_cfg<HP, 1, 8, BF16>(a, s);
     }
+}
+
+template <bool BF16>
+hipError_t launch_heads(const ScoreArgs &a, hipStream_t s)
+{
+    const int h = a.heads;
+    if (h <= 1) return launch_hp<1, BF16>(a, s);
+    if (h <= 2) return launch_hp<2, BF16>(a, s);
+    if (h <= 4) return launch_hp<4, BF16>(a, s);
+    if (h <= 8) return launch_hp<8, BF16>(a, s);
+    if (h <= 16) return launch_hp<16, BF16>(a, s);
+    if (h <= 32) return launch_hp<32, BF16>(a, s);
+    if (h <= 64) return launch_hp<64, BF16>(a, s);
+    return hipErrorInvalidValue;
 }
 
 } // namespace
 
-hipError_t launch_scores(const ScoreArgs &a, hipStream_t s)
-{
-    const int h = a.heads;
-    if (h <= 1) return launch_hp<1>(a, s);
-    if (h <= 2) return launch_hp<2>(a, s);
-    if (h <= 4) return launch_hp<4>(a, s);
-    if (h <= 8) return launch_hp<8>(a, s);
-    if (h <= 16) return launch_hp<16>(a, s);
-    if (h <= 32) return launch_hp<32>(a, s);
-    if (h <= 64) return launch_hp<64>(a, s);
-    return hipErrorInvalidValue;
-}
+hipError_t launch_scores(const ScoreArgs &a, hipStream_t s) { return launch_heads<false>(a, s); }
+
+hipError_t launch_scores_bf16(const ScoreArgs &a, hipStream_t s) { return launch_heads<true>(a, s); }
 
 } // namespace qsa

@@ -98,6 +98,20 @@ def quantize64(z: np.ndarray) -> np.ndarray:
     return (np.clip(np.rint(z.astype(np.float64) * 8.0), -32, 31) / 8.0).astype(np.float32)
 
 
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 values rounded to bfloat16 (the top 16 bits of the float32
+    pattern, rounded to nearest, ties to even), as uint16 bit patterns. Inputs
+    must be finite. This only defines the inputs of the BF16 scorer."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_values(bits: np.ndarray) -> np.ndarray:
+    """The float32 values of bfloat16 bit patterns (exact)."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
 def integers(tag: str, n: int, lo: int, hi: int) -> np.ndarray:
     """n integers uniform in [lo, hi] (inclusive) from the stream ``tag``."""
     x = splitmix64(stream_seed(tag), n)

@@ -98,3 +98,77 @@ def test_prompt_select_shape_sampled():
     err = np.abs(s[qi, bi].astype(np.float64) - ref)
     assert (err <= tol).all(), f"worst {np.max(err / tol):.3f} x tolerance"
     assert_scores_close(s[:2], rows, "C5 rows 0-1")
+
+
+# ---------------------------------------------------------------- BF16 inputs
+# qsa_block_scores_bf16 takes q and k rounded to bfloat16; the oracle scores
+# the same (exactly representable) values in FP64, so the tolerance is the
+# FP32 path's: only the FP32 accumulation differs from the exact result.
+
+def gpu_scores_bf16(qb, kb, w, ld=None, fill=None):
+    nq, nb = qb.shape[0], kb.shape[0]
+    ld = nb if ld is None else ld
+    s = torch.full((nq, ld), float("nan") if fill is None else fill, dtype=torch.float32, device="cuda")
+    q = to_dev(qb.view(np.int16)).view(torch.bfloat16)
+    k = to_dev(kb.view(np.int16)).view(torch.bfloat16)
+    qsa.block_scores_bf16(q, k, to_dev(w), scores=s)
+    torch.cuda.synchronize()
+    return s.cpu().numpy()
+
+
+@pytest.mark.parametrize("heads", [1, 2, 3, 8, 16, 17, 32, 33, 64])
+@pytest.mark.parametrize("nq,n_blocks", [(1, 1), (3, 1000), (7, 4133), (19, 2049)])
+def test_bf16_shapes(heads, nq, n_blocks):
+    tag = f"gpu/scores_bf16/{heads}/{nq}/{n_blocks}"
+    qb = synth.bf16_bits(synth.normal(tag + "/q", (nq, heads, 128)))
+    kb = synth.bf16_bits(synth.normal(tag + "/k", (n_blocks, 128)))
+    w = synth.uniform01(tag + "/w", (nq, heads)) * 2.0 - 0.5
+    q, k = synth.bf16_values(qb), synth.bf16_values(kb)
+    say(f"scores bf16 heads={heads} nq={nq} nb={n_blocks}")
+    s = gpu_scores_bf16(qb, kb, w, ld=n_blocks + 3, fill=7.0)
+    ref = oracle.block_scores(q, k, w)
+    terms = oracle.block_scores(np.abs(q), np.abs(k), np.abs(w))
+    assert_scores_close(s[:, :n_blocks], ref, f"bf16 h={heads} nq={nq} nb={n_blocks}", terms)
+    assert (s[:, n_blocks:] == 7.0).all(), "columns past n_blocks were written"
+
+
+@pytest.mark.parametrize("heads,nq", [(8, 1030), (31, 257)])
+def test_bf16_many_rows(heads, nq):
+    n_blocks = 1000
+    tag = f"gpu/scores_bf16/many/{heads}/{nq}"
+    qb = synth.bf16_bits(synth.normal(tag + "/q", (nq, heads, 128)))
+    kb = synth.bf16_bits(synth.normal(tag + "/k", (n_blocks, 128)))
+    w = synth.uniform01(tag + "/w", (nq, heads))
+    say(f"scores bf16 many rows heads={heads} nq={nq}")
+    s = gpu_scores_bf16(qb, kb, w, ld=n_blocks + 1, fill=7.0)
+    ref = oracle.block_scores(synth.bf16_values(qb), synth.bf16_values(kb), w)
+    assert_scores_close(s[:, :n_blocks], ref, f"bf16 many rows h={heads} nq={nq}")
+    assert (s[:, n_blocks:] == 7.0).all(), "columns past n_blocks were written"
+
+
+def test_bf16_decode_select_shapes_full():
+    for wl in (synth.c1(), synth.c3()):
+        q, k, w = wl.tensors()
+        qb, kb = synth.bf16_bits(q), synth.bf16_bits(k)
+        say(f"scores bf16 {wl.name} full")
+        s = gpu_scores_bf16(qb, kb, w)
+        ref = oracle.block_scores(synth.bf16_values(qb), synth.bf16_values(kb), w)
+        assert_scores_close(s, ref, f"bf16 {wl.name}")
+
+
+def test_bf16_prompt_select_shape_sampled():
+    wl = synth.c5()
+    q, k, w = wl.tensors()
+    qb, kb = synth.bf16_bits(q), synth.bf16_bits(k)
+    q, k = synth.bf16_values(qb), synth.bf16_values(kb)
+    say("scores bf16 C5 full size")
+    s = gpu_scores_bf16(qb, kb, w)
+    qi = synth.integers("gpu/scores_bf16/C5/qi", 20000, 0, wl.nq - 1).astype(np.int32)
+    bi = synth.integers("gpu/scores_bf16/C5/bi", 20000, 0, wl.n_blocks - 1).astype(np.int32)
+    ref = oracle.block_scores_at(q, k, w, qi, bi)
+    rows = oracle.block_scores(q[:2], k, w[:2])
+    floor = 0.01 * np.abs(rows).mean()
+    tol = 1e-4 * np.maximum(np.abs(ref), floor)
+    err = np.abs(s[qi, bi].astype(np.float64) - ref)
+    assert (err <= tol).all(), f"worst {np.max(err / tol):.3f} x tolerance"
+    assert_scores_close(s[:2], rows, "bf16 C5 rows 0-1")

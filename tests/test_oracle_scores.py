@@ -144,3 +144,4 @@ def test_weights_enter_linearly(oracle_lib):
     s1 = oracle_lib.block_scores(q, k, w)
     s2 = oracle_lib.block_scores(q, k, 2 * w)
     assert (s2 == 2 * s1).all()
+
