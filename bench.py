@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 METRIC = "qsa_select µs/call (score+top-k) decode nq=3 & prompt nq=256; % HBM/MFMA peak"
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 SCORER_SOURCES = [os.path.join(ROOT, "sparse_attention_block_scores_amd", "csrc", f)
                   for f in ("scores_kernel.hip", "scores_device.h")]
@@ -200,6 +201,22 @@ def secondary(torch, qsa, synth, dev, reps=50):
             del bufs
         prm[str(nb * 4)] = entry
     out["prompt_nq256_topk_by_cells"] = prm
+
+    # The BF16-input scorer (qsa_block_scores_bf16) on the prompt-call and
+    # 16-query decode shapes; torch's float -> bfloat16 conversion rounds to
+    # nearest even, as the parity tests do.
+    bf = {}
+    for wlb in (synth.c5(), synth.c3()):
+        qh, kh, wh = wlb.tensors()
+        qb = torch.from_numpy(qh).to(dev).to(torch.bfloat16)
+        kb = torch.from_numpy(kh).to(dev).to(torch.bfloat16)
+        wb = torch.from_numpy(wh).to(dev)
+        sb = torch.empty((wlb.nq, wlb.n_blocks), device=dev)
+        us = time_us(lambda i: qsa.block_scores_bf16(qb, kb, wb, scores=sb, stream=cur()), n=20)
+        tf = wlb.flops() / (us * 1e-6) / 1e12
+        bf[wlb.name] = {"us": round(us, 2), "TFLOPs": round(tf, 1), "bf16_peak_frac": round(tf / PEAK_BF16_MFMA_TFLOPS, 4)}
+        del qb, kb, wb, sb
+    out["bf16_scorer"] = bf
     return out
 
 

@@ -133,8 +133,9 @@ qsa_status qsa_block_scores(const float *q, const float *k, const float *w,
                             int32_t n_blocks, void *stream);
 
 /*
- * qsa_block_scores_bf16 - step 1 with BF16 q and k (a low-precision variant
- * the pages mention for the scorer; Strata pull #1091, section What).
+ * qsa_block_scores_bf16 - step 1 with BF16 q and k: the lower-precision
+ * tensor-core scorer that Strata pull #1091 names as an existing switch in its
+ * opening description; the score itself is that pull's section What.
  *
  *   q       [nq][n_heads][head_dim] bfloat16 (raw 16-bit IEEE bfloat16
  *           values), row-major, 16-byte aligned
