@@ -1,4 +1,5 @@
-"""Plain CPU oracle for block scores and block top-k (ctypes wrapper).
+"""Plain CPU oracle for block scores, block top-k and the attention over
+the selected cells (ctypes wrapper).
 
 TEST INFRASTRUCTURE ONLY: tests/, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package; the HIP product
@@ -43,7 +44,9 @@ class Library:
         topk = ("oracle_topk_sort", "oracle_topk_rule", "oracle_topk_sort_cells", "oracle_topk_rule_cells")
         for name in topk:
             getattr(lib, name).argtypes = [P, i64, i32, i32, i32, i32, P, P, P]
-        for name in ("oracle_block_scores", "oracle_block_scores_at") + topk:
+        lib.oracle_selection_attention.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, i32, i32,
+                                                   ctypes.c_double, P, P]
+        for name in ("oracle_block_scores", "oracle_block_scores_at", "oracle_selection_attention") + topk:
             getattr(lib, name).restype = None
         self.lib = lib
         self.path = path
@@ -104,6 +107,27 @@ class Library:
         return self._topk("oracle_topk_rule_cells", scores, n_blocks, block_size, width, cells)
 
 
+    def selection_attention(self, q, k, v, ids, scale: float):
+        """FP64 attention of every query head over the cells listed in its
+        query's row of ``ids``: returns out [nq, n_heads, head_dim] and
+        lse [nq, n_heads]. q [nq, n_heads, D], k and v [n_cells, kv_heads, D]
+        (float32 values), ids [nq, width] int32 (entries outside
+        [0, n_cells) select nothing)."""
+        q, k, v = _f32(q), _f32(k), _f32(v)
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        nq, n_heads, head_dim = q.shape
+        n_cells, kv_heads = k.shape[0], k.shape[1]
+        assert k.shape == v.shape == (n_cells, kv_heads, head_dim)
+        assert n_heads % kv_heads == 0 and ids.shape[0] == nq
+        width = ids.shape[1]
+        out = np.zeros((nq, n_heads, head_dim), dtype=np.float64)
+        lse = np.zeros((nq, n_heads), dtype=np.float64)
+        self.lib.oracle_selection_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(ids), width, nq, n_heads,
+                                            kv_heads, head_dim, n_cells, width, float(scale),
+                                            _ptr(out), _ptr(lse))
+        return out, lse
+
+
 def compile_source(source_text: str, out_path: str) -> str:
     """Compile a (possibly edited) copy of the oracle source; used by the
     mutation tests that check the pins catch planted mistakes."""
@@ -156,3 +180,7 @@ def topk_sort_cells(scores, n_blocks, block_size, width, cells):
 
 def topk_rule_cells(scores, n_blocks, block_size, width, cells):
     return _load().topk_rule_cells(scores, n_blocks, block_size, width, cells)
+
+
+def selection_attention(q, k, v, ids, scale):
+    return _load().selection_attention(q, k, v, ids, scale)

@@ -30,6 +30,20 @@
  *     32-bit image of the float keys), not by sorting, so that forms 2 and 3
  *     are two independent computations of one definition.
  *
+ *  4. Attention over the selected cells, the consumer of the selection
+ *     (iree-org/wave issue #1257 "NSA: LDS optimization for block-gather in
+ *     selection attention", sections Problem and Per-block LDS staging: each
+ *     query attends to the key/value pairs of the cells it selected, and the
+ *     query heads of one group share one key/value head). For query q, query
+ *     head h and its key/value head g = h / (n_heads / kv_heads):
+ *         s_c = scale * sum_d q[q][h][d] * k[c][g][d]     for each listed c
+ *         out[q][h][:] = sum_c exp(s_c) * v[c][g][:] / sum_c exp(s_c)
+ *         lse[q][h]    = log(sum_c exp(s_c))
+ *     over the entries c of row q of the id list that lie in [0, n_cells)
+ *     (others select nothing). A query that selects nothing gets out = 0 and
+ *     lse = -inf. Every exp(s_c) is taken as exp(s_c - max s) * exp(max s),
+ *     the same ratios without overflow.
+ *
  * Visible cells: on a decode call every cell of the n_blocks blocks; on a
  * prompt call the cells of the first min(max(active[q], 0), n_blocks) blocks
  * of query q. The *_cells entry points take a cell count per query instead,
@@ -37,6 +51,7 @@
  * block may hold fewer than block_size cells; every visible cell still carries
  * its block's key.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -259,4 +274,62 @@ EXPORT void oracle_topk_rule_cells(const float *scores, int64_t ld, int nq, int 
                                    int32_t *ids, int32_t *counts)
 {
     topk_rule(scores, ld, nq, n_blocks, block_size, width, NULL, cells, ids, counts);
+}
+
+/* ------------------------------------------------- selection attention */
+
+EXPORT void oracle_selection_attention(const float *q, const float *k, const float *v,
+                                       const int32_t *ids, int64_t ld_ids, int nq,
+                                       int n_heads, int kv_heads, int head_dim,
+                                       int n_cells, int width, double scale,
+                                       double *out, double *lse)
+{
+    const int group = n_heads / kv_heads;
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+    for (int iq = 0; iq < nq; ++iq) {
+        for (int h = 0; h < n_heads; ++h) {
+            const int g = h / group;
+            const float *qrow = q + ((int64_t)iq * n_heads + h) * head_dim;
+            const int32_t *list = ids + (int64_t)iq * ld_ids;
+            double *o = out + ((int64_t)iq * n_heads + h) * head_dim;
+            double *s = malloc(sizeof(double) * (size_t)(width > 0 ? width : 1));
+            /* logits of the listed cells (NAN marks an entry that selects nothing) */
+            double top = -INFINITY;
+            for (int i = 0; i < width; ++i) {
+                const int32_t c = list[i];
+                if (c < 0 || c >= n_cells) {
+                    s[i] = NAN;
+                    continue;
+                }
+                const float *krow = k + ((int64_t)c * kv_heads + g) * head_dim;
+                double dot = 0.0;
+                for (int d = 0; d < head_dim; ++d)
+                    dot += (double)qrow[d] * (double)krow[d];
+                s[i] = scale * dot;
+                if (s[i] > top)
+                    top = s[i];
+            }
+            for (int d = 0; d < head_dim; ++d)
+                o[d] = 0.0;
+            double total = 0.0;
+            for (int i = 0; i < width; ++i) {
+                if (isnan(s[i]))
+                    continue;
+                const double e = exp(s[i] - top);
+                const float *vrow = v + ((int64_t)list[i] * kv_heads + g) * head_dim;
+                total += e;
+                for (int d = 0; d < head_dim; ++d)
+                    o[d] += e * (double)vrow[d];
+            }
+            if (total > 0.0) {
+                for (int d = 0; d < head_dim; ++d)
+                    o[d] /= total;
+                if (lse)
+                    lse[(int64_t)iq * n_heads + h] = top + log(total);
+            } else if (lse) {
+                lse[(int64_t)iq * n_heads + h] = -INFINITY;
+            }
+            free(s);
+        }
+    }
 }

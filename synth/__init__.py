@@ -27,6 +27,7 @@ cells, a 2,048-cell selection); see ``c1`` .. ``c5``.
 """
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass
 
 import numpy as np
@@ -72,24 +73,37 @@ def uniform01(tag: str, shape, dtype=np.float32) -> np.ndarray:
     return u.astype(dtype).reshape(shape)
 
 
-def normal(tag: str, shape, dtype=np.float32, chunk: int = 1 << 22) -> np.ndarray:
-    """N(0,1) by Box-Muller, generated in slices to bound host memory."""
+def _normal_slice(seed: int, n: int, p0: int, p1: int, out: np.ndarray) -> None:
+    x = splitmix64(seed, 2 * (p1 - p0), offset=2 * p0)
+    u1 = ((x[0::2] >> np.uint64(11)).astype(np.float64) + 1.0) * _TWO_M53
+    u2 = (x[1::2] >> np.uint64(11)).astype(np.float64) * _TWO_M53
+    r = np.sqrt(-2.0 * np.log(u1))
+    z = np.empty(2 * (p1 - p0), dtype=np.float64)
+    z[0::2] = r * np.cos(2.0 * np.pi * u2)
+    z[1::2] = r * np.sin(2.0 * np.pi * u2)
+    lo = 2 * p0
+    hi = min(n, 2 * p1)
+    out[lo:hi] = z[: hi - lo].astype(out.dtype)
+
+
+def normal(tag: str, shape, dtype=np.float32, chunk: int = 1 << 21) -> np.ndarray:
+    """N(0,1) by Box-Muller, generated in slices to bound host memory. The
+    stream is counter based, so the slices are independent and large tensors
+    fill them on several threads (numpy releases the GIL); the values do not
+    depend on the thread count."""
     n = int(np.prod(shape))
     seed = stream_seed(tag)
     out = np.empty(n, dtype=dtype)
     npairs = (n + 1) // 2
-    for p0 in range(0, npairs, chunk):
-        p1 = min(npairs, p0 + chunk)
-        x = splitmix64(seed, 2 * (p1 - p0), offset=2 * p0)
-        u1 = ((x[0::2] >> np.uint64(11)).astype(np.float64) + 1.0) * _TWO_M53
-        u2 = (x[1::2] >> np.uint64(11)).astype(np.float64) * _TWO_M53
-        r = np.sqrt(-2.0 * np.log(u1))
-        z = np.empty(2 * (p1 - p0), dtype=np.float64)
-        z[0::2] = r * np.cos(2.0 * np.pi * u2)
-        z[1::2] = r * np.sin(2.0 * np.pi * u2)
-        lo = 2 * p0
-        hi = min(n, 2 * p1)
-        out[lo:hi] = z[: hi - lo].astype(dtype)
+    slices = [(p0, min(npairs, p0 + chunk)) for p0 in range(0, npairs, chunk)]
+    if len(slices) <= 1:
+        for p0, p1 in slices:
+            _normal_slice(seed, n, p0, p1, out)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        workers = max(1, min(len(slices), os.cpu_count() or 1, 16))
+        with ThreadPoolExecutor(workers) as pool:
+            list(pool.map(lambda sl: _normal_slice(seed, n, sl[0], sl[1], out), slices))
     return out.reshape(shape)
 
 
@@ -194,3 +208,73 @@ def c4(n_blocks: int, variant: str = "continuous") -> TopkWorkload:
 
 def c5() -> SelectWorkload:
     return SelectWorkload("C5", nq=256, heads=32, n_blocks=131072, block_size=4, width=2048, call="prompt")
+
+
+# --------------------------------------------------------------------------
+# Attention over the selected cells
+# --------------------------------------------------------------------------
+@dataclass
+class AttnWorkload:
+    """Attention of every query head over its query's selected cells:
+    q[nq, heads, 128], k and v[n_cells, kv_heads, 128] N(0,1) rounded to
+    bfloat16; the selection of each query is ``width // block_size`` distinct
+    blocks drawn uniformly from the ``n_cells // block_size`` blocks, in
+    ascending cell order (the form the block top-k emits)."""
+    name: str
+    nq: int
+    heads: int
+    kv_heads: int
+    n_cells: int
+    width: int
+    block_size: int = 4
+    head_dim: int = 128
+
+    def tensors(self):
+        """bfloat16 bit patterns (uint16) of q, k and v."""
+        q = bf16_bits(normal(f"{self.name}/q", (self.nq, self.heads, self.head_dim)))
+        k = bf16_bits(normal(f"{self.name}/k", (self.n_cells, self.kv_heads, self.head_dim)))
+        v = bf16_bits(normal(f"{self.name}/v", (self.n_cells, self.kv_heads, self.head_dim)))
+        return q, k, v
+
+    def selection(self):
+        return random_selection(f"{self.name}/ids", self.nq, self.n_cells // self.block_size,
+                                self.block_size, self.width)
+
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.head_dim))
+
+    def gathered_bytes(self, ids=None) -> int:
+        """K and V bytes of the listed cells (2 bytes per element)."""
+        ids = self.selection() if ids is None else ids
+        cells = int(((ids >= 0) & (ids < self.n_cells)).sum())
+        return cells * self.kv_heads * self.head_dim * 2 * 2
+
+
+def random_selection(tag: str, nq: int, n_blocks: int, block_size: int, width: int) -> np.ndarray:
+    """ids [nq, width] int32: per query, min(width // block_size, n_blocks)
+    distinct blocks uniform over [0, n_blocks) (the blocks of the smallest
+    stream values), expanded to their cells in ascending order, then -1."""
+    nsel = min(width // block_size, n_blocks)
+    ids = np.full((nq, width), -1, dtype=np.int32)
+    cells = np.arange(block_size, dtype=np.int64)
+    for iq in range(nq):
+        x = splitmix64(stream_seed(f"{tag}/{iq}"), n_blocks)
+        blocks = np.sort(np.argpartition(x, nsel - 1)[:nsel]) if nsel < n_blocks else np.arange(n_blocks)
+        row = (blocks[:, None] * block_size + cells[None, :]).reshape(-1)
+        ids[iq, : row.size] = row
+    return ids
+
+
+def a1() -> AttnWorkload:
+    """Tiny decode: 3 queries, 2 key/value heads of 8 query heads, 4,096 cells."""
+    return AttnWorkload("A1", nq=3, heads=16, kv_heads=2, n_cells=4096, width=256)
+
+
+def a3() -> AttnWorkload:
+    """Decode: 16 queries, one group of 16 heads, 262,144 cells, 2,048 selected."""
+    return AttnWorkload("A3", nq=16, heads=16, kv_heads=1, n_cells=262144, width=2048)
+
+
+def a5() -> AttnWorkload:
+    """Prompt chunk: 256 queries, one group of 16 heads, 524,288 cells, 2,048 selected."""
+    return AttnWorkload("A5", nq=256, heads=16, kv_heads=1, n_cells=524288, width=2048)

@@ -10,6 +10,7 @@ import os
 import pytest
 
 import oracle
+import test_oracle_attention as A
 import test_oracle_scores as S
 import test_oracle_topk as T
 
@@ -33,6 +34,16 @@ TOPK_PINS = [
     lambda lib: T.test_cells_hand_cases(lib, "topk_sort_cells"),
     lambda lib: T.test_cells_hand_cases(lib, "topk_rule_cells"),
     lambda lib: T.test_cells_brute_force_tiny(lib, 3),
+]
+
+ATTN_PINS = [
+    A.test_single_cell_returns_its_value,
+    A.test_equal_logits_average_the_values,
+    A.test_two_cells_are_a_logistic_mix,
+    lambda lib: A.test_full_selection_is_dense_attention(lib, 8, 2),
+    A.test_order_padding_and_foreign_ids_do_not_matter,
+    A.test_empty_selection,
+    A.test_group_sharing_uses_consecutive_heads,
 ]
 
 # (name, original text, planted mistake, pins expected to notice)
@@ -76,6 +87,20 @@ MUTANTS = [
     ("visible cells rounded up to whole blocks", "        return c < 0 ? 0 : (c > all ? all : c);",
      "        c = (c + block_size - 1) / block_size * block_size;\n        return c < 0 ? 0 : (c > all ? all : c);",
      TOPK_PINS),
+    ("attention scale dropped", "s[i] = scale * dot;", "s[i] = dot;", ATTN_PINS),
+    ("attention key head by modulo", "const int g = h / group;", "const int g = h % kv_heads;", ATTN_PINS),
+    ("attention not normalised", "o[d] /= total;", "o[d] /= 1.0;", ATTN_PINS),
+    ("attention lse without the max", "lse[(int64_t)iq * n_heads + h] = top + log(total);",
+     "lse[(int64_t)iq * n_heads + h] = log(total);", ATTN_PINS),
+    ("attention reads keys as values", "const float *vrow = v + ((int64_t)list[i] * kv_heads + g) * head_dim;",
+     "const float *vrow = k + ((int64_t)list[i] * kv_heads + g) * head_dim;", ATTN_PINS),
+    ("attention drops the last listed cell", "            for (int i = 0; i < width; ++i) {\n                if (isnan(s[i]))",
+     "            for (int i = 0; i < width - 1; ++i) {\n                if (isnan(s[i]))", ATTN_PINS),
+    ("attention keeps foreign ids", "if (c < 0 || c >= n_cells) {", "if (c < 0) {", ATTN_PINS),
+    ("attention weights without the exponential", "const double e = exp(s[i] - top);",
+     "const double e = 1.0 + (s[i] - top);", ATTN_PINS),
+    ("attention cell rows without the head stride", "k + ((int64_t)c * kv_heads + g) * head_dim;",
+     "k + ((int64_t)c + g) * head_dim;", ATTN_PINS),
 ]
 
 
