@@ -229,6 +229,37 @@ qsa_status qsa_select_cells(const float *q, const float *k, const float *w,
                             void *workspace, size_t workspace_bytes, void *stream,
                             const qsa_options *opt);
 
+/*
+ * qsa_selection_attention - attention of every query head over the cells its
+ * query selected: the consumer of the selection (iree-org/wave issue #1257
+ * "NSA: LDS optimization for block-gather in selection attention", sections
+ * Problem and Per-block LDS staging). The heads of one group,
+ * g = h / (n_heads / kv_heads), share key/value head g:
+ *     s_c        = scale * q[q][h][:] . k[c][g][:]   for each listed cell c
+ *     out[q][h]  = sum_c exp(s_c) v[c][g][:] / sum_c exp(s_c)
+ *     lse[q][h]  = log(sum_c exp(s_c))
+ *
+ *   q      [nq][n_heads][head_dim]    bfloat16 (raw 16-bit values), 16-byte aligned
+ *   k, v   [n_cells][kv_heads][head_dim] bfloat16, 16-byte aligned
+ *   ids    [nq][ld_ids] int32 device; entries 0 .. width-1 of each row are the
+ *          query's list (the cell_ids of qsa_block_topk fit as they are); an
+ *          entry outside [0, n_cells) selects nothing
+ *   out    [nq][n_heads][head_dim] float output, 16-byte aligned
+ *   lse    [nq][n_heads] float output (natural log), or NULL
+ *   A query that selects no cell gets out = 0 and lse = -inf.
+ *   head_dim must be 128 (else QSA_EUNSUPPORTED); n_heads a multiple of
+ *   kv_heads; n_cells, width >= 1; ld_ids >= width; scale finite.
+ *   Products of bfloat16 values with FP32 accumulation, FP32 softmax.
+ *   workspace: qsa_selection_attention_workspace_bytes() bytes, 256-byte
+ *   aligned (may be NULL when that is 0); per call, contents need no set-up.
+ */
+size_t qsa_selection_attention_workspace_bytes(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width);
+qsa_status qsa_selection_attention(const void *q, const void *k, const void *v,
+                                   const int32_t *ids, int64_t ld_ids, float *out, float *lse,
+                                   int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t head_dim,
+                                   int32_t n_cells, int32_t width, float scale,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *qsa_status_str(qsa_status status);
 

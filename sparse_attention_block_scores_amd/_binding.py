@@ -89,8 +89,12 @@ def lib() -> ctypes.CDLL:
         L.qsa_select.argtypes = [P, P, P, i32, i32, P, i64, i32, i32, i32, i32, i32, P, P, P, P, sz, P, P]
         L.qsa_block_topk_cells.argtypes = L.qsa_block_topk.argtypes
         L.qsa_select_cells.argtypes = L.qsa_select.argtypes
+        L.qsa_selection_attention_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.qsa_selection_attention_workspace_bytes.restype = sz
+        L.qsa_selection_attention.argtypes = [P, P, P, P, i64, P, P, i32, i32, i32, i32, i32, i32,
+                                              ctypes.c_float, P, sz, P]
         for name in ("qsa_block_scores", "qsa_block_scores_bf16", "qsa_topk_plan_get", "qsa_workspace_init", "qsa_block_topk",
-                     "qsa_select", "qsa_block_topk_cells", "qsa_select_cells"):
+                     "qsa_select", "qsa_block_topk_cells", "qsa_select_cells", "qsa_selection_attention"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -209,6 +213,49 @@ def block_scores_bf16(q, k, w, scores=None, stream=None):
     _check(lib().qsa_block_scores_bf16(_ptr(q), _ptr(k), _ptr(w), _ptr(scores), scores.stride(0), nq, heads,
                                        head_dim, n_blocks, _stream(stream)), "qsa_block_scores_bf16")
     return scores
+
+
+def attention_workspace_bytes(nq: int, n_heads: int, kv_heads: int, width: int) -> int:
+    return int(lib().qsa_selection_attention_workspace_bytes(nq, n_heads, kv_heads, width))
+
+
+def selection_attention(q, k, v, ids, width=None, scale=None, out=None, lse=None, ws=None, stream=None):
+    """Attention of each query head over its query's listed cells.
+
+    q [nq, n_heads, 128] and k, v [n_cells, kv_heads, 128] bfloat16; ids
+    [nq, ld] int32 (the first ``width`` entries of a row are the list,
+    default all of them; entries outside [0, n_cells) select nothing).
+    scale defaults to 1/sqrt(128). Returns (out [nq, n_heads, 128] float32,
+    lse [nq, n_heads] float32)."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, torch.bfloat16, name)
+        if not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous 3-d tensor")
+    _dev(ids, torch.int32, "ids")
+    if ids.dim() != 2 or ids.stride(1) != 1:
+        raise ValueError("ids must be [nq, ld] with unit column stride")
+    nq, n_heads, head_dim = q.shape
+    n_cells, kv_heads = k.shape[0], k.shape[1]
+    if tuple(v.shape) != tuple(k.shape) or k.shape[2] != head_dim or ids.shape[0] != nq:
+        raise ValueError("shape mismatch between q, k, v and ids")
+    width = ids.shape[1] if width is None else int(width)
+    scale = 1.0 / head_dim ** 0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((nq, n_heads, head_dim), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((nq, n_heads), dtype=torch.float32, device=q.device)
+    _dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse")
+    if not out.is_contiguous() or not lse.is_contiguous():
+        raise ValueError("out and lse must be contiguous")
+    need = attention_workspace_bytes(nq, n_heads, kv_heads, width)
+    if ws is None and need > 0:
+        ws = workspace(need, q.device)
+    _check(lib().qsa_selection_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(ids), ids.stride(0), _ptr(out),
+                                         _ptr(lse), nq, n_heads, kv_heads, head_dim, n_cells, width, scale,
+                                         _ptr(ws) if ws is not None else None,
+                                         ws.numel() * ws.element_size() if ws is not None else 0,
+                                         _stream(stream)), "qsa_selection_attention")
+    return out, lse
 
 
 def _topk_outputs(nq, width, device, ids, counts):

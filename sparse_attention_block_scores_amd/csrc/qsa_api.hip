@@ -1,6 +1,7 @@
 // qsa_api.hip - the C ABI of libqsa.so: argument checks, the top-k dispatch
 // plan, workspace layout and the launches. Nothing here allocates device
 // memory, synchronises or prints.
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -401,6 +402,59 @@ qsa_status qsa_select_cells(const float *q, const float *k, const float *w, int3
 {
     return select_call(q, k, w, n_heads, head_dim, scores, ld_scores, nq, n_blocks, block_size, width, call,
                        nullptr, visible_cells, cell_ids, counts, workspace, workspace_bytes, stream, opt);
+}
+
+size_t qsa_selection_attention_workspace_bytes(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width)
+{
+    AttnPlan plan;
+    if (!make_attn_plan(nq, n_heads, kv_heads, width, plan))
+        return 0;
+    return plan.bytes;
+}
+
+qsa_status qsa_selection_attention(const void *q, const void *k, const void *v, const int32_t *ids,
+                                   int64_t ld_ids, float *out, float *lse, int32_t nq, int32_t n_heads,
+                                   int32_t kv_heads, int32_t head_dim, int32_t n_cells, int32_t width,
+                                   float scale, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (nq < 0 || n_heads < 1 || kv_heads < 1 || n_heads % kv_heads != 0 || n_cells < 1 || width < 1 ||
+        ld_ids < width || !isfinite(scale))
+        return QSA_EINVAL;
+    if (head_dim != 128)
+        return QSA_EUNSUPPORTED;
+    AttnPlan plan;
+    if (!make_attn_plan(nq, n_heads, kv_heads, width, plan))
+        return QSA_EINVAL;
+    if (nq == 0)
+        return QSA_OK;
+    if (!q || !k || !v || !ids || !out)
+        return QSA_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(ids, 4) ||
+        !aligned(lse, 4))
+        return QSA_EINVAL;
+    if (plan.bytes > 0 && (!workspace || !aligned(workspace, kAlign) || workspace_bytes < plan.bytes))
+        return QSA_EWORKSPACE;
+    AttnArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.ids = ids;
+    a.ld_ids = ld_ids;
+    a.out = out;
+    a.lse = lse;
+    a.part_ml = plan.bytes ? at<float2>(workspace, plan.ml_offset) : nullptr;
+    a.part_o = plan.bytes ? at<float>(workspace, plan.o_offset) : nullptr;
+    a.nq = nq;
+    a.n_heads = n_heads;
+    a.kv_heads = kv_heads;
+    a.group = n_heads / kv_heads;
+    a.hblocks = plan.hblocks;
+    a.n_cells = n_cells;
+    a.width = width;
+    a.steps_per_wave = plan.steps_per_wave;
+    a.n_chunks = plan.n_chunks;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    return launch_attention(a, plan, (hipStream_t)stream) == hipSuccess ? QSA_OK : QSA_EHIP;
 }
 
 } // extern "C"

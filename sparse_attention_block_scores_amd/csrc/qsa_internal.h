@@ -122,4 +122,37 @@ struct FusedArgs {
 bool fused_select_fits(int32_t nq, int32_t heads, int32_t n_blocks);
 hipError_t launch_fused_select(FusedArgs a, hipStream_t s);
 
+// Attention of every query head over its query's selected cells.
+constexpr int kAttnWaves = 4;             // waves per workgroup
+constexpr int kAttnStepCells = 32;        // cells per wave step
+constexpr int kAttnHeadBlock = 16;        // query heads per workgroup (one matrix-core column each)
+constexpr int kAttnTargetGroups = 1024;   // workgroups the chunking aims for
+
+struct AttnPlan {
+    int32_t hblocks;         // blocks of up to 16 heads per key/value head
+    int32_t steps_per_wave;  // 32-cell steps each wave takes
+    int32_t n_chunks;        // chunks of the id list per (query, kv head, head block)
+    int64_t units;           // nq * kv_heads * hblocks
+    size_t ml_offset;        // workspace: (max, sum) per partial, float2
+    size_t o_offset;         // workspace: 128 floats per partial
+    size_t bytes;            // 0 when one chunk covers the list
+};
+
+struct AttnArgs {
+    const uint16_t *q;       // [nq][n_heads][128] bfloat16
+    const uint16_t *k;       // [n_cells][kv_heads][128] bfloat16
+    const uint16_t *v;       // [n_cells][kv_heads][128] bfloat16
+    const int32_t *ids;      // [nq][ld_ids]
+    int64_t ld_ids;
+    float *out;              // [nq][n_heads][128]
+    float *lse;              // [nq][n_heads] or null
+    float2 *part_ml;
+    float *part_o;
+    int32_t nq, n_heads, kv_heads, group, hblocks, n_cells, width, steps_per_wave, n_chunks;
+    float scale_log2;        // softmax scale times log2(e)
+};
+
+bool make_attn_plan(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width, AttnPlan &plan);
+hipError_t launch_attention(const AttnArgs &a, const AttnPlan &plan, hipStream_t s);
+
 } // namespace qsa

@@ -170,3 +170,49 @@ def test_scores_empty_is_a_no_op():
 def test_plan_struct_size_matches_header():
     assert ctypes.sizeof(B.Plan) == 12 * 4 + 8
     assert ctypes.sizeof(B.Options) == 8 * 4
+
+
+def _attn(L, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ids=FAKE, ld=2048, out=FAKE, lse=FAKE, nq=16, h=16, kvh=1, d=128,
+             cells=262144, width=2048, scale=0.0883883, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    return L.qsa_selection_attention(a["q"], a["k"], a["v"], a["ids"], a["ld"], a["out"], a["lse"], a["nq"],
+                                     a["h"], a["kvh"], a["d"], a["cells"], a["width"], a["scale"], a["ws"],
+                                     a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d=64), B.QSA_EUNSUPPORTED),
+    (dict(h=16, kvh=3), B.QSA_EINVAL),       # heads must split evenly over key/value heads
+    (dict(kvh=0), B.QSA_EINVAL),
+    (dict(ld=2047), B.QSA_EINVAL),
+    (dict(width=0), B.QSA_EINVAL),
+    (dict(cells=0), B.QSA_EINVAL),
+    (dict(nq=-1), B.QSA_EINVAL),
+    (dict(scale=float("nan")), B.QSA_EINVAL),
+    (dict(scale=float("inf")), B.QSA_EINVAL),
+    (dict(k=FAKE + 8), B.QSA_EINVAL),        # rows are read 16 bytes at a time
+    (dict(out=FAKE + 4), B.QSA_EINVAL),
+    (dict(ids=FAKE + 2), B.QSA_EINVAL),
+    (dict(v=None), B.QSA_EINVAL),
+    (dict(ws=None), B.QSA_EWORKSPACE),
+    (dict(wsb=1024), B.QSA_EWORKSPACE),
+    (dict(ws=FAKE + 64), B.QSA_EWORKSPACE),
+])
+def test_attention_argument_errors(over, status):
+    assert _attn(qsa.lib(), **over) == status
+
+
+def test_attention_zero_queries_is_a_no_op():
+    assert _attn(qsa.lib(), nq=0) == B.QSA_OK
+
+
+def test_attention_workspace_sizes():
+    # 1,024 units (query, key/value head, head block) already fill the chip:
+    # one chunk each, nothing to keep.
+    assert qsa.attention_workspace_bytes(1024, 16, 1, 256) == 0
+    # 16 queries x 2,048 cells: 16 chunks of 128 cells, a (max, sum) pair and
+    # 128 floats per partial and head.
+    parts = 16 * 16 * 16
+    assert qsa.attention_workspace_bytes(16, 16, 1, 2048) == (parts * 8 + 255) // 256 * 256 + parts * 512
+    assert qsa.attention_workspace_bytes(16, 16, 3, 2048) == 0  # invalid grouping

@@ -1,0 +1,190 @@
+"""GPU attention over the selected cells (qsa_selection_attention) against the
+FP64 oracle on the same bfloat16 inputs (iree-org/wave issue #1257 "NSA: LDS
+optimization for block-gather in selection attention", section Problem).
+
+Tolerance, from the arithmetic: the logits are FP32 sums of exact bfloat16
+products, the softmax weights are split into a bfloat16 head and tail (2^-17
+relative) for the matrix cores, and outputs and sums accumulate in FP32.
+Together that is a few 1e-5 of T = sum_c p_c |v_c| / sum_c p_c, the oracle's
+output for |v|. The tests ask |gpu - oracle| <= 1e-4 T per output and
+|lse error| <= 1e-4 max(1, |lse|); leaving one cell out of the sum moves an
+output by about T / width, well past that for every width tested."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_block_scores_amd as qsa
+import synth
+from qsa_testutil import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-4
+
+
+def bf16_dev(bits):
+    return to_dev(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+
+
+def gpu_attention(qb, kb, vb, ids, scale, width=None):
+    out, lse = qsa.selection_attention(bf16_dev(qb), bf16_dev(kb), bf16_dev(vb), to_dev(ids),
+                                       width=width, scale=scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def check(qb, kb, vb, ids, scale, label, width=None):
+    width = ids.shape[1] if width is None else width
+    q, k, v = synth.bf16_values(qb), synth.bf16_values(kb), synth.bf16_values(vb)
+    listed = np.ascontiguousarray(ids[:, :width])
+    ref, ref_lse = oracle.selection_attention(q, k, v, listed, scale)
+    scale_t, _ = oracle.selection_attention(q, k, np.abs(v), listed, scale)
+    say(f"attention {label}")
+    out, lse = gpu_attention(qb, kb, vb, ids, scale, width)
+    err = np.abs(out.astype(np.float64) - ref)
+    tol = RTOL * scale_t
+    if not (err <= tol).all():
+        i = np.unravel_index(np.argmax(err - tol), err.shape)
+        raise AssertionError(f"{label}: out{list(i)} gpu {out[i]} oracle {ref[i]} (tolerance {tol[i]:.3g}); "
+                             f"{int((err > tol).sum())} outputs off")
+    empty = np.isneginf(ref_lse)
+    assert (np.isneginf(lse) == empty).all(), f"{label}: empty selections differ"
+    assert (out[empty] == 0).all(), f"{label}: an empty selection gave a nonzero output"
+    le = np.abs(lse[~empty].astype(np.float64) - ref_lse[~empty])
+    lt = RTOL * np.maximum(1.0, np.abs(ref_lse[~empty]))
+    assert (le <= lt).all(), f"{label}: lse off by up to {np.max(le / lt):.3f} x tolerance"
+
+
+def make_ids(tag, variant, nq, n_cells, width, ld):
+    """Id lists of several structures; columns past the width hold valid ids,
+    which must be ignored."""
+    ids = np.full((nq, ld), 1, np.int32)
+    nb = max(1, n_cells // 4)
+    if variant == "random":
+        ids[:, :width] = synth.integers(tag + "/c", nq * width, 0, n_cells - 1).reshape(nq, width)
+        return ids
+    sel = synth.random_selection(tag + "/sel", nq, nb, 4, width)
+    ids[:, :width] = sel
+    if variant == "ragged":      # ragged counts, a partial last block, one empty query
+        counts = synth.integers(tag + "/n", nq, 0, width)
+        for iq in range(nq):
+            ids[iq, counts[iq]:width] = -1
+        ids[nq - 1, :width] = -1
+    elif variant == "foreign":   # ids outside [0, n_cells) select nothing
+        pos = synth.integers(tag + "/p", nq * 4, 0, width - 1)
+        val = synth.integers(tag + "/v", nq * 4, n_cells, n_cells + 1000)
+        for j in range(nq * 4):
+            ids[j % nq, pos[j]] = val[j] if j % 2 else -5 - j
+    elif variant == "dups":      # a cell listed twice counts twice
+        ids[:, 1] = ids[:, 0]
+    return ids
+
+
+CASES = [
+    # tag, nq, heads, kv_heads, n_cells, width, ld, variant
+    ("one", 1, 1, 1, 64, 1, 1, "random"),
+    ("tiny", 1, 16, 1, 8, 3, 3, "random"),
+    ("ragged", 2, 8, 1, 1000, 100, 103, "ragged"),
+    ("group20", 5, 20, 1, 3000, 300, 300, "blocks"),
+    ("kv3", 4, 6, 3, 500, 77, 80, "ragged"),
+    ("h64", 2, 64, 4, 2048, 520, 520, "blocks"),
+    ("mha", 3, 16, 16, 300, 64, 64, "blocks"),
+    ("g33", 7, 33, 1, 999, 2047, 2050, "ragged"),
+    ("foreign", 2, 2, 2, 50, 31, 31, "foreign"),
+    ("dups", 2, 2, 1, 50, 33, 40, "dups"),
+    ("long", 3, 16, 2, 20000, 4100, 4100, "blocks"),
+]
+
+
+@pytest.mark.parametrize("tag,nq,heads,kvh,n_cells,width,ld,variant", CASES, ids=[c[0] for c in CASES])
+def test_shapes(tag, nq, heads, kvh, n_cells, width, ld, variant):
+    t = f"gpu/attn/{tag}"
+    qb = synth.bf16_bits(synth.normal(t + "/q", (nq, heads, 128)))
+    kb = synth.bf16_bits(synth.normal(t + "/k", (n_cells, kvh, 128)))
+    vb = synth.bf16_bits(synth.normal(t + "/v", (n_cells, kvh, 128)))
+    ids = make_ids(t, variant, nq, n_cells, width, ld)
+    check(qb, kb, vb, ids, 1.0 / np.sqrt(128.0), f"{tag} nq={nq} h={heads}/{kvh} cells={n_cells} w={width}",
+          width=width)
+
+
+def test_scale_and_peaked_softmax():
+    """A large scale makes a few cells dominate: the running max is replaced
+    many times and most weights underflow to 0."""
+    qb = synth.bf16_bits(synth.normal("gpu/attn/peak/q", (4, 16, 128)))
+    kb = synth.bf16_bits(synth.normal("gpu/attn/peak/k", (5000, 1, 128)))
+    vb = synth.bf16_bits(synth.normal("gpu/attn/peak/v", (5000, 1, 128)))
+    ids = make_ids("gpu/attn/peak", "blocks", 4, 5000, 1024, 1024)
+    check(qb, kb, vb, ids, 0.7, "peaked (scale 0.7)")
+
+
+def test_single_cell_is_exact():
+    """One listed cell: its weight is exactly 1, so out is its value row."""
+    nq, heads, kvh, n_cells = 6, 16, 2, 300
+    qb = synth.bf16_bits(synth.normal("gpu/attn/single/q", (nq, heads, 128)))
+    kb = synth.bf16_bits(synth.normal("gpu/attn/single/k", (n_cells, kvh, 128)))
+    vb = synth.bf16_bits(synth.normal("gpu/attn/single/v", (n_cells, kvh, 128)))
+    ids = np.full((nq, 70), -1, np.int32)
+    cells = synth.integers("gpu/attn/single/c", nq, 0, n_cells - 1)
+    pos = synth.integers("gpu/attn/single/p", nq, 0, 69)
+    ids[np.arange(nq), pos] = cells
+    say("attention single cell")
+    out, _ = gpu_attention(qb, kb, vb, ids, 0.1)
+    v = synth.bf16_values(vb)
+    for iq in range(nq):
+        for h in range(heads):
+            assert np.array_equal(out[iq, h], v[cells[iq], h // (heads // kvh)]), (iq, h)
+
+
+@pytest.mark.parametrize("make", [synth.a1, synth.a3, synth.a5], ids=["A1", "A3", "A5"])
+def test_workloads_full(make):
+    """The decode and prompt workloads in full, in the launch configuration
+    the benchmark times."""
+    wl = make()
+    qb, kb, vb = wl.tensors()
+    check(qb, kb, vb, wl.selection(), wl.scale(), wl.name)
+
+
+def test_topk_ids_feed_attention():
+    """The top-k's id buffer goes into the attention as it is: the GPU's ids
+    from the oracle's scores equal the oracle's ids, and the attention over
+    them matches the oracle's attention over its own ids."""
+    sel = synth.c1()
+    q, k, w = sel.tensors()
+    scores = oracle.block_scores(q, k, w).astype(np.float32)
+    ref_ids, _ = oracle.topk_sort(scores, sel.n_blocks, sel.block_size, sel.width)
+    say("attention fed by the top-k")
+    ids_d, _ = qsa.block_topk(to_dev(scores), sel.n_blocks, sel.block_size, sel.width, "decode")
+    torch.cuda.synchronize()
+    assert np.array_equal(ids_d.cpu().numpy(), ref_ids)
+    att = synth.a1()
+    assert att.n_cells == sel.n_blocks * sel.block_size and att.nq == sel.nq and att.width == sel.width
+    qb, kb, vb = att.tensors()
+    out, lse = qsa.selection_attention(bf16_dev(qb), bf16_dev(kb), bf16_dev(vb), ids_d, scale=att.scale())
+    torch.cuda.synchronize()
+    qf, kf, vf = synth.bf16_values(qb), synth.bf16_values(kb), synth.bf16_values(vb)
+    ref, ref_lse = oracle.selection_attention(qf, kf, vf, ref_ids, att.scale())
+    scale_t, _ = oracle.selection_attention(qf, kf, np.abs(vf), ref_ids, att.scale())
+    assert (np.abs(out.cpu().numpy() - ref) <= RTOL * scale_t).all()
+    assert (np.abs(lse.cpu().numpy() - ref_lse) <= RTOL * np.maximum(1.0, np.abs(ref_lse))).all()
+
+
+def test_repeat_calls_reuse_the_workspace():
+    """Two calls on one workspace, the second smaller: partials of the first
+    never leak into the second."""
+    wl = synth.a3()
+    qb, kb, vb = wl.tensors()
+    ids = wl.selection()
+    need = qsa.attention_workspace_bytes(wl.nq, wl.heads, wl.kv_heads, wl.width)
+    assert need > 0
+    ws = qsa.workspace(need)
+    q, k, v = bf16_dev(qb), bf16_dev(kb), bf16_dev(vb)
+    say("attention workspace reuse")
+    qsa.selection_attention(q, k, v, to_dev(ids), scale=wl.scale(), ws=ws)
+    ids2 = np.ascontiguousarray(ids[:5])
+    out, lse = qsa.selection_attention(q[:5].contiguous(), k, v, to_dev(ids2), scale=wl.scale(), ws=ws)
+    torch.cuda.synchronize()
+    qf, kf, vf = synth.bf16_values(qb[:5]), synth.bf16_values(kb), synth.bf16_values(vb)
+    ref, _ = oracle.selection_attention(qf, kf, vf, ids2, wl.scale())
+    scale_t, _ = oracle.selection_attention(qf, kf, np.abs(vf), ids2, wl.scale())
+    assert (np.abs(out.cpu().numpy() - ref) <= RTOL * scale_t).all()
