@@ -251,7 +251,9 @@ qsa_status qsa_select_cells(const float *q, const float *k, const float *w,
  *   kv_heads; n_cells, width >= 1; ld_ids >= width; scale finite.
  *   Products of bfloat16 values with FP32 accumulation, FP32 softmax.
  *   workspace: qsa_selection_attention_workspace_bytes() bytes, 256-byte
- *   aligned (may be NULL when that is 0); per call, contents need no set-up.
+ *   aligned (may be NULL when that is 0): per-chunk partial results, written
+ *   and read within the call; its contents need no set-up. Calls that may
+ *   overlap need separate workspaces.
  */
 size_t qsa_selection_attention_workspace_bytes(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width);
 qsa_status qsa_selection_attention(const void *q, const void *k, const void *v,

@@ -7,10 +7,21 @@
 // over the listed cells c, and lse[q][h] = log sum_c exp(scale * q . k).
 //
 // Work unit: one query, one key/value head, a block of up to 16 of its query
-// heads and a chunk of the query's id list. A workgroup of four waves takes a
-// unit; each wave walks 32-cell steps of the chunk with its own running
-// softmax (max, sum, output) and the four are merged in LDS at the end.
-// Several chunks per unit are merged by attn_combine_kernel.
+// heads and a chunk of the query's id list. A workgroup of eight waves (one
+// per CU at two waves per SIMD) takes a unit; each wave walks 32-cell steps of
+// the chunk with its own running softmax (max, sum, output) and the eight are
+// merged in LDS at the end. When a unit's list is split into several chunks,
+// each chunk's workgroup leaves its merged partial in the workspace and
+// attn_merge_kernel combines them. (A last-arriving-workgroup hand-off in the
+// same launch was measured slower on MI355X: its write-through stores, the
+// ticket and the device-coherent loads cost more round trips than the kernel
+// boundary.)
+//
+// The gather is software-pipelined: a wave's id loads run two steps ahead and
+// its key/value row loads one step ahead (a second register set), so every
+// wave keeps a step's rows in flight while it computes the previous one.
+// Loads past the wave's range are issued too, masked to cell 0 (cache hits),
+// so that no load sits under a branch and the compiler's waits stay exact.
 //
 // Matrix cores (v_mfma_f32_16x16x32_bf16, FP32 accumulation):
 //  * S^T[16 cells x 16 heads] = K[16 cells x 128] . Q^T[128 x 16 heads] in four
@@ -46,6 +57,7 @@ constexpr int kThreads = 64 * kAttnWaves;
 constexpr int kVtPitch = 18;
 constexpr int kVtWords = 128 * kVtPitch + 4 * 16;
 constexpr int kOPitch = 132;  // floats per head row of the merge buffer
+constexpr float kRescale = 8.f;  // log2 headroom of the running softmax reference
 
 __device__ __forceinline__ int vt_index(int row, int pair) { return row * kVtPitch + (row >> 5) * 16 + pair; }
 
@@ -67,16 +79,148 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// A listed id selects a cell when it lies in [0, n_cells); position p of the
-// list counts when p < width.
-__device__ __forceinline__ int cell_at(const int32_t *row, int p, int width, int n_cells, bool &ok)
+// The ids of one step: this lane's positions c0+n and c0+16+n (key rows, the
+// two 16-cell halves) and c0+2n, c0+2n+1 (the value rows it transposes).
+struct StepIds {
+    int a, b, v0, v1;
+    int c0;
+};
+
+// One step's gathered rows and the validity of its 32 cells (bit c).
+struct StepRows {
+    uint4 ka[4], kb[4], v0[4], v1[4];
+    uint64_t ma, mb;
+};
+
+__device__ __forceinline__ StepIds load_ids(const int32_t *row, int c0, int width, int n)
 {
-    const int id = row[min(p, width - 1)];
-    ok = p < width && (unsigned)id < (unsigned)n_cells;
-    return ok ? id : 0;
+    const int last = width - 1;
+    StepIds s;
+    s.c0 = c0;
+    s.a = row[min(c0 + n, last)];
+    s.b = row[min(c0 + 16 + n, last)];
+    s.v0 = row[min(c0 + 2 * n, last)];
+    s.v1 = row[min(c0 + 2 * n + 1, last)];
+    return s;
 }
 
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
+// Positions at or past `limit` and ids outside [0, n_cells) select nothing;
+// their rows are read from cell 0.
+__device__ __forceinline__ void load_rows(const StepIds &s, const AttnArgs &a, int limit, int64_t kv_row,
+                                          int64_t head_off, int n, StepRows &r)
+{
+    const bool va = s.c0 + n < limit && (unsigned)s.a < (unsigned)a.n_cells;
+    const bool vb = s.c0 + 16 + n < limit && (unsigned)s.b < (unsigned)a.n_cells;
+    const bool w0 = s.c0 + 2 * n < limit && (unsigned)s.v0 < (unsigned)a.n_cells;
+    const bool w1 = s.c0 + 2 * n + 1 < limit && (unsigned)s.v1 < (unsigned)a.n_cells;
+    r.ma = __ballot(va);
+    r.mb = __ballot(vb);
+    // Row offsets in elements: a non-negative 31-bit id times the row length.
+    const uint64_t len = (uint32_t)kv_row;
+    const uint4 *kap = reinterpret_cast<const uint4 *>(a.k + (uint64_t)(uint32_t)(va ? s.a : 0) * len + head_off);
+    const uint4 *kbp = reinterpret_cast<const uint4 *>(a.k + (uint64_t)(uint32_t)(vb ? s.b : 0) * len + head_off);
+    const uint4 *v0p = reinterpret_cast<const uint4 *>(a.v + (uint64_t)(uint32_t)(w0 ? s.v0 : 0) * len + head_off);
+    const uint4 *v1p = reinterpret_cast<const uint4 *>(a.v + (uint64_t)(uint32_t)(w1 ? s.v1 : 0) * len + head_off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r.ka[i] = kap[i];
+        r.kb[i] = kbp[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r.v0[i] = v0p[i];
+        r.v1[i] = v1p[i];
+    }
+}
+
+// One step: logits, the online softmax update, and the weighted value sum.
+__device__ __forceinline__ void attend(const StepRows &r, const bf16x8 (&qb)[4], float scale_log2, int n, int lg,
+                                       uint32_t *vt, float &m, float &l, f32x4 (&o)[8])
+{
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        sa = mfma(as_bf16x8(r.ka[s]), qb[s], sa);
+        sb = mfma(as_bf16x8(r.kb[s]), qb[s], sb);
+    }
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = ((r.ma >> (4 * lg + i)) & 1) ? sa[i] * scale_log2 : -INFINITY;
+        x[4 + i] = ((r.mb >> (4 * lg + i)) & 1) ? sb[i] * scale_log2 : -INFINITY;
+    }
+    float smax = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+        smax = fmaxf(smax, x[i]);
+    smax = fmaxf(smax, __shfl_xor(smax, 16));
+    smax = fmaxf(smax, __shfl_xor(smax, 32));
+    // The running sums are kept relative to a reference m that moves only when
+    // a head's max passes it by more than kRescale (then every lane rebases,
+    // a wave-uniform branch): weights stay below 2^kRescale, and any
+    // reference gives the same ratios.
+    if (__ballot(smax > m + kRescale)) {
+        const float mnew = fmaxf(m, smax);
+        const float alpha = mnew == m ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+        l *= alpha;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            o[t] *= alpha;
+        m = mnew;
+    }
+    const float mref = m == -INFINITY ? 0.f : m;  // a head with no cell yet has only -inf logits
+    float psum = 0.f;
+    bf16x8 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float p = __builtin_amdgcn_exp2f(x[i] - mref);
+        psum += p;
+        const __bf16 hi = (__bf16)p;
+        ph[i] = hi;
+        pl[i] = (__bf16)(p - (float)hi);
+    }
+    l += psum;
+
+    // V^T into LDS: this lane holds cells 2n and 2n+1, dims 32lg .. 32lg+31;
+    // one byte permutation packs a dim's two cells into a dword.
+    {
+        const uint32_t *w0 = reinterpret_cast<const uint32_t *>(r.v0);
+        const uint32_t *w1 = reinterpret_cast<const uint32_t *>(r.v1);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = 32 * lg + 2 * e;
+            vt[vt_index(row, n)] = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
+            vt[vt_index(row + 1, n)] = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
+        }
+    }
+    // The wave reads what its own lanes wrote (LDS keeps a wave's order).
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int row = 16 * t + n;
+        const uint2 lo = *reinterpret_cast<const uint2 *>(&vt[vt_index(row, 2 * lg)]);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(&vt[vt_index(row, 8 + 2 * lg)]);
+        const bf16x8 av = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[t] = mfma(av, ph, o[t]);
+        o[t] = mfma(av, pl, o[t]);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Normalised output (4 dims) and, when asked, the log-sum-exp in natural
+// log units; a head with no selected cell gets 0 and -inf.
+__device__ __forceinline__ void finish(f32x4 acc, float sum, float ref, float *dst, float *dst_lse)
+{
+    *reinterpret_cast<float4 *>(dst) = sum > 0.f ? make_float4(acc[0] / sum, acc[1] / sum, acc[2] / sum, acc[3] / sum)
+                                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (dst_lse)
+        *dst_lse = sum > 0.f ? (ref + log2f(sum)) * 0.69314718055994531f : -INFINITY;
+}
+
+// Two waves per SIMD: at most 256 VGPRs, room for two steps of rows.
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a)
 {
     __shared__ AttnLds sm;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -91,21 +235,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
     const int g = u % a.kv_heads;
     const int iq = u / a.kv_heads;
 
-    // This lane's matrix-core column: query head hb*16 + n of the group.
-    const bool head_ok = hb * kAttnHeadBlock + n < a.group;
-    const int head = g * a.group + (head_ok ? hb * kAttnHeadBlock + n : 0);
-    bf16x8 qb[4];
-    {
-        const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((int64_t)iq * a.n_heads + head) * 128 + 32 * lg);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            uint4 x = qp[s];
-            if (!head_ok)
-                x = make_uint4(0, 0, 0, 0);
-            qb[s] = as_bf16x8(x);
-        }
-    }
-
     float m = -INFINITY, l = 0.f;
     f32x4 o[8];
 #pragma unroll
@@ -115,104 +244,44 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
     uint32_t *vt = sm.vt[wv];
     const int32_t *idrow = a.ids + (int64_t)iq * a.ld_ids;
     const int64_t kv_row = (int64_t)a.kv_heads * 128;
-    const int step0 = (chunk * kAttnWaves + wv) * a.steps_per_wave;
-    for (int j = 0; j < a.steps_per_wave; ++j) {
-        const int c0 = (step0 + j) * kAttnStepCells;
-        if (c0 >= a.width)
-            break;  // wave-uniform
-        bool va, vb, v0ok, v1ok;
-        const int ida = cell_at(idrow, c0 + n, a.width, a.n_cells, va);
-        const int idb = cell_at(idrow, c0 + 16 + n, a.width, a.n_cells, vb);
-        const int iv0 = cell_at(idrow, c0 + 2 * n, a.width, a.n_cells, v0ok);
-        const int iv1 = cell_at(idrow, c0 + 2 * n + 1, a.width, a.n_cells, v1ok);
-        const int64_t head_off = (int64_t)g * 128 + 32 * lg;
-        const uint4 *kap = reinterpret_cast<const uint4 *>(a.k + ida * kv_row + head_off);
-        const uint4 *kbp = reinterpret_cast<const uint4 *>(a.k + idb * kv_row + head_off);
-        const uint4 *v0p = reinterpret_cast<const uint4 *>(a.v + iv0 * kv_row + head_off);
-        const uint4 *v1p = reinterpret_cast<const uint4 *>(a.v + iv1 * kv_row + head_off);
-        uint4 ka[4], kb[4], v0[4], v1[4];
+    const int64_t head_off = (int64_t)g * 128 + 32 * lg;
+    const int first = (chunk * kAttnWaves + wv) * a.steps_per_wave * kAttnStepCells;
+    // Steps of this wave that hold listed positions (wave-uniform).
+    const int steps = min(a.steps_per_wave, max(0, (a.width - first + kAttnStepCells - 1) / kAttnStepCells));
+    const int limit = min(a.width, first + steps * kAttnStepCells);
+    if (steps > 0) {
+        // The id loads start the dependent chain; the query rows load beside them.
+        StepIds i0 = load_ids(idrow, first, a.width, n);
+        StepIds i1 = load_ids(idrow, first + kAttnStepCells, a.width, n);
+        // This lane's matrix-core column: query head hb*16 + n of the group
+        // (a padding column reads head 0 of the group and is zeroed).
+        const bool head_ok = hb * kAttnHeadBlock + n < a.group;
+        const int head = g * a.group + (head_ok ? hb * kAttnHeadBlock + n : 0);
+        const uint32_t keep = head_ok ? 0xFFFFFFFFu : 0u;
+        const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((int64_t)iq * a.n_heads + head) * 128 + 32 * lg);
+        bf16x8 qb[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            ka[s] = kap[s];
-            kb[s] = kbp[s];
+            const uint4 x = qp[s];
+            qb[s] = as_bf16x8(make_uint4(x.x & keep, x.y & keep, x.z & keep, x.w & keep));
         }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            v0[s] = v0p[s];
-            v1[s] = v1p[s];
+        StepRows r0, r1;
+        load_rows(i0, a, limit, kv_row, head_off, n, r0);
+        for (int j = 0; j < steps; j += 2) {
+            i0 = load_ids(idrow, first + (j + 2) * kAttnStepCells, a.width, n);
+            load_rows(i1, a, limit, kv_row, head_off, n, r1);
+            attend(r0, qb, a.scale_log2, n, lg, vt, m, l, o);
+            if (j + 1 >= steps)
+                break;
+            i1 = load_ids(idrow, first + (j + 3) * kAttnStepCells, a.width, n);
+            load_rows(i0, a, limit, kv_row, head_off, n, r0);
+            attend(r1, qb, a.scale_log2, n, lg, vt, m, l, o);
         }
-
-        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            sa = mfma(as_bf16x8(ka[s]), qb[s], sa);
-            sb = mfma(as_bf16x8(kb[s]), qb[s], sb);
-        }
-
-        // Lanes 0-15 hold cells 0-15 of each half: bit c of the ballot is the
-        // validity of cell c.
-        const uint64_t ma = __ballot(va), mb = __ballot(vb);
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[i] = ((ma >> (4 * lg + i)) & 1) ? sa[i] * a.scale_log2 : -INFINITY;
-            x[4 + i] = ((mb >> (4 * lg + i)) & 1) ? sb[i] * a.scale_log2 : -INFINITY;
-        }
-        float smax = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i)
-            smax = fmaxf(smax, x[i]);
-        smax = fmaxf(smax, __shfl_xor(smax, 16));
-        smax = fmaxf(smax, __shfl_xor(smax, 32));
-        const float mnew = fmaxf(m, smax);
-        const float mref = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = exp2f(m - mref);
-        float psum = 0.f;
-        bf16x8 ph, pl;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p = exp2f(x[i] - mref);
-            psum += p;
-            const __bf16 hi = (__bf16)p;
-            ph[i] = hi;
-            pl[i] = (__bf16)(p - (float)hi);
-        }
-        l = l * alpha + psum;
-        m = mnew;
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            o[t] *= alpha;
-
-        // V^T into LDS: this lane holds cells 2n and 2n+1, dims 32lg .. 32lg+31.
-        {
-            const uint32_t *w0 = reinterpret_cast<const uint32_t *>(v0);
-            const uint32_t *w1 = reinterpret_cast<const uint32_t *>(v1);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = 32 * lg + 2 * e;
-                vt[vt_index(row, n)] = (w0[e] & 0xFFFFu) | (w1[e] << 16);
-                vt[vt_index(row + 1, n)] = (w0[e] >> 16) | (w1[e] & 0xFFFF0000u);
-            }
-        }
-        // The wave reads what its own lanes wrote (LDS keeps a wave's order).
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int row = 16 * t + n;
-            const uint2 lo = *reinterpret_cast<const uint2 *>(&vt[vt_index(row, 2 * lg)]);
-            const uint2 hi = *reinterpret_cast<const uint2 *>(&vt[vt_index(row, 8 + 2 * lg)]);
-            const bf16x8 av = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-            o[t] = mfma(av, ph, o[t]);
-            o[t] = mfma(av, pl, o[t]);
-        }
-        __builtin_amdgcn_wave_barrier();
     }
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
 
-    // Merge the four waves.
+    // Merge the eight waves.
     __syncthreads();  // every wave is done with its V^T rows
     if (lg == 0) {
         sm.merge.m[wv][n] = m;
@@ -223,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
         *reinterpret_cast<f32x4 *>(&sm.merge.o[wv][n][16 * t + 4 * lg]) = o[t];
     __syncthreads();
 
-    const int hn = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 8;
+    const int hn = threadIdx.x >> 5, d0 = (threadIdx.x & 31) * 4;
     float mw[kAttnWaves], big = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) {
@@ -231,45 +300,33 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a)
         big = fmaxf(big, mw[w]);
     }
     const float ref = big == -INFINITY ? 0.f : big;
-    float sum = 0.f, acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        acc[e] = 0.f;
+    float sum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) {
         const float f = exp2f(mw[w] - ref);
         sum += sm.merge.l[w][hn] * f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            acc[e] += sm.merge.o[w][hn][d0 + e] * f;
+        acc += *reinterpret_cast<const f32x4 *>(&sm.merge.o[w][hn][d0]) * f;
     }
-    if (hb * kAttnHeadBlock + hn >= a.group)
-        return;
+    const bool out_ok = hb * kAttnHeadBlock + hn < a.group;
     const int head_out = g * a.group + hb * kAttnHeadBlock + hn;
+    float *dst = a.out + ((int64_t)iq * a.n_heads + head_out) * 128 + d0;
+    float *dst_lse = a.lse ? a.lse + (int64_t)iq * a.n_heads + head_out : nullptr;
     if (a.n_chunks == 1) {
-        float4 *dst = reinterpret_cast<float4 *>(a.out + ((int64_t)iq * a.n_heads + head_out) * 128 + d0);
-        if (sum > 0.f) {
-            dst[0] = make_float4(acc[0] / sum, acc[1] / sum, acc[2] / sum, acc[3] / sum);
-            dst[1] = make_float4(acc[4] / sum, acc[5] / sum, acc[6] / sum, acc[7] / sum);
-        } else {
-            dst[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-            dst[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        if (a.lse && d0 == 0)
-            a.lse[(int64_t)iq * a.n_heads + head_out] =
-                sum > 0.f ? (ref + log2f(sum)) * 0.69314718055994531f : -INFINITY;
-    } else {
-        const int64_t slot = ((int64_t)unit * a.n_chunks + chunk) * kAttnHeadBlock + hn;
-        float4 *dst = reinterpret_cast<float4 *>(a.part_o + slot * 128 + d0);
-        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-        if (d0 == 0)
-            a.part_ml[slot] = make_float2(big, sum);
+        if (out_ok)
+            finish(acc, sum, ref, dst, d0 == 0 ? dst_lse : nullptr);
+        return;
     }
+    // This chunk's partial; attn_merge_kernel combines the chunks.
+    const int64_t slot = ((int64_t)unit * a.n_chunks + chunk) * kAttnHeadBlock + hn;
+    *reinterpret_cast<f32x4 *>(a.part_o + slot * 128 + d0) = acc;
+    if (d0 == 0)
+        a.part_ml[slot] = make_float2(big, sum);
 }
 
 // One workgroup per (unit, head of the block): merges the unit's chunks.
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a)
+// Every chunk's partial is loaded before any is used, so the loads overlap.
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a)
 {
     const int hn = blockIdx.x % kAttnHeadBlock;
     const int unit = blockIdx.x / kAttnHeadBlock;
@@ -283,22 +340,31 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a)
     const int head = g * a.group + hb * kAttnHeadBlock + hn;
     const int d = threadIdx.x;
     const int64_t slot0 = (int64_t)unit * a.n_chunks * kAttnHeadBlock + hn;
+    float2 ml[kAttnMaxChunks];
+    float po[kAttnMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kAttnMaxChunks; ++c) {
+        const int64_t sl = slot0 + (int64_t)min(c, a.n_chunks - 1) * kAttnHeadBlock;
+        ml[c] = a.part_ml[sl];
+        po[c] = a.part_o[sl * 128 + d];
+    }
     float big = -INFINITY;
-    for (int c = 0; c < a.n_chunks; ++c)
-        big = fmaxf(big, a.part_ml[slot0 + (int64_t)c * kAttnHeadBlock].x);
+#pragma unroll
+    for (int c = 0; c < kAttnMaxChunks; ++c)
+        big = c < a.n_chunks ? fmaxf(big, ml[c].x) : big;
     const float ref = big == -INFINITY ? 0.f : big;
     float sum = 0.f, acc = 0.f;
-    for (int c = 0; c < a.n_chunks; ++c) {
-        const int64_t slot = slot0 + (int64_t)c * kAttnHeadBlock;
-        const float2 ml = a.part_ml[slot];
-        const float f = exp2f(ml.x - ref);
-        sum += ml.y * f;
-        acc += a.part_o[slot * 128 + d] * f;
+#pragma unroll
+    for (int c = 0; c < kAttnMaxChunks; ++c) {
+        const float f = c < a.n_chunks ? exp2f(ml[c].x - ref) : 0.f;
+        sum += ml[c].y * f;
+        acc += po[c] * f;
     }
     a.out[((int64_t)iq * a.n_heads + head) * 128 + d] = sum > 0.f ? acc / sum : 0.f;
     if (a.lse && d == 0)
         a.lse[(int64_t)iq * a.n_heads + head] = sum > 0.f ? (ref + log2f(sum)) * 0.69314718055994531f : -INFINITY;
 }
+
 
 } // namespace
 
@@ -314,6 +380,7 @@ bool make_attn_plan(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width
     const int32_t max_chunks = (steps + kAttnWaves - 1) / kAttnWaves;
     int64_t chunks = p.units > 0 ? (kAttnTargetGroups + p.units - 1) / p.units : 1;
     chunks = chunks < 1 ? 1 : (chunks > max_chunks ? max_chunks : chunks);
+    chunks = chunks > kAttnMaxChunks ? kAttnMaxChunks : chunks;  // the merge loads every partial at once
     p.steps_per_wave = (int32_t)((steps + kAttnWaves * chunks - 1) / (kAttnWaves * chunks));
     p.n_chunks = (steps + kAttnWaves * p.steps_per_wave - 1) / (kAttnWaves * p.steps_per_wave);
     if (p.units * p.n_chunks * kAttnHeadBlock > 0x7fffffffLL)
@@ -329,12 +396,11 @@ bool make_attn_plan(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width
 
 hipError_t launch_attention(const AttnArgs &a, const AttnPlan &p, hipStream_t s)
 {
-    const int64_t groups = p.units * p.n_chunks;
-    hipLaunchKernelGGL(attn_kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_kernel, dim3((unsigned)(p.units * p.n_chunks)), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_chunks == 1)
         return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(p.units * kAttnHeadBlock)), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(p.units * kAttnHeadBlock)), dim3(128), 0, s, a);
     return hipGetLastError();
 }
 

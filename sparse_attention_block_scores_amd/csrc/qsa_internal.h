@@ -123,10 +123,11 @@ bool fused_select_fits(int32_t nq, int32_t heads, int32_t n_blocks);
 hipError_t launch_fused_select(FusedArgs a, hipStream_t s);
 
 // Attention of every query head over its query's selected cells.
-constexpr int kAttnWaves = 4;             // waves per workgroup
+constexpr int kAttnWaves = 8;             // waves per workgroup (one workgroup per CU)
 constexpr int kAttnStepCells = 32;        // cells per wave step
 constexpr int kAttnHeadBlock = 16;        // query heads per workgroup (one matrix-core column each)
-constexpr int kAttnTargetGroups = 1024;   // workgroups the chunking aims for
+constexpr int kAttnTargetGroups = 256;    // workgroups the chunking aims for (one per CU)
+constexpr int kAttnMaxChunks = 16;        // chunks of one unit's list at most
 
 struct AttnPlan {
     int32_t hblocks;         // blocks of up to 16 heads per key/value head

@@ -208,11 +208,11 @@ def test_attention_zero_queries_is_a_no_op():
 
 
 def test_attention_workspace_sizes():
-    # 1,024 units (query, key/value head, head block) already fill the chip:
+    # 256 units (query, key/value head, head block) already fill the chip:
     # one chunk each, nothing to keep.
-    assert qsa.attention_workspace_bytes(1024, 16, 1, 256) == 0
-    # 16 queries x 2,048 cells: 16 chunks of 128 cells, a (max, sum) pair and
-    # 128 floats per partial and head.
-    parts = 16 * 16 * 16
+    assert qsa.attention_workspace_bytes(256, 16, 1, 2048) == 0
+    # 16 queries x 2,048 cells: 8 chunks of 256 cells (eight waves of one
+    # 32-cell step); a (max, sum) pair and 128 floats per partial and head.
+    parts = 16 * 8 * 16
     assert qsa.attention_workspace_bytes(16, 16, 1, 2048) == (parts * 8 + 255) // 256 * 256 + parts * 512
     assert qsa.attention_workspace_bytes(16, 16, 3, 2048) == 0  # invalid grouping

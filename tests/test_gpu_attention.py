@@ -66,7 +66,9 @@ def make_ids(tag, variant, nq, n_cells, width, ld):
         return ids
     sel = synth.random_selection(tag + "/sel", nq, nb, 4, width)
     ids[:, :width] = sel
-    if variant == "ragged":      # ragged counts, a partial last block, one empty query
+    if variant == "ragged1":     # one query: a partial last block, no empty row
+        ids[0, width - 7:width] = -1
+    elif variant == "ragged":    # ragged counts, a partial last block, one empty query
         counts = synth.integers(tag + "/n", nq, 0, width)
         for iq in range(nq):
             ids[iq, counts[iq]:width] = -1
@@ -94,6 +96,7 @@ CASES = [
     ("foreign", 2, 2, 2, 50, 31, 31, "foreign"),
     ("dups", 2, 2, 1, 50, 33, 40, "dups"),
     ("long", 3, 16, 2, 20000, 4100, 4100, "blocks"),
+    ("huge", 1, 16, 1, 100000, 32768, 32768, "ragged1"),  # 16 chunks of 8 steps per wave
 ]
 
 
@@ -188,3 +191,32 @@ def test_repeat_calls_reuse_the_workspace():
     ref, _ = oracle.selection_attention(qf, kf, vf, ids2, wl.scale())
     scale_t, _ = oracle.selection_attention(qf, kf, np.abs(vf), ids2, wl.scale())
     assert (np.abs(out.cpu().numpy() - ref) <= RTOL * scale_t).all()
+
+
+def test_back_to_back_calls_on_one_workspace():
+    """Chunked calls leave partials in the workspace for the merge: five calls
+    in a row on one workspace, alternating two id lists, all match the
+    oracle."""
+    nq, heads, kvh, n_cells, width = 6, 16, 1, 40000, 2048
+    qb = synth.bf16_bits(synth.normal("gpu/attn/b2b/q", (nq, heads, 128)))
+    kb = synth.bf16_bits(synth.normal("gpu/attn/b2b/k", (n_cells, kvh, 128)))
+    vb = synth.bf16_bits(synth.normal("gpu/attn/b2b/v", (n_cells, kvh, 128)))
+    lists = [make_ids("gpu/attn/b2b/x", "blocks", nq, n_cells, width, width),
+             make_ids("gpu/attn/b2b/y", "ragged", nq, n_cells, width, width)]
+    need = qsa.attention_workspace_bytes(nq, heads, kvh, width)
+    assert need > 0
+    ws = qsa.workspace(need)
+    q, k, v = bf16_dev(qb), bf16_dev(kb), bf16_dev(vb)
+    qf, kf, vf = synth.bf16_values(qb), synth.bf16_values(kb), synth.bf16_values(vb)
+    refs = [oracle.selection_attention(qf, kf, vf, ids, 0.09) for ids in lists]
+    scales = [oracle.selection_attention(qf, kf, np.abs(vf), ids, 0.09)[0] for ids in lists]
+    say("attention five calls on one workspace")
+    for call in range(5):
+        out, lse = qsa.selection_attention(q, k, v, to_dev(lists[call % 2]), scale=0.09, ws=ws)
+        torch.cuda.synchronize()
+        ref, ref_lse = refs[call % 2]
+        assert (np.abs(out.cpu().numpy() - ref) <= RTOL * scales[call % 2]).all(), call
+        got_lse = lse.cpu().numpy()
+        fin = np.isfinite(ref_lse)
+        assert (np.isneginf(got_lse) == ~fin).all(), call
+        assert (np.abs(got_lse[fin] - ref_lse[fin]) <= RTOL * np.maximum(1.0, np.abs(ref_lse[fin]))).all(), call
