@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode / top-k-only figures")
+    ap.add_argument("--only-attention", action="store_true",
+                    help="time only the attention over the selected cells (for profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (to scale profiler byte counters)")
     return ap.parse_args()
@@ -135,7 +137,8 @@ def graph_us(torch, dev, fn, n):
 
 
 def secondary(torch, qsa, synth, dev, reps=50):
-    """Decode-call latency at each context and top-k-only prompt figures.
+    """Decode-call latency at each context, top-k-only prompt figures, the
+    BF16 scorer and the attention over the selected cells.
     Every figure is the mean over a HIP graph of back-to-back calls on
     torch's current stream (the library is capture-safe: no allocation, no
     host synchronisation, no memset nodes)."""
@@ -217,7 +220,53 @@ def secondary(torch, qsa, synth, dev, reps=50):
         bf[wlb.name] = {"us": round(us, 2), "TFLOPs": round(tf, 1), "bf16_peak_frac": round(tf / PEAK_BF16_MFMA_TFLOPS, 4)}
         del qb, kb, wb, sb
     out["bf16_scorer"] = bf
+
+    out["selection_attention"] = attention_figures(torch, qsa, synth, dev, time_us)
     return out
+
+
+def attention_figures(torch, qsa, synth, dev, time_us):
+    """Attention over the selected cells (qsa_selection_attention), decode
+    and prompt shapes; bytes are the gathered key and value rows. The prompt
+    shape is also timed over three rotated key/value copies (768 MiB), so that
+    its reads come from HBM rather than the 256 MB last-level cache."""
+    import numpy as np
+
+    cur = torch.cuda.current_stream
+    att = {}
+    for wla in (synth.a3(), synth.a5()):
+        qh, kh, vh = wla.tensors()
+        sel = wla.selection()
+
+        def bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        qa, ids_a = bf16(qh), torch.from_numpy(sel).to(dev)
+        copies = 3 if wla.nq >= 256 else 1
+        ks = [bf16(kh) for _ in range(copies)]
+        vs = [bf16(vh) for _ in range(copies)]
+        oa = torch.empty((wla.nq, wla.heads, 128), device=dev)
+        la = torch.empty((wla.nq, wla.heads), device=dev)
+        need = qsa.attention_workspace_bytes(wla.nq, wla.heads, wla.kv_heads, wla.width)
+        wsa = qsa.workspace(need, dev) if need else None
+        gathered = wla.gathered_bytes(sel)
+
+        def call(i, rot):
+            j = i % len(ks) if rot else 0
+            qsa.selection_attention(qa, ks[j], vs[j], ids_a, scale=wla.scale(), out=oa, lse=la, ws=wsa,
+                                    stream=cur())
+
+        us = time_us(lambda i: call(i, False), n=30)
+        entry = {"us": round(us, 2), "gathered_MiB": round(gathered / 2 ** 20, 1),
+                 "gathered_GBps": round(gathered / us / 1e3, 1),
+                 "hbm_frac": round(gathered / us / 1e3 / PEAK_HBM_GBS, 3)}
+        if copies > 1:
+            us_r = time_us(lambda i: call(i, True), n=30)
+            entry.update({"rotated_us": round(us_r, 2), "rotated_GBps": round(gathered / us_r / 1e3, 1),
+                          "rotated_hbm_frac": round(gathered / us_r / 1e3 / PEAK_HBM_GBS, 3)})
+        att[wla.name] = entry
+        del ks, vs, qa, ids_a, oa, la, wsa
+    return att
 
 
 def main():
@@ -237,6 +286,17 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda", 0)
+    if args.copy_calibration_mib:
+        src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if args.only_attention:
+        att = attention_figures(torch, qsa, synth, dev, lambda fn, n: graph_us(torch, dev, fn, n))
+        print(json.dumps({"selection_attention": att}), flush=True)
+        return
     wl = synth.c5()
     q_h, k_h, w_h = wl.tensors()
     q, k, w = (torch.from_numpy(x).to(dev) for x in (q_h, k_h, w_h))
@@ -244,13 +304,6 @@ def main():
     ids = torch.empty((wl.nq, wl.width), dtype=torch.int32, device=dev)
     counts = torch.empty((wl.nq,), dtype=torch.int32, device=dev)
     ws = qsa.workspace(qsa.topk_workspace_bytes(wl.nq, wl.n_blocks, wl.block_size, wl.width, wl.call), dev)
-
-    if args.copy_calibration_mib:
-        src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
 

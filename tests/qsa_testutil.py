@@ -78,12 +78,19 @@ def assert_scores_close(got: np.ndarray, ref: np.ndarray, label: str, terms=None
 
 
 def check_selection_near_threshold(ids_gpu, counts_gpu, ref_row: np.ndarray, bs: int, width: int,
-                                   label: str):
-    """End-to-end ids of one query against the oracle's FP64 scores: the same
-    count, and every block in which the two selections differ lies within
-    twice the score tolerance of the oracle's threshold score."""
+                                   label: str, active=None, cells=None):
+    """End-to-end ids of one query against the oracle's own selection from its
+    FP64 scores (rounded to FP32): the same count, and every block in which
+    the two selections differ lies within twice the score tolerance of the
+    oracle's threshold score. `active` (visible blocks) or `cells` (visible
+    cells) restrict the row as the entry points do."""
     n_blocks = ref_row.shape[0]
-    e_ids, e_cnt = oracle.topk_sort(ref_row.astype(np.float32)[None, :], n_blocks, bs, width)
+    row32 = ref_row.astype(np.float32)[None, :]
+    if cells is not None:
+        e_ids, e_cnt = oracle.topk_sort_cells(row32, n_blocks, bs, width, np.array([cells], np.int32))
+    else:
+        act = None if active is None else np.array([active], np.int32)
+        e_ids, e_cnt = oracle.topk_sort(row32, n_blocks, bs, width, act)
     assert counts_gpu == e_cnt[0], f"{label}: count {counts_gpu} vs {e_cnt[0]}"
     g = set(ids_gpu[:counts_gpu].tolist())
     e = set(e_ids[0, : e_cnt[0]].tolist())
