@@ -246,7 +246,9 @@ qsa_status qsa_select_cells(const float *q, const float *k, const float *w,
  *          entry outside [0, n_cells) selects nothing
  *   out    [nq][n_heads][head_dim] float output, 16-byte aligned
  *   lse    [nq][n_heads] float output (natural log), or NULL
- *   A query that selects no cell gets out = 0 and lse = -inf.
+ *   A query that selects no cell gets out = 0 and lse = -inf. Only the listed
+ *   cells' rows of k and v are read into the result (they must be finite);
+ *   other rows may hold anything.
  *   head_dim must be 128 (else QSA_EUNSUPPORTED); n_heads a multiple of
  *   kv_heads; n_cells, width >= 1; ld_ids >= width; scale finite.
  *   Products of bfloat16 values with FP32 accumulation, FP32 softmax.

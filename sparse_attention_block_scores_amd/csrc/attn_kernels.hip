@@ -86,10 +86,12 @@ struct StepIds {
     int c0;
 };
 
-// One step's gathered rows and the validity of its 32 cells (bit c).
+// One step's gathered rows, the validity of its 32 cells (bit c) and of the
+// two value rows this lane transposes.
 struct StepRows {
     uint4 ka[4], kb[4], v0[4], v1[4];
     uint64_t ma, mb;
+    bool w0, w1;
 };
 
 __device__ __forceinline__ StepIds load_ids(const int32_t *row, int c0, int width, int n)
@@ -115,6 +117,8 @@ __device__ __forceinline__ void load_rows(const StepIds &s, const AttnArgs &a, i
     const bool w1 = s.c0 + 2 * n + 1 < limit && (unsigned)s.v1 < (unsigned)a.n_cells;
     r.ma = __ballot(va);
     r.mb = __ballot(vb);
+    r.w0 = w0;
+    r.w1 = w1;
     // Row offsets in elements: a non-negative 31-bit id times the row length.
     const uint64_t len = (uint32_t)kv_row;
     const uint4 *kap = reinterpret_cast<const uint4 *>(a.k + (uint64_t)(uint32_t)(va ? s.a : 0) * len + head_off);
@@ -182,15 +186,19 @@ __device__ __forceinline__ void attend(const StepRows &r, const bf16x8 (&qb)[4],
     l += psum;
 
     // V^T into LDS: this lane holds cells 2n and 2n+1, dims 32lg .. 32lg+31;
-    // one byte permutation packs a dim's two cells into a dword.
+    // one byte permutation packs a dim's two cells into a dword. A masked
+    // cell's row (read from cell 0) is zeroed: its weight is exactly 0, and
+    // 0 times a non-finite value in a row nobody listed must not reach the sum.
     {
         const uint32_t *w0 = reinterpret_cast<const uint32_t *>(r.v0);
         const uint32_t *w1 = reinterpret_cast<const uint32_t *>(r.v1);
+        const uint32_t k0 = r.w0 ? 0xFFFFFFFFu : 0u, k1 = r.w1 ? 0xFFFFFFFFu : 0u;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int row = 32 * lg + 2 * e;
-            vt[vt_index(row, n)] = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
-            vt[vt_index(row + 1, n)] = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
+            const uint32_t a0 = w0[e] & k0, a1 = w1[e] & k1;
+            vt[vt_index(row, n)] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+            vt[vt_index(row + 1, n)] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
         }
     }
     // The wave reads what its own lanes wrote (LDS keeps a wave's order).

@@ -220,3 +220,59 @@ def test_back_to_back_calls_on_one_workspace():
         fin = np.isfinite(ref_lse)
         assert (np.isneginf(got_lse) == ~fin).all(), call
         assert (np.abs(got_lse[fin] - ref_lse[fin]) <= RTOL * np.maximum(1.0, np.abs(ref_lse[fin]))).all(), call
+
+
+def test_cache_beyond_4_gib():
+    """Key and value caches of 2^25 + 4,096 cells (8 GiB each): the listed
+    cells' row offsets pass 2^32 bytes. Only the listed rows are written (the
+    kernel reads nothing else); the oracle gets them compacted, with the ids
+    renumbered."""
+    nq, heads, n_cells, width = 3, 16, (1 << 25) + 4096, 512
+    ids = make_ids("gpu/attn/big", "blocks", nq, n_cells, width, width)
+    ids[0, :8] = np.arange(n_cells - 8, n_cells, dtype=np.int32)  # the very last cells
+    ids[1, 500:] = -1  # masked positions inside a step read cell 0, which holds NaN here
+    used = np.unique(ids[ids >= 0])
+    assert used[0] > 0
+    qb = synth.bf16_bits(synth.normal("gpu/attn/big/q", (nq, heads, 128)))
+    kb = synth.bf16_bits(synth.normal("gpu/attn/big/k", (used.size, 1, 128)))
+    vb = synth.bf16_bits(synth.normal("gpu/attn/big/v", (used.size, 1, 128)))
+    say("attention over 8 GiB key/value caches")
+    k = torch.empty((n_cells, 1, 128), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((n_cells, 1, 128), dtype=torch.bfloat16, device="cuda")
+    rows = to_dev(used.astype(np.int64))
+    k[rows] = bf16_dev(kb)
+    v[rows] = bf16_dev(vb)
+    k[0] = float("nan")
+    v[0] = float("nan")
+    out, lse = qsa.selection_attention(bf16_dev(qb), k, v, to_dev(ids), scale=0.088)
+    torch.cuda.synchronize()
+    del k, v
+    compact = np.searchsorted(used, np.where(ids >= 0, ids, 0)).astype(np.int32)
+    compact[ids < 0] = -1
+    qf, kf, vf = synth.bf16_values(qb), synth.bf16_values(kb), synth.bf16_values(vb)
+    ref, ref_lse = oracle.selection_attention(qf, kf, vf, compact, 0.088)
+    scale_t, _ = oracle.selection_attention(qf, kf, np.abs(vf), compact, 0.088)
+    assert (np.abs(out.cpu().numpy() - ref) <= RTOL * scale_t).all()
+    assert (np.abs(lse.cpu().numpy() - ref_lse) <= RTOL * np.maximum(1.0, np.abs(ref_lse))).all()
+
+
+def test_unlisted_rows_are_never_used():
+    """Every key and value row that no query lists holds NaN: ragged lists,
+    -1 tails, foreign ids and columns past the width must not pull any of them
+    into a result."""
+    nq, heads, kvh, n_cells, width, ld = 5, 16, 2, 3000, 300, 310
+    ids = make_ids("gpu/attn/nan", "ragged", nq, n_cells, width, ld)
+    ids[0, 7] = n_cells + 11
+    ids[1, 3] = -9
+    listed = ids[:, :width]
+    listed[(listed >= 0) & (listed < 4)] = -1  # block 0 unlisted: masked positions read its rows
+    ids[:, width:] = 0  # past the width: must be ignored
+    used = np.unique(listed[(listed >= 0) & (listed < n_cells)])
+    assert used[0] >= 4
+    qb = synth.bf16_bits(synth.normal("gpu/attn/nan/q", (nq, heads, 128)))
+    kb = synth.bf16_bits(synth.normal("gpu/attn/nan/k", (n_cells, kvh, 128)))
+    vb = synth.bf16_bits(synth.normal("gpu/attn/nan/v", (n_cells, kvh, 128)))
+    nan_rows = np.setdiff1d(np.arange(n_cells), used)
+    kb[nan_rows] = 0x7FC0  # bfloat16 NaN
+    vb[nan_rows] = 0x7FC0
+    check(qb, kb, vb, ids, 0.088, "unlisted rows hold NaN", width=width)
