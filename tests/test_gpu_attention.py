@@ -276,3 +276,47 @@ def test_unlisted_rows_are_never_used():
     kb[nan_rows] = 0x7FC0  # bfloat16 NaN
     vb[nan_rows] = 0x7FC0
     check(qb, kb, vb, ids, 0.088, "unlisted rows hold NaN", width=width)
+
+
+def test_graph_replays_with_changing_lists():
+    """Captured once in a HIP graph (the chunked two-launch shape of a decode
+    call) and replayed four times; between replays the id buffer is rewritten
+    eagerly, and every replay must match the oracle for the ids it saw."""
+    nq, heads, kvh, n_cells, width = 4, 16, 1, 20000, 1024
+    qb = synth.bf16_bits(synth.normal("gpu/attn/graph/q", (nq, heads, 128)))
+    kb = synth.bf16_bits(synth.normal("gpu/attn/graph/k", (n_cells, kvh, 128)))
+    vb = synth.bf16_bits(synth.normal("gpu/attn/graph/v", (n_cells, kvh, 128)))
+    lists = [make_ids(f"gpu/attn/graph/{j}", "ragged" if j % 2 else "blocks", nq, n_cells, width, width)
+             for j in range(4)]
+    need = qsa.attention_workspace_bytes(nq, heads, kvh, width)
+    assert need > 0  # several chunks per query: two launches in the graph
+    q, k, v = bf16_dev(qb), bf16_dev(kb), bf16_dev(vb)
+    ids = to_dev(lists[0])
+    out = torch.empty((nq, heads, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((nq, heads), dtype=torch.float32, device="cuda")
+    ws = qsa.workspace(need)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    say("attention graph capture")
+    with torch.cuda.stream(side):
+        qsa.selection_attention(q, k, v, ids, scale=0.09, out=out, lse=lse, ws=ws, stream=side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            qsa.selection_attention(q, k, v, ids, scale=0.09, out=out, lse=lse, ws=ws, stream=side)
+    torch.cuda.synchronize()
+    qf, kf, vf = synth.bf16_values(qb), synth.bf16_values(kb), synth.bf16_values(vb)
+    for j, lst in enumerate(lists):
+        ids.copy_(to_dev(lst))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say(f"attention graph replay {j}")
+        graph.replay()
+        torch.cuda.synchronize()
+        ref, ref_lse = oracle.selection_attention(qf, kf, vf, lst, 0.09)
+        scale_t, _ = oracle.selection_attention(qf, kf, np.abs(vf), lst, 0.09)
+        assert (np.abs(out.cpu().numpy() - ref) <= RTOL * scale_t).all(), j
+        got_lse = lse.cpu().numpy()
+        fin = np.isfinite(ref_lse)
+        assert (np.isneginf(got_lse) == ~fin).all(), j
+        assert (np.abs(got_lse[fin] - ref_lse[fin]) <= RTOL * np.maximum(1.0, np.abs(ref_lse[fin]))).all(), j
