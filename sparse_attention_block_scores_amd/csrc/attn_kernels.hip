@@ -260,7 +260,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a)
     if (steps > 0) {
         // The id loads start the dependent chain; the query rows load beside them.
         StepIds i0 = load_ids(idrow, first, a.width, n);
-        StepIds i1 = load_ids(idrow, first + kAttnStepCells, a.width, n);
         // This lane's matrix-core column: query head hb*16 + n of the group
         // (a padding column reads head 0 of the group and is zeroed).
         const bool head_ok = hb * kAttnHeadBlock + n < a.group;
@@ -274,16 +273,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a)
             qb[s] = as_bf16x8(make_uint4(x.x & keep, x.y & keep, x.z & keep, x.w & keep));
         }
         StepRows r0, r1;
-        load_rows(i0, a, limit, kv_row, head_off, n, r0);
-        for (int j = 0; j < steps; j += 2) {
-            i0 = load_ids(idrow, first + (j + 2) * kAttnStepCells, a.width, n);
-            load_rows(i1, a, limit, kv_row, head_off, n, r1);
-            attend(r0, qb, a.scale_log2, n, lg, vt, m, l, o);
-            if (j + 1 >= steps)
-                break;
-            i1 = load_ids(idrow, first + (j + 3) * kAttnStepCells, a.width, n);
+        if (steps == 1) {  // wave-uniform: nothing to overlap (decode calls), no prefetch
             load_rows(i0, a, limit, kv_row, head_off, n, r0);
-            attend(r1, qb, a.scale_log2, n, lg, vt, m, l, o);
+            attend(r0, qb, a.scale_log2, n, lg, vt, m, l, o);
+        } else {
+            StepIds i1 = load_ids(idrow, first + kAttnStepCells, a.width, n);
+            load_rows(i0, a, limit, kv_row, head_off, n, r0);
+            for (int j = 0; j < steps; j += 2) {
+                i0 = load_ids(idrow, first + (j + 2) * kAttnStepCells, a.width, n);
+                load_rows(i1, a, limit, kv_row, head_off, n, r1);
+                attend(r0, qb, a.scale_log2, n, lg, vt, m, l, o);
+                if (j + 1 >= steps)
+                    break;
+                i1 = load_ids(idrow, first + (j + 3) * kAttnStepCells, a.width, n);
+                load_rows(i0, a, limit, kv_row, head_off, n, r0);
+                attend(r1, qb, a.scale_log2, n, lg, vt, m, l, o);
+            }
         }
     }
     l += __shfl_xor(l, 16);
