@@ -255,7 +255,8 @@ qsa_status qsa_select_cells(const float *q, const float *k, const float *w,
  *   workspace: qsa_selection_attention_workspace_bytes() bytes, 256-byte
  *   aligned (may be NULL when that is 0): per-chunk partial results, written
  *   and read within the call; its contents need no set-up. Calls that may
- *   overlap need separate workspaces.
+ *   overlap need separate workspaces. The size function also returns 0 for
+ *   sizes the call rejects (it then fails with QSA_EINVAL).
  */
 size_t qsa_selection_attention_workspace_bytes(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width);
 qsa_status qsa_selection_attention(const void *q, const void *k, const void *v,
