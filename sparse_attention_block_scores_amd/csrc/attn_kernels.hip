@@ -33,10 +33,12 @@
 //    i: a head's softmax is lane-local apart from one max and one sum over the
 //    four lane groups.
 //  * O^T[128 dims x 16 heads] += V^T[dims x 32 cells] . P^T[32 cells x heads].
-//    The cells are the contraction, so V is transposed through LDS (cell
-//    pairs packed per dword) and P comes straight from the S^T registers:
-//    contraction position 8j+i is cell 4j+i of the step's first 16 cells and
-//    8j+4+i is cell 16+4j+i. P is split into a bfloat16 head and tail
+//    The cells are the contraction, so the operand is V transposed: the rows
+//    go into LDS as they are and come back transposed by gfx950's transpose
+//    read (ds_read_b64_tr_b16: within 16 lanes, lane 4a+b receives element b
+//    of the 4-element reads of lanes a, 4+a, 8+a, 12+a). P comes straight
+//    from the S^T registers: contraction position 8j+i is cell 4j+i of the
+//    step's first 16 cells and 8j+4+i is cell 16+4j+i. P is split into a bfloat16 head and tail
 //    (hi + lo equals p to about 2^-17 relative) and both are multiplied, so
 //    the weighted sum keeps close to FP32 accuracy.
 #include <math.h>
@@ -49,17 +51,17 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int kThreads = 64 * kAttnWaves;
-// V^T rows: 16 dwords (32 cells as bfloat16 pairs) + 2 of padding, and 16
-// more dwords after every 32 rows, so that the four lane groups' packed
-// writes and the matrix-core operand reads fall in distinct banks.
-constexpr int kVtPitch = 18;
-constexpr int kVtWords = 128 * kVtPitch + 4 * 16;
+// V rows in LDS: 128 bfloat16 (64 dwords) + 8 dwords of padding per cell, so
+// that the 16 lanes of a transpose read (4 cells x 4 dim quads) fall in
+// distinct banks.
+constexpr int kVPitch = 72;
+constexpr int kVtWords = kAttnStepCells * kVPitch;
 constexpr int kOPitch = 132;  // floats per head row of the merge buffer
 constexpr float kRescale = 8.f;  // log2 headroom of the running softmax reference
-
-__device__ __forceinline__ int vt_index(int row, int pair) { return row * kVtPitch + (row >> 5) * 16 + pair; }
 
 struct AttnMerge {
     float o[kAttnWaves][kAttnHeadBlock][kOPitch];
@@ -79,19 +81,19 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// The ids of one step: this lane's positions c0+n and c0+16+n (key rows, the
-// two 16-cell halves) and c0+2n, c0+2n+1 (the value rows it transposes).
+// The ids of one step: this lane's positions c0+n and c0+16+n (its key and
+// value rows in the two 16-cell halves).
 struct StepIds {
-    int a, b, v0, v1;
+    int a, b;
     int c0;
 };
 
-// One step's gathered rows, the validity of its 32 cells (bit c) and of the
-// two value rows this lane transposes.
+// One step's gathered rows and the validity of its 32 cells (bit c) and of
+// this lane's two cells.
 struct StepRows {
     uint4 ka[4], kb[4], v0[4], v1[4];
     uint64_t ma, mb;
-    bool w0, w1;
+    bool va, vb;
 };
 
 __device__ __forceinline__ StepIds load_ids(const int32_t *row, int c0, int width, int n)
@@ -101,8 +103,6 @@ __device__ __forceinline__ StepIds load_ids(const int32_t *row, int c0, int widt
     s.c0 = c0;
     s.a = row[min(c0 + n, last)];
     s.b = row[min(c0 + 16 + n, last)];
-    s.v0 = row[min(c0 + 2 * n, last)];
-    s.v1 = row[min(c0 + 2 * n + 1, last)];
     return s;
 }
 
@@ -113,18 +113,16 @@ __device__ __forceinline__ void load_rows(const StepIds &s, const AttnArgs &a, i
 {
     const bool va = s.c0 + n < limit && (unsigned)s.a < (unsigned)a.n_cells;
     const bool vb = s.c0 + 16 + n < limit && (unsigned)s.b < (unsigned)a.n_cells;
-    const bool w0 = s.c0 + 2 * n < limit && (unsigned)s.v0 < (unsigned)a.n_cells;
-    const bool w1 = s.c0 + 2 * n + 1 < limit && (unsigned)s.v1 < (unsigned)a.n_cells;
     r.ma = __ballot(va);
     r.mb = __ballot(vb);
-    r.w0 = w0;
-    r.w1 = w1;
+    r.va = va;
+    r.vb = vb;
     // Row offsets in elements: a non-negative 31-bit id times the row length.
     const uint64_t len = (uint32_t)kv_row;
     const uint4 *kap = reinterpret_cast<const uint4 *>(a.k + (uint64_t)(uint32_t)(va ? s.a : 0) * len + head_off);
     const uint4 *kbp = reinterpret_cast<const uint4 *>(a.k + (uint64_t)(uint32_t)(vb ? s.b : 0) * len + head_off);
-    const uint4 *v0p = reinterpret_cast<const uint4 *>(a.v + (uint64_t)(uint32_t)(w0 ? s.v0 : 0) * len + head_off);
-    const uint4 *v1p = reinterpret_cast<const uint4 *>(a.v + (uint64_t)(uint32_t)(w1 ? s.v1 : 0) * len + head_off);
+    const uint4 *v0p = reinterpret_cast<const uint4 *>(a.v + (uint64_t)(uint32_t)(va ? s.a : 0) * len + head_off);
+    const uint4 *v1p = reinterpret_cast<const uint4 *>(a.v + (uint64_t)(uint32_t)(vb ? s.b : 0) * len + head_off);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         r.ka[i] = kap[i];
@@ -185,32 +183,37 @@ __device__ __forceinline__ void attend(const StepRows &r, const bf16x8 (&qb)[4],
     }
     l += psum;
 
-    // V^T into LDS: this lane holds cells 2n and 2n+1, dims 32lg .. 32lg+31;
-    // one byte permutation packs a dim's two cells into a dword. A masked
-    // cell's row (read from cell 0) is zeroed: its weight is exactly 0, and
-    // 0 times a non-finite value in a row nobody listed must not reach the sum.
+    // V rows into LDS as they are: this lane holds cells n and 16+n, dims
+    // 32lg .. 32lg+31. A masked cell's row (read from cell 0) is zeroed: its
+    // weight is exactly 0, and 0 times a non-finite value in a row nobody
+    // listed must not reach the sum.
     {
-        const uint32_t *w0 = reinterpret_cast<const uint32_t *>(r.v0);
-        const uint32_t *w1 = reinterpret_cast<const uint32_t *>(r.v1);
-        const uint32_t k0 = r.w0 ? 0xFFFFFFFFu : 0u, k1 = r.w1 ? 0xFFFFFFFFu : 0u;
+        const uint32_t k0 = r.va ? 0xFFFFFFFFu : 0u, k1 = r.vb ? 0xFFFFFFFFu : 0u;
+        uint4 *d0 = reinterpret_cast<uint4 *>(vt + n * kVPitch + 16 * lg);
+        uint4 *d1 = reinterpret_cast<uint4 *>(vt + (16 + n) * kVPitch + 16 * lg);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int row = 32 * lg + 2 * e;
-            const uint32_t a0 = w0[e] & k0, a1 = w1[e] & k1;
-            vt[vt_index(row, n)] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-            vt[vt_index(row + 1, n)] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+        for (int i = 0; i < 4; ++i) {
+            d0[i] = make_uint4(r.v0[i].x & k0, r.v0[i].y & k0, r.v0[i].z & k0, r.v0[i].w & k0);
+            d1[i] = make_uint4(r.v1[i].x & k1, r.v1[i].y & k1, r.v1[i].z & k1, r.v1[i].w & k1);
         }
     }
     // The wave reads what its own lanes wrote (LDS keeps a wave's order).
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // Operand of dim tile t for lane (lg, n): V[4lg + j][16t + n] and
+    // V[16 + 4lg + j][16t + n], j = 0..3, by two transpose reads in which lane
+    // n of the group reads dims 16t + 4(n%4) .. +3 of cell 4lg + n/4 (16 + ...).
+    const int rsel = 4 * lg + (n >> 2), csel = 2 * (n & 3);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const int row = 16 * t + n;
-        const uint2 lo = *reinterpret_cast<const uint2 *>(&vt[vt_index(row, 2 * lg)]);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(&vt[vt_index(row, 8 + 2 * lg)]);
-        const bf16x8 av = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        uint32_t *p0 = vt + rsel * kVPitch + 8 * t + csel;
+        uint32_t *p1 = p0 + 16 * kVPitch;
+        // vt is LDS: the generic pointer converts to the local address space.
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p0);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p1);
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        const bf16x8 av = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
         o[t] = mfma(av, ph, o[t]);
         o[t] = mfma(av, pl, o[t]);
     }
