@@ -261,7 +261,10 @@ __device__ __forceinline__ void score_tiles_bf16(const ScoreArgs &a, int row0, i
     const uint16_t *qh = reinterpret_cast<const uint16_t *>(a.q);
     const uint16_t *kh = reinterpret_cast<const uint16_t *>(a.k);
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
+    const int lane = tid & 63;
+    // Wave-uniform (scalar): the tile's first query, and with it the score
+    // stores' buffer resource, stay in scalar registers.
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, half = lane >> 5;
     const bool live = __builtin_amdgcn_readfirstlane(row0 + wv * MR * 32) < a.nq * HP;  // wave-uniform
 
