@@ -247,7 +247,7 @@ constexpr int kScoreBufferWord3 = 0x00020000;
 
 template <int ROWS>
 struct ScoreLdsH {
-    __attribute__((aligned(16))) uint16_t k[2][kTileBlocks * kLdsRowH];
+    __attribute__((aligned(16))) uint16_t k[4][kTileBlocks * kLdsRowH];  // two pairs of key tiles
     float w[ROWS];
 };
 
@@ -325,17 +325,17 @@ __device__ __forceinline__ void score_tiles_bf16(const ScoreArgs &a, int row0, i
         }
     };
 
-    // Key tiles come in PF deep: tile t + PF is loaded while tile t is
-    // scored, so the load latency hides behind PF - 1 tiles of matrix-core
-    // work (a tile is only 8 steps here), and the barrier between tiles
-    // orders LDS only, leaving the loads in flight. The loop body has no
-    // branch around a memory access, so the compiler waits for exactly the
-    // load a step needs: slots past the last tile score the last tile again
-    // with every store dropped, loads of tiles past the end re-read the last
-    // one, and waves whose rows are all padding score zero rows (their
-    // stores are dropped too).
-    constexpr int PF = 2;
-    uint4 ring[PF][GPT];
+    // Key tiles go through LDS in pairs: the workgroup scores one pair from
+    // one half of the LDS while the next pair, loaded a pair ago into
+    // registers, is stored into the other half and the pair after it is
+    // loaded; one barrier per pair (a tile is only 8 matrix-core steps here,
+    // so a barrier per tile costs a visible share). The barrier orders LDS
+    // only, leaving the loads in flight. The loop body has no branch around a
+    // memory access, so the compiler waits for exactly the loads a step needs:
+    // slots past the last tile score the last tile again with every store
+    // dropped, loads of tiles past the end re-read the last one, and waves
+    // whose rows are all padding score zero rows (their stores are dropped too).
+    uint4 ring[2][GPT];
     auto load_into = [&](int t, uint4 (&dst)[GPT]) {
         load_tile(min(t, t1 - 1));
 #pragma unroll
@@ -348,10 +348,12 @@ __device__ __forceinline__ void score_tiles_bf16(const ScoreArgs &a, int row0, i
             pre[i] = src[i];
         store_tile(dst);
     };
-#pragma unroll
-    for (int d = 0; d < PF; ++d)
-        load_into(t0 + d, ring[d]);
+    load_into(t0, ring[0]);
+    load_into(t0 + 1, ring[1]);
     store_from(ring[0], sm.k[0]);
+    store_from(ring[1], sm.k[1]);
+    load_into(t0 + 2, ring[0]);
+    load_into(t0 + 3, ring[1]);
     __syncthreads();
 
     // The q rows and the first tiles were loaded above; nothing of the
@@ -366,33 +368,38 @@ __device__ __forceinline__ void score_tiles_bf16(const ScoreArgs &a, int row0, i
             wr[m][v] = sm.w[(wv * MR + m) * 32 + 8 * (v >> 2) + 4 * half + (v & 3)];
     (void)live;
 
-    for (int tb = t0; tb < t1; tb += PF) {
+    for (int tb = t0; tb < t1; tb += 4) {
 #pragma unroll
-        for (int d = 0; d < PF; ++d) {
-            const int t = tb + d;
-            const int cur = d & 1;  // (t - t0) & 1, as PF is even
-            f32x16 acc[MR];
+        for (int pr = 0; pr < 2; ++pr) {      // pair tb + 2pr .. tb + 2pr + 1 in LDS half pr
 #pragma unroll
-            for (int m = 0; m < MR; ++m)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    acc[m][v] = 0.f;
-            const uint16_t *kb = &sm.k[cur][li * kLdsRowH + 64 * half];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(kb + 8 * u));
+            for (int d = 0; d < 2; ++d) {
+                const int t = tb + 2 * pr + d;
+                f32x16 acc[MR];
 #pragma unroll
                 for (int m = 0; m < MR; ++m)
-                    acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[m][u], b, acc[m], 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        acc[m][v] = 0.f;
+                const uint16_t *kb = &sm.k[2 * pr + d][li * kLdsRowH + 64 * half];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(kb + 8 * u));
+#pragma unroll
+                    for (int m = 0; m < MR; ++m)
+                        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[m][u], b, acc[m], 0, 0, 0);
+                }
+                // A slot past the last tile: its column test fails for every lane.
+                const int blk = t < t1 ? t * kTileBlocks + li : a.n_blocks;
+                score_epilogue<HP, MR, true>(acc, a, row0, wv, half, blk, [&](int m, int v) { return wr[m][v]; },
+                                             store);
             }
-            // A slot past the last tile: its column test fails for every lane.
-            const int blk = t < t1 ? t * kTileBlocks + li : a.n_blocks;
-            score_epilogue<HP, MR, true>(acc, a, row0, wv, half, blk, [&](int m, int v) { return wr[m][v]; },
-                                         store);
-            // Tile t + 1 (in ring slot (d + 1) % PF) into the other LDS buffer;
-            // tile t + PF into the slot tile t came from.
-            store_from(ring[(d + 1) % PF], sm.k[cur ^ 1]);
-            load_into(t + PF, ring[d]);
+            // The next pair (in the ring) into the other LDS half, and the
+            // pair after it into the ring.
+            const int tn = tb + 2 * pr + 2;
+            store_from(ring[0], sm.k[2 * (pr ^ 1)]);
+            store_from(ring[1], sm.k[2 * (pr ^ 1) + 1]);
+            load_into(tn + 2, ring[0]);
+            load_into(tn + 3, ring[1]);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
