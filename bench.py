@@ -32,6 +32,7 @@ METRIC = "qsa_select µs/call (score+top-k) decode nq=3 & prompt nq=256; % HBM/M
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
 PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+ROTATION_BYTES = 512 << 20      # score lines touched per rotation cycle: 2x the 256 MB last-level cache
 SCORER_SOURCES = [os.path.join(ROOT, "sparse_attention_block_scores_amd", "csrc", f)
                   for f in ("scores_kernel.hip", "scores_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scores_kernel_c5_traffic.json")
@@ -187,18 +188,25 @@ def secondary(torch, qsa, synth, dev, reps=50):
         for variant in ("continuous", "q64", "equal"):
             t = synth.c4(nb, variant)
             host = t.scores()
-            # Four distinct score buffers (4 x 128 MiB) so that reads come from HBM,
-            # not from the 256 MB last-level cache.
-            bufs = [torch.from_numpy(host).to(dev) for _ in range(4)]
+            # Distinct score buffers, cycled, so that the score lines one cycle
+            # touches (nq x n_blocks x 4 bytes per buffer, rows ld apart) add
+            # up to at least 512 MiB: twice the 256 MB last-level cache, so
+            # every call reads its scores from HBM.
+            touched = t.nq * nb * 4
+            nbuf = -(-ROTATION_BYTES // touched)
+            bufs = [torch.from_numpy(host).to(dev) for _ in range(nbuf)]
             wsp = qsa.workspace(qsa.topk_workspace_bytes(t.nq, nb, 4, t.width, "prompt"), dev)
             idp = torch.empty((t.nq, t.width), dtype=torch.int32, device=dev)
             cp = torch.empty((t.nq,), dtype=torch.int32, device=dev)
-            us = time_us(lambda i: qsa.block_topk(bufs[i % 4], nb, 4, t.width, "prompt", ids=idp, counts=cp,
-                                                  ws=wsp, stream=cur()), n=40)
-            gbs = t.nq * nb * 4 / us / 1e3
+            us = time_us(lambda i: qsa.block_topk(bufs[i % nbuf], nb, 4, t.width, "prompt", ids=idp, counts=cp,
+                                                  ws=wsp, stream=cur()), n=max(40, 2 * nbuf))
+            gbs = touched / us / 1e3
             if variant == "continuous":
+                warm = time_us(lambda i: qsa.block_topk(bufs[0], nb, 4, t.width, "prompt", ids=idp, counts=cp,
+                                                        ws=wsp, stream=cur()), n=40)
                 entry.update({"us": round(us, 2), "scores_GBps": round(gbs, 1),
-                              "hbm_frac": round(gbs / PEAK_HBM_GBS, 3)})
+                              "hbm_frac": round(gbs / PEAK_HBM_GBS, 3), "rotated_buffers": nbuf,
+                              "rotated_MiB": round(nbuf * touched / 2 ** 20), "warm_us": round(warm, 2)})
             else:  # 64-level keys; all-equal keys (every query takes the exact fallback)
                 entry[variant + "_us"] = round(us, 2)
             del bufs

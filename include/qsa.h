@@ -92,10 +92,7 @@ typedef struct qsa_options {
     int32_t force_fallback; /* ONEREAD: every query takes the exact fallback over its whole row */
     int32_t oneread_blocks; /* ONEREAD blocks streamed per batch: 0 or 16384 (others QSA_EUNSUPPORTED) */
     int32_t oneread_parts;  /* ONEREAD workgroups per query: 0 = auto, else 1..16 */
-    int32_t fused_select;   /* qsa_select, decode calls of up to 1,024 blocks, 16 queries and 32 heads,
-                               no length array: 1 = scores and top-k in one launch (the default, 0,
-                               is two launches, which measured faster on MI355X) */
-    int32_t reserved[1];    /* must be zero */
+    int32_t reserved[2];    /* must be zero */
 } qsa_options;
 
 /* The launch plan the top-k would use; exported so host code and tests can

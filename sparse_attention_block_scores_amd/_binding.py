@@ -38,8 +38,7 @@ class Options(ctypes.Structure):
         ("force_fallback", ctypes.c_int32),
         ("oneread_blocks", ctypes.c_int32),
         ("oneread_parts", ctypes.c_int32),
-        ("fused_select", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 1),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -168,13 +167,69 @@ def topk_workspace_bytes(nq, n_blocks, block_size, width, call, options=None) ->
 
 
 def workspace(nbytes: int, device=None, stream=None) -> torch.Tensor:
-    """A zero-filled workspace of nbytes (256-byte aligned)."""
+    """A zero-filled workspace of nbytes (256-byte aligned), allocated and
+    zeroed on `stream` (default: the current stream). The caching allocator
+    ties a block to the stream it was allocated on, so a workspace the calls
+    below make for themselves, used on `stream` and dropped on return, is not
+    handed to other work until that stream's kernels are done with it."""
     device = device or torch.device("cuda", torch.cuda.current_device())
-    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    st = torch.cuda.current_stream(device) if stream is None else stream
+    with torch.cuda.stream(st):
+        buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
     off = (-buf.data_ptr()) % 256
     ws = buf[off:off + nbytes]
-    _check(lib().qsa_workspace_init(_ptr(ws), nbytes, _stream(stream)), "qsa_workspace_init")
+    _check(lib().qsa_workspace_init(_ptr(ws), nbytes, _stream(st)), "qsa_workspace_init")
     return ws
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+# ---------------------------------------------------------------- shape checks
+# Pure functions of shapes and strides (no device needed), so a mismatch is
+# reported before any launch and the checks are testable on the CPU.
+
+def scorer_shapes(q_shape, k_shape, w_shape):
+    """(nq, heads, head_dim, n_blocks) of q [nq, heads, head_dim], k
+    [n_blocks, head_dim] and w [nq, heads]; ValueError on a mismatch."""
+    if len(q_shape) != 3 or len(k_shape) != 2 or len(w_shape) != 2:
+        raise ValueError(f"q must be 3-d, k and w 2-d; got q{tuple(q_shape)} k{tuple(k_shape)} w{tuple(w_shape)}")
+    nq, heads, head_dim = (int(x) for x in q_shape)
+    n_blocks = int(k_shape[0])
+    if int(k_shape[1]) != head_dim:
+        raise ValueError(f"k is [n_blocks, {int(k_shape[1])}] but q's head width is {head_dim}")
+    if tuple(int(x) for x in w_shape) != (nq, heads):
+        raise ValueError(f"w must be [nq, heads] = [{nq}, {heads}], got {tuple(w_shape)}")
+    return nq, heads, head_dim, n_blocks
+
+
+def score_matrix_shape(shape, strides, nq, n_blocks, name="scores"):
+    """ld of a [nq, ld] score matrix with unit column stride and ld >= n_blocks."""
+    if len(shape) != 2 or int(strides[1]) != 1:
+        raise ValueError(f"{name} must be [nq, ld] with unit column stride")
+    if int(shape[0]) != nq:
+        raise ValueError(f"{name} has {int(shape[0])} rows, expected nq = {nq}")
+    if int(shape[1]) < n_blocks:
+        raise ValueError(f"{name} has {int(shape[1])} columns, fewer than n_blocks = {n_blocks}")
+    ld = int(strides[0]) if nq > 1 else max(int(strides[0]), int(shape[1]))
+    if ld < n_blocks:
+        raise ValueError(f"{name} row stride {ld} is below n_blocks = {n_blocks}")
+    return ld
+
+
+def topk_output_shapes(ids_shape, ids_contiguous, counts_shape, counts_contiguous, nq, width):
+    """ids [nq, width] and counts [nq], both contiguous."""
+    if tuple(int(x) for x in ids_shape) != (nq, width) or not ids_contiguous:
+        raise ValueError(f"ids must be a contiguous [nq, width] = [{nq}, {width}] int32 tensor, "
+                         f"got {tuple(ids_shape)}")
+    if tuple(int(x) for x in counts_shape) != (nq,) or not counts_contiguous:
+        raise ValueError(f"counts must be a contiguous [nq] = [{nq}] int32 tensor, got {tuple(counts_shape)}")
+
+
+def length_shape(shape, contiguous, nq, name):
+    if tuple(int(x) for x in shape) != (nq,) or not contiguous:
+        raise ValueError(f"{name} must be a contiguous [nq] = [{nq}] int32 tensor, got {tuple(shape)}")
 
 
 def block_scores(q, k, w, scores=None, stream=None):
@@ -182,16 +237,12 @@ def block_scores(q, k, w, scores=None, stream=None):
     _dev(q, torch.float32, "q"), _dev(k, torch.float32, "k"), _dev(w, torch.float32, "w")
     if not (q.is_contiguous() and k.is_contiguous() and w.is_contiguous()):
         raise ValueError("q, k and w must be contiguous")
-    nq, heads, head_dim = q.shape
-    n_blocks = k.shape[0]
-    if k.shape[1] != head_dim or tuple(w.shape) != (nq, heads):
-        raise ValueError("shape mismatch between q, k and w")
+    nq, heads, head_dim, n_blocks = scorer_shapes(q.shape, k.shape, w.shape)
     if scores is None:
         scores = torch.empty((nq, n_blocks), dtype=torch.float32, device=q.device)
     _dev(scores, torch.float32, "scores")
-    if scores.dim() != 2 or scores.shape[0] != nq or scores.stride(1) != 1:
-        raise ValueError("scores must be [nq, ld] with unit column stride")
-    _check(lib().qsa_block_scores(_ptr(q), _ptr(k), _ptr(w), _ptr(scores), scores.stride(0), nq, heads,
+    ld = score_matrix_shape(scores.shape, scores.stride(), nq, n_blocks)
+    _check(lib().qsa_block_scores(_ptr(q), _ptr(k), _ptr(w), _ptr(scores), ld, nq, heads,
                                   head_dim, n_blocks, _stream(stream)), "qsa_block_scores")
     return scores
 
@@ -201,16 +252,12 @@ def block_scores_bf16(q, k, w, scores=None, stream=None):
     _dev(q, torch.bfloat16, "q"), _dev(k, torch.bfloat16, "k"), _dev(w, torch.float32, "w")
     if not (q.is_contiguous() and k.is_contiguous() and w.is_contiguous()):
         raise ValueError("q, k and w must be contiguous")
-    nq, heads, head_dim = q.shape
-    n_blocks = k.shape[0]
-    if k.shape[1] != head_dim or tuple(w.shape) != (nq, heads):
-        raise ValueError("shape mismatch between q, k and w")
+    nq, heads, head_dim, n_blocks = scorer_shapes(q.shape, k.shape, w.shape)
     if scores is None:
         scores = torch.empty((nq, n_blocks), dtype=torch.float32, device=q.device)
     _dev(scores, torch.float32, "scores")
-    if scores.dim() != 2 or scores.shape[0] != nq or scores.stride(1) != 1:
-        raise ValueError("scores must be [nq, ld] with unit column stride")
-    _check(lib().qsa_block_scores_bf16(_ptr(q), _ptr(k), _ptr(w), _ptr(scores), scores.stride(0), nq, heads,
+    ld = score_matrix_shape(scores.shape, scores.stride(), nq, n_blocks)
+    _check(lib().qsa_block_scores_bf16(_ptr(q), _ptr(k), _ptr(w), _ptr(scores), ld, nq, heads,
                                        head_dim, n_blocks, _stream(stream)), "qsa_block_scores_bf16")
     return scores
 
@@ -249,11 +296,11 @@ def selection_attention(q, k, v, ids, width=None, scale=None, out=None, lse=None
         raise ValueError("out and lse must be contiguous")
     need = attention_workspace_bytes(nq, n_heads, kv_heads, width)
     if ws is None and need > 0:
-        ws = workspace(need, q.device)
+        ws = workspace(need, q.device, stream)
     _check(lib().qsa_selection_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(ids), ids.stride(0), _ptr(out),
                                          _ptr(lse), nq, n_heads, kv_heads, head_dim, n_cells, width, scale,
                                          _ptr(ws) if ws is not None else None,
-                                         ws.numel() * ws.element_size() if ws is not None else 0,
+                                         _nbytes(ws) if ws is not None else 0,
                                          _stream(stream)), "qsa_selection_attention")
     return out, lse
 
@@ -264,8 +311,7 @@ def _topk_outputs(nq, width, device, ids, counts):
     if counts is None:
         counts = torch.empty((nq,), dtype=torch.int32, device=device)
     _dev(ids, torch.int32, "ids"), _dev(counts, torch.int32, "counts")
-    if not ids.is_contiguous() or tuple(ids.shape) != (nq, width):
-        raise ValueError("ids must be a contiguous [nq, width] int32 tensor")
+    topk_output_shapes(ids.shape, ids.is_contiguous(), counts.shape, counts.is_contiguous(), nq, width)
     return ids, counts
 
 
@@ -273,8 +319,7 @@ def _active(active, nq, name="active"):
     if active is None:
         return None
     _dev(active, torch.int32, name)
-    if tuple(active.shape) != (nq,) or not active.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous [nq] int32 tensor")
+    length_shape(active.shape, active.is_contiguous(), nq, name)
     return active
 
 
@@ -293,9 +338,10 @@ def block_topk(scores, n_blocks, block_size, width, call, active=None, ids=None,
     `cells` ([nq] int32 on the device) gives a visible cell count per query
     (qsa_block_topk_cells) instead of `active` blocks."""
     _dev(scores, torch.float32, "scores")
-    if scores.dim() != 2 or scores.stride(1) != 1:
+    if scores.dim() != 2:
         raise ValueError("scores must be [nq, ld] with unit column stride")
     nq = scores.shape[0]
+    ld = score_matrix_shape(scores.shape, scores.stride(), nq, n_blocks)
     code = _call_code(call)
     lengths, by_cells = _lengths(active, cells, nq)
     ids, counts = _topk_outputs(nq, width, scores.device, ids, counts)
@@ -303,8 +349,8 @@ def block_topk(scores, n_blocks, block_size, width, call, active=None, ids=None,
     if ws is None:
         ws = workspace(need, scores.device, stream)
     name = "qsa_block_topk_cells" if by_cells else "qsa_block_topk"
-    _check(getattr(lib(), name)(_ptr(scores), scores.stride(0), nq, n_blocks, block_size, width, code,
-                                _ptr(lengths), _ptr(ids), _ptr(counts), _ptr(ws), ws.numel(),
+    _check(getattr(lib(), name)(_ptr(scores), ld, nq, n_blocks, block_size, width, code,
+                                _ptr(lengths), _ptr(ids), _ptr(counts), _ptr(ws), _nbytes(ws),
                                 _stream(stream), _opt(options)), name)
     return ids, counts
 
@@ -316,11 +362,11 @@ def select(q, k, w, block_size, width, call, scores=None, active=None, ids=None,
         _dev(t, torch.float32, n)
         if not t.is_contiguous():
             raise ValueError(f"{n} must be contiguous")
-    nq, heads, head_dim = q.shape
-    n_blocks = k.shape[0]
+    nq, heads, head_dim, n_blocks = scorer_shapes(q.shape, k.shape, w.shape)
     if scores is None:
         scores = torch.empty((nq, n_blocks), dtype=torch.float32, device=q.device)
     _dev(scores, torch.float32, "scores")
+    ld = score_matrix_shape(scores.shape, scores.stride(), nq, n_blocks)
     code = _call_code(call)
     lengths, by_cells = _lengths(active, cells, nq)
     ids, counts = _topk_outputs(nq, width, q.device, ids, counts)
@@ -328,7 +374,7 @@ def select(q, k, w, block_size, width, call, scores=None, active=None, ids=None,
     if ws is None:
         ws = workspace(need, q.device, stream)
     name = "qsa_select_cells" if by_cells else "qsa_select"
-    _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(w), heads, head_dim, _ptr(scores), scores.stride(0), nq,
+    _check(getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(w), heads, head_dim, _ptr(scores), ld, nq,
                                 n_blocks, block_size, width, code, _ptr(lengths), _ptr(ids), _ptr(counts),
-                                _ptr(ws), ws.numel(), _stream(stream), _opt(options)), name)
+                                _ptr(ws), _nbytes(ws), _stream(stream), _opt(options)), name)
     return scores, ids, counts

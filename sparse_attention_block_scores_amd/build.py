@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libqsa.so")
-SOURCES = ["qsa_api.hip", "topk_kernels.hip", "scores_kernel.hip", "select_fused.hip", "attn_kernels.hip"]
+SOURCES = ["qsa_api.hip", "topk_kernels.hip", "scores_kernel.hip", "attn_kernels.hip"]
 HEADERS = ["qsa_internal.h", "topk_device.h", "scores_device.h"]
 ARCH = "gfx950"
 

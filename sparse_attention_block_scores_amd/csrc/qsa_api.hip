@@ -21,9 +21,7 @@ qsa_status check_options(const qsa_options *opt)
 {
     if (!opt)
         return QSA_OK;
-    if (opt->reserved[0] != 0)
-        return QSA_EINVAL;
-    if (opt->fused_select != 0 && opt->fused_select != 1)
+    if (opt->reserved[0] != 0 || opt->reserved[1] != 0)
         return QSA_EINVAL;
     if (opt->topk_path < QSA_PATH_AUTO || opt->topk_path > QSA_PATH_ONEREAD)
         return QSA_EINVAL;
@@ -262,21 +260,6 @@ qsa_status select_call(const float *q, const float *k, const float *w, int32_t n
         return QSA_OK;
     if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < plan.lay.bytes)
         return QSA_EWORKSPACE;
-    // Small decode calls, on request: scores and top-k in one launch (it uses
-    // the first ticket word of the split's workspace). Not the default: on
-    // MI355X its cross-workgroup hand-off costs more than the kernel boundary
-    // (14.2 against 10.9 us for 3 queries x 8 heads x 1,024 blocks).
-    if (opt && opt->fused_select && call == QSA_DECODE && !active && !cells && plan.pub.path == QSA_PATH_SPLIT &&
-        fused_select_fits(nq, n_heads, n_blocks)) {
-        FusedArgs f{};
-        f.s = ScoreArgs{q, k, w, scores, ld_scores, nq, n_heads, n_blocks};
-        f.bs = block_size;
-        f.width = width;
-        f.ids = cell_ids;
-        f.counts = counts;
-        f.ticket = at<uint32_t>(workspace, plan.lay.split_tickets);
-        return launch_fused_select(f, (hipStream_t)stream) == hipSuccess ? QSA_OK : QSA_EHIP;
-    }
     if (n_blocks > 0) {
         ScoreArgs a{q, k, w, scores, ld_scores, nq, n_heads, n_blocks};
         if (launch_scores(a, (hipStream_t)stream) != hipSuccess)

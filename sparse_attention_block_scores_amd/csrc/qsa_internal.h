@@ -103,25 +103,6 @@ hipError_t launch_scores(const ScoreArgs &a, hipStream_t s);
 // The same with q and k holding BF16 values (ScoreArgs' q and k point at them).
 hipError_t launch_scores_bf16(const ScoreArgs &a, hipStream_t s);
 
-// Fused small decode-call selection (scores and top-k in one launch).
-constexpr int kFusedMaxBlocks = 1024;  // 16 keys per lane in the selecting wave
-constexpr int kFusedMaxQueries = 16;
-
-struct FusedArgs {
-    ScoreArgs s;
-    int32_t bs;
-    int32_t width;
-    int32_t *ids;
-    int32_t *counts;      // nullable
-    uint32_t *ticket;     // one word of workspace, zero between calls
-    int32_t n_tiles;      // set by the launcher
-    int32_t tiles_per_group;
-};
-
-// Whether a call of these sizes can take the fused path (host).
-bool fused_select_fits(int32_t nq, int32_t heads, int32_t n_blocks);
-hipError_t launch_fused_select(FusedArgs a, hipStream_t s);
-
 // Attention of every query head over its query's selected cells.
 constexpr int kAttnWaves = 8;             // waves per workgroup (one workgroup per CU)
 constexpr int kAttnStepCells = 32;        // cells per wave step

@@ -1,6 +1,5 @@
-// scores_device.h - the indexer block scorer's building blocks on FP32
-// matrix cores (gfx950), shared by the scorer kernel and the fused decode
-// select.
+// scores_device.h - the indexer block scorer's building blocks on FP32 and
+// BF16 matrix cores (gfx950), used by the scorer kernels.
 //
 // score[q][b] = sum_h w[q][h] * relu(dot(q[q][h][:], k[b][:])), K = 128
 // (Strata pull #1091 "qsa_select: FP32 tiled block scores below sm_80",

@@ -2,14 +2,16 @@
 //
 //  * split_kernel: the exact chunked split (Strata pull #3987, section
 //    Approach). Stage A: one workgroup per (query, chunk) loads the chunk's
-//    block keys into LDS once and keeps the chunk's own top-r blocks (block
-//    order) as candidates. A query's selection restricted to one chunk is a
-//    prefix of that chunk's order, so the candidates hold every selected
-//    block. Stage B: the workgroup that finishes a query last (an atomic
-//    ticket, no waiting) runs the same rule over the candidates and writes the
-//    cells. With one chunk the single workgroup writes the cells directly.
-//    Used for decode calls (few queries: the chunks fill the GPU) and for
-//    prompt calls too small for the one-read path.
+//    block keys into LDS once and keeps the chunk's own top-r blocks, in block
+//    order, as candidates. Every block of the query's selection is among the
+//    candidates of its chunk: if a chunk held a selected block outside its own
+//    top r, r blocks of that chunk would precede it in (key desc, block asc)
+//    order, and the selection, which has r blocks, would not reach it. Stage
+//    B: the workgroup that finishes a query last (an atomic ticket, no
+//    waiting) selects over the candidates of all chunks with the same
+//    threshold rule and writes the cells. With one chunk the single workgroup
+//    writes the cells directly. Used for rows that fit one chunk and for rows
+//    where a sampled bound would keep a large share of the blocks.
 //
 //  * oneread_kernel: the prompt path with one read of the scores (Strata
 //    pull #2093 "sm_75: the prompt path's top-k with one full read of the
@@ -842,15 +844,15 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t s)
 
 hipError_t launch_split(const SplitArgs &a, hipStream_t s)
 {
-    static bool lds_limit_raised = false;
-    if (!lds_limit_raised) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&split_kernel<kSplitThreads>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 2 * kStageBLdsWords * 4);
-        if (e != hipSuccess)
-            return e;
-        lds_limit_raised = true;
-    }
+    // Stage B may keep up to 2 * kStageBLdsWords words in dynamic LDS, above
+    // the default limit. The attribute belongs to the kernel function, so it
+    // is set once per process; the function-local static is initialised by
+    // exactly one thread (the C++ guarantee), others wait for its result.
+    static const hipError_t lds_limit = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&split_kernel<kSplitThreads>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        2 * kStageBLdsWords * 4);
+    if (lds_limit != hipSuccess)
+        return lds_limit;
     const dim3 grid((unsigned)a.n_chunks, (unsigned)a.g.nq);
     hipLaunchKernelGGL(split_kernel<kSplitThreads>, grid, dim3(kSplitThreads),
                        (size_t)(a.lds_words + a.blk_words) * 4, s, a);

@@ -100,8 +100,8 @@ def test_width_larger_than_context():
     (dict(topk_path=7), B.QSA_EINVAL),
     (dict(sample=9), B.QSA_EINVAL),
     (dict(oneread_blocks=2048), B.QSA_EUNSUPPORTED),
-    (dict(reserved=(1,)), B.QSA_EINVAL),
-    (dict(fused_select=2), B.QSA_EINVAL),
+    (dict(reserved=(1, 0)), B.QSA_EINVAL),
+    (dict(reserved=(0, 1)), B.QSA_EINVAL),
     (dict(oneread_parts=17), B.QSA_EINVAL),
     (dict(oneread_parts=-1), B.QSA_EINVAL),
 ])
