@@ -73,7 +73,9 @@ typedef enum qsa_call {
 enum {
     QSA_PATH_AUTO = 0,
     QSA_PATH_SPLIT = 1,    /* exact chunked split: per-chunk stage A, per-query stage B */
-    QSA_PATH_ONEREAD = 2   /* prompt calls: sampled bound, one read, exact fallback per query */
+    QSA_PATH_ONEREAD = 2,  /* sampled bound, one read by one workgroup per query, exact fallback */
+    QSA_PATH_FILTER = 3    /* sampled bound and one read spread over chunk workgroups (first launch),
+                              per-query selection over their candidates (second launch) */
 };
 
 /* Sampling of the one-read path's lower bound (results never depend on it). */
@@ -89,27 +91,30 @@ typedef struct qsa_options {
     int32_t topk_path;      /* QSA_PATH_* */
     int32_t chunk_blocks;   /* SPLIT chunk size in blocks: 0 = auto, else 64..15360, multiple of 4 */
     int32_t sample;         /* QSA_SAMPLE_* */
-    int32_t force_fallback; /* ONEREAD: every query takes the exact fallback over its whole row */
-    int32_t oneread_blocks; /* ONEREAD blocks streamed per batch: 0 or 16384 (others QSA_EUNSUPPORTED) */
-    int32_t oneread_parts;  /* ONEREAD workgroups per query: 0 = auto, else 1..16 */
-    int32_t reserved[2];    /* must be zero */
+    int32_t force_fallback; /* ONEREAD, FILTER: every query takes the exact path over its whole row */
+    int32_t filter_blocks;  /* FILTER chunk size in blocks: 0 = auto, else 1024, 2048, 4096 or 8192 */
+    int32_t reserved[3];    /* must be zero */
 } qsa_options;
 
 /* The launch plan the top-k would use; exported so host code and tests can
  * inspect the dispatch without a GPU. Sizes are for the largest query. */
 typedef struct qsa_topk_plan {
-    int32_t path;            /* QSA_PATH_SPLIT or QSA_PATH_ONEREAD */
+    int32_t path;            /* QSA_PATH_SPLIT, QSA_PATH_ONEREAD or QSA_PATH_FILTER */
     int32_t r_blocks;        /* blocks a full selection touches: ceil(min(width, n_blocks*bs) / bs) */
     int32_t chunk_blocks;    /* SPLIT chunk size: the fewest chunks of <= 4,104 blocks, equal sizes */
     int32_t n_chunks;        /* SPLIT chunks per query */
     int32_t split_threads;   /* SPLIT workgroup size */
     int32_t stage_b_lds;     /* 1 if stage B keeps its candidates in LDS */
     int32_t oneread_blocks;  /* ONEREAD blocks streamed per batch */
-    int32_t oneread_groups;  /* ONEREAD workgroups per query (parts of the row; >1 hands off in the workspace) */
-    int32_t cap;             /* ONEREAD candidate cap per query (blocks) */
+    int32_t cap;             /* ONEREAD, FILTER candidate cap per query (blocks) */
     int32_t sample_stride;   /* 32 */
     int32_t sample_mode;     /* QSA_SAMPLE_STRIDE or QSA_SAMPLE_LINES */
     int32_t ks;              /* sample rank of the bound: 2*r_blocks/32 + 16 */
+    int32_t filter_blocks;   /* FILTER blocks per chunk workgroup */
+    int32_t filter_chunks;   /* FILTER chunks of the longest row */
+    int32_t filter_slot;     /* FILTER candidates a chunk may keep */
+    int32_t filter_groups;   /* FILTER first-launch workgroups */
+    int32_t reserved;
     uint64_t workspace_bytes;
 } qsa_topk_plan;
 

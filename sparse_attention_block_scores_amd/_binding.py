@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "qsa.h")
 
 QSA_OK, QSA_EINVAL, QSA_EUNSUPPORTED, QSA_EWORKSPACE, QSA_EHIP = range(5)
 DECODE, PROMPT = 0, 1
-PATH_AUTO, PATH_SPLIT, PATH_ONEREAD = 0, 1, 2
+PATH_AUTO, PATH_SPLIT, PATH_ONEREAD, PATH_FILTER = 0, 1, 2, 3
 SAMPLE_AUTO, SAMPLE_STRIDE, SAMPLE_LINES = 0, 1, 2
 
 
@@ -36,9 +36,8 @@ class Options(ctypes.Structure):
         ("chunk_blocks", ctypes.c_int32),
         ("sample", ctypes.c_int32),
         ("force_fallback", ctypes.c_int32),
-        ("oneread_blocks", ctypes.c_int32),
-        ("oneread_parts", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 2),
+        ("filter_blocks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
     ]
 
 
@@ -52,11 +51,15 @@ class Plan(ctypes.Structure):
         ("split_threads", ctypes.c_int32),
         ("stage_b_lds", ctypes.c_int32),
         ("oneread_blocks", ctypes.c_int32),
-        ("oneread_groups", ctypes.c_int32),
         ("cap", ctypes.c_int32),
         ("sample_stride", ctypes.c_int32),
         ("sample_mode", ctypes.c_int32),
         ("ks", ctypes.c_int32),
+        ("filter_blocks", ctypes.c_int32),
+        ("filter_chunks", ctypes.c_int32),
+        ("filter_slot", ctypes.c_int32),
+        ("filter_groups", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_uint64),
     ]
 

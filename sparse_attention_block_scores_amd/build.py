@@ -13,8 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libqsa.so")
-SOURCES = ["qsa_api.hip", "topk_kernels.hip", "scores_kernel.hip", "attn_kernels.hip"]
-HEADERS = ["qsa_internal.h", "topk_device.h", "scores_device.h"]
+SOURCES = ["qsa_api.hip", "topk_kernels.hip", "topk_filter.hip", "scores_kernel.hip", "attn_kernels.hip"]
+HEADERS = ["qsa_internal.h", "topk_device.h", "topk_select.h", "scores_device.h"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

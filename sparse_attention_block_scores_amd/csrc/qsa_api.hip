@@ -21,9 +21,12 @@ qsa_status check_options(const qsa_options *opt)
 {
     if (!opt)
         return QSA_OK;
-    if (opt->reserved[0] != 0 || opt->reserved[1] != 0)
+    if (opt->reserved[0] != 0 || opt->reserved[1] != 0 || opt->reserved[2] != 0)
         return QSA_EINVAL;
-    if (opt->topk_path < QSA_PATH_AUTO || opt->topk_path > QSA_PATH_ONEREAD)
+    if (opt->filter_blocks != 0 && opt->filter_blocks != 1024 && opt->filter_blocks != 2048 &&
+        opt->filter_blocks != 4096 && opt->filter_blocks != 8192)
+        return QSA_EINVAL;
+    if (opt->topk_path < QSA_PATH_AUTO || opt->topk_path > QSA_PATH_FILTER)
         return QSA_EINVAL;
     if (opt->chunk_blocks != 0 &&
         (opt->chunk_blocks < kMinChunk || opt->chunk_blocks > kMaxChunk || opt->chunk_blocks % 4 != 0))
@@ -31,10 +34,6 @@ qsa_status check_options(const qsa_options *opt)
     if (opt->sample < QSA_SAMPLE_AUTO || opt->sample > QSA_SAMPLE_LINES)
         return QSA_EINVAL;
     if (opt->force_fallback != 0 && opt->force_fallback != 1)
-        return QSA_EINVAL;
-    if (opt->oneread_blocks != 0 && opt->oneread_blocks != kOneReadBatch)
-        return QSA_EUNSUPPORTED;
-    if (opt->oneread_parts < 0 || opt->oneread_parts > kOneReadMaxParts)
         return QSA_EINVAL;
     return QSA_OK;
 }
@@ -79,18 +78,37 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
     plan.cand_stride = ((int64_t)p.n_chunks * (cap_c > 0 ? cap_c : 1) + 3) / 4 * 4;
     p.stage_b_lds = plan.cand_stride <= kStageBLdsWords ? 1 : 0;
 
-    // One-read geometry: each query's row streams in batches of blocks, by
-    // one workgroup, or by several parts (one workgroup each) that hand their
-    // candidates to the last of them. Parts are opt-in: measured on MI355X,
-    // the hand-off (device-coherent stores, a ticket, one load round trip
-    // per part) costs about what the shorter stream saves at the decode
-    // contexts.
+    // One-read geometry: one workgroup streams each query's row in batches of
+    // blocks (one slice per wave).
     p.oneread_blocks = kOneReadBatch;
-    p.oneread_groups = (opt && opt->oneread_parts) ? opt->oneread_parts : 1;
     p.cap = kOneReadCap;
     p.sample_stride = kSampleStride;
     p.sample_mode = (opt && opt->sample) ? opt->sample : QSA_SAMPLE_LINES;
     p.ks = 2 * p.r_blocks / kSampleStride + 16;
+
+    // Filtered split geometry: chunks of 1,024-8,192 blocks, the largest size
+    // that still gives about kFilterTargetGroups first-launch workgroups (or
+    // the forced size), at most kFilterMaxChunks chunks per row. A chunk's
+    // slot holds up to twice an even share of the candidate cap (at least
+    // 512), so a row whose candidates fit the cap overflows no slot unless
+    // they crowd into a few chunks.
+    {
+        int32_t fb = kFilterMaxChunk;
+        if (opt && opt->filter_blocks) {
+            fb = opt->filter_blocks;
+        } else {
+            const int64_t nb = n_blocks > 0 ? n_blocks : 1;
+            while (fb > kFilterMinChunk && (int64_t)nq * ((nb + fb - 1) / fb) < kFilterTargetGroups)
+                fb /= 2;
+        }
+        p.filter_blocks = fb;
+        p.filter_chunks = n_blocks > 0 ? (int32_t)(((int64_t)n_blocks + fb - 1) / fb) : 1;
+        const int32_t share = (2 * kOneReadCap + p.filter_chunks - 1) / p.filter_chunks;
+        int32_t slot = (share + 63) / 64 * 64;
+        slot = slot < 512 ? 512 : slot;
+        p.filter_slot = slot < fb ? slot : fb;
+        p.filter_groups = (int32_t)((int64_t)nq * p.filter_chunks);
+    }
 
     // Dispatch (measured on MI355X; results never depend on it). A row that
     // fits one chunk is selected in LDS by one workgroup. Longer rows take the
@@ -103,6 +121,8 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
                    : QSA_PATH_SPLIT;
     if (path == QSA_PATH_ONEREAD && n_blocks > kOneReadMaxBatches * kOneReadBatch)
         path = QSA_PATH_SPLIT;  // per-batch counts of longer rows do not fit the LDS table
+    if (path == QSA_PATH_FILTER && p.filter_chunks > kFilterMaxChunks)
+        path = QSA_PATH_SPLIT;  // stage B scans at most kFilterMaxChunks chunk headers
     p.path = path;
 
     // Workspace: only the split keeps candidates in global memory.
@@ -113,10 +133,10 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
         L.split_tickets = off; off = align_up(off + q * 4);
         L.split_keys = off;    off = align_up(off + q * (size_t)plan.cand_stride * 4);
         L.split_blocks = off;  off = align_up(off + q * (size_t)plan.cand_stride * 4);
-    } else if (p.oneread_groups > 1) {
+    } else if (path == QSA_PATH_FILTER) {
         const size_t q = (size_t)(nq > 0 ? nq : 1);
-        L.part_tickets = off; off = align_up(off + q * 4);
-        L.part_slots = off;   off = align_up(off + q * (size_t)p.oneread_groups * kPartWords * 4);
+        L.filter_heads = off; off = align_up(off + q * (size_t)p.filter_chunks * 16);
+        L.filter_slots = off; off = align_up(off + q * (size_t)p.filter_chunks * 2 * (size_t)p.filter_slot * 4);
     } else {
         off = kAlign;  // nothing is kept; a minimal non-empty workspace
     }
@@ -169,14 +189,24 @@ qsa_status run_topk(const TopkGeom &g, const TopkPlan &plan, void *ws, hipStream
                     const qsa_options *opt)
 {
     const qsa_topk_plan &p = plan.pub;
+    if (p.path == QSA_PATH_FILTER) {
+        FilterArgs fa;
+        fa.g = g;
+        fa.heads = at<uint32_t>(ws, plan.lay.filter_heads);
+        fa.slots = at<uint32_t>(ws, plan.lay.filter_slots);
+        fa.chunk = p.filter_blocks;
+        fa.n_chunks = p.filter_chunks;
+        fa.slot = p.filter_slot;
+        fa.mode = p.sample_mode;
+        fa.force_flag = (opt && opt->force_fallback) ? 1 : 0;
+        fa.xcd = (g.nq % 8 == 0) ? 1 : 0;
+        return launch_filter(fa, s) == hipSuccess ? QSA_OK : QSA_EHIP;
+    }
     if (p.path == QSA_PATH_ONEREAD) {
         OneReadArgs oa;
         oa.g = g;
         oa.mode = p.sample_mode;
         oa.force_flag = (opt && opt->force_fallback) ? 1 : 0;
-        oa.parts = p.oneread_groups;
-        oa.part_tickets = p.oneread_groups > 1 ? at<uint32_t>(ws, plan.lay.part_tickets) : nullptr;
-        oa.part_ws = p.oneread_groups > 1 ? at<uint32_t>(ws, plan.lay.part_slots) : nullptr;
         return launch_oneread(oa, s) == hipSuccess ? QSA_OK : QSA_EHIP;
     }
     const TopkLayout &L = plan.lay;

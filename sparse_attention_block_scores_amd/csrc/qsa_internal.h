@@ -23,18 +23,25 @@ constexpr int kMaxChunk = 15360;          // keeps a chunk's keys under 60 KB of
 constexpr int kStageBLdsWords = 15360;    // stage B keeps up to this many candidates (keys and blocks) in LDS
 constexpr int kOneReadCap = 8192;         // one-read candidate cap per query (blocks)
 constexpr int kOneReadSample = 4096;      // one-read sample: at most this many keys
-constexpr int kPartWords = 4 + 2 * kOneReadCap;  // one-read hand-off slot per part (u32 words)
-constexpr int kOneReadMaxParts = 16;
 constexpr int kOneReadMinRatio = 16;      // one-read when n_blocks >= this many times r_blocks ...
 constexpr int kSampleStride = 32;
+
+// Two-launch filtered split: stage A filters chunks of a row by the sampled
+// bound (one 256-thread workgroup per chunk), stage B selects per query.
+constexpr int kFilterThreads = 256;
+constexpr int kFilterMinChunk = 1024;     // blocks per stage-A chunk: 1024 * (1, 2, 4 or 8)
+constexpr int kFilterMaxChunk = 8192;
+constexpr int kFilterMaxChunks = 1024;    // chunks per row (stage B scans one header per thread)
+constexpr int kFilterTargetGroups = 1024; // stage-A workgroups the chunk size aims for
+constexpr uint32_t kFilterOverflow = 0xFFFFFFFFu;  // header count of a chunk whose slot overflowed
 
 // Workspace layout of the split (byte offsets, 256-byte aligned).
 struct TopkLayout {
     size_t split_tickets;   // u32 [nq]
     size_t split_keys;      // u32 [nq][cand_stride]
     size_t split_blocks;    // i32 [nq][cand_stride]
-    size_t part_tickets;    // u32 [nq]             (one-read with several parts)
-    size_t part_slots;      // u32 [nq][parts][kPartWords]
+    size_t filter_heads;    // u32 [nq][n_chunks][4]  (filtered split)
+    size_t filter_slots;    // u32 [nq][n_chunks][2][slot]
     size_t bytes;
 };
 
@@ -76,14 +83,24 @@ struct SplitArgs {
 
 struct OneReadArgs {
     TopkGeom g;
-    int32_t parts;          // workgroups per query (part = a range of slices)
-    uint32_t *part_tickets; // [nq], zero between calls (parts > 1)
-    uint32_t *part_ws;      // [nq][parts][kPartWords] hand-off slots (parts > 1)
     int32_t mode;           // QSA_SAMPLE_STRIDE / QSA_SAMPLE_LINES
     int32_t force_flag;     // take the exact path for every query
 };
 
+struct FilterArgs {
+    TopkGeom g;
+    uint32_t *heads;        // [nq][n_chunks] x {count or kFilterOverflow, min key, max key, bound key}
+    uint32_t *slots;        // [nq][n_chunks][2][slot]: candidate keys, then their block indices
+    int32_t chunk;          // blocks per chunk
+    int32_t n_chunks;       // chunks of the longest row
+    int32_t slot;           // candidates a chunk may keep
+    int32_t mode;           // QSA_SAMPLE_STRIDE / QSA_SAMPLE_LINES
+    int32_t force_flag;     // every query takes the exact fallback
+    int32_t xcd;            // 1: the chunks of a query run on one XCD (nq a multiple of 8)
+};
+
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+hipError_t launch_filter(const FilterArgs &a, hipStream_t s);
 hipError_t launch_split(const SplitArgs &a, hipStream_t s);
 hipError_t launch_oneread(const OneReadArgs &a, hipStream_t s);
 

@@ -192,21 +192,22 @@ constexpr int kFineBits = 11;                        // fine bins: 2,048 ...
 constexpr int kFineBins = 1 << kFineBits;
 constexpr int kFinePerCoarse = kFineBins / kBins;    // ... in 256 coarse bins of 8
 
-template <int NT>
+// LDS state of a selection, sized for workgroups of up to 16 waves.
 struct SelectShared {
-    static constexpr int NW = NT / kWave;
+    static constexpr int NW = 16;
     alignas(16) uint32_t hist[3][kBins];  // rotating: fill one, pick from it, clear the one before
     alignas(16) uint32_t fine[kFineBins];
     alignas(16) uint32_t coarse[kBins];
     uint32_t small[kWave];                // keys of one fine bin
     uint32_t small_n;
+    uint32_t bcast;                       // one value from one wave to all
     uint32_t red[2][NW];
     uint32_t wave_ties[NW];
     uint32_t wave_gts[NW];
 };
 
 template <int NT>
-__device__ __forceinline__ void clear_fine(SelectShared<NT> &sh)
+__device__ __forceinline__ void clear_fine(SelectShared &sh)
 {
     uint4 *f = reinterpret_cast<uint4 *>(sh.fine);
     for (int i = threadIdx.x; i < kFineBins / 4; i += NT)
@@ -218,7 +219,7 @@ __device__ __forceinline__ void clear_fine(SelectShared<NT> &sh)
 
 // Every histogram and counter of sh to zero (a barrier must follow).
 template <int NT>
-__device__ __forceinline__ void clear_hists(SelectShared<NT> &sh)
+__device__ __forceinline__ void clear_hists(SelectShared &sh)
 {
     uint4 *h = reinterpret_cast<uint4 *>(&sh.hist[0][0]);
     for (int i = threadIdx.x; i < 3 * kBins / 4; i += NT)
@@ -229,7 +230,7 @@ __device__ __forceinline__ void clear_hists(SelectShared<NT> &sh)
 }
 
 template <int NT>
-__device__ __forceinline__ void clear_hist(SelectShared<NT> &sh, int which)
+__device__ __forceinline__ void clear_hist(SelectShared &sh, int which)
 {
     uint4 *h = reinterpret_cast<uint4 *>(&sh.hist[which][0]);
     for (int i = threadIdx.x; i < kBins / 4; i += NT)
@@ -238,7 +239,7 @@ __device__ __forceinline__ void clear_hist(SelectShared<NT> &sh, int which)
 
 // Workgroup min and max of a per-thread pair (all threads call).
 template <int NT>
-__device__ __forceinline__ void wg_minmax(uint32_t lo, uint32_t hi, SelectShared<NT> &sh, uint32_t &mn,
+__device__ __forceinline__ void wg_minmax(uint32_t lo, uint32_t hi, SelectShared &sh, uint32_t &mn,
                                           uint32_t &mx)
 {
     constexpr int NW = NT / kWave;
@@ -300,7 +301,7 @@ __device__ __forceinline__ void wave_pick(const uint32_t *hist, uint32_t r, uint
 // lies in coarse bin f / kFinePerCoarse): its index, its count, and the count
 // of everything in higher fine bins. Every wave computes it on its own.
 template <int NT>
-__device__ __forceinline__ void pick_fine(const SelectShared<NT> &sh, uint32_t r, uint32_t &fb, uint32_t &c,
+__device__ __forceinline__ void pick_fine(const SelectShared &sh, uint32_t r, uint32_t &fb, uint32_t &c,
                                           uint32_t &above)
 {
     uint32_t cb, h;
@@ -355,7 +356,7 @@ __device__ __forceinline__ void wave_rank_small(const uint32_t *keys, uint32_t c
 // barrier.
 template <int NT, class Src, class Member>
 __device__ __forceinline__ void rank_members(const Src &src, int n, Member member, uint32_t c, uint32_t rank,
-                                             SelectShared<NT> &sh, uint32_t &T, uint32_t &n_above)
+                                             SelectShared &sh, uint32_t &T, uint32_t &n_above)
 {
     for_each_key<NT>(src, n, [&](uint32_t k) {
         if (member(k)) {
@@ -385,7 +386,7 @@ __device__ __forceinline__ int first_digit_shift(uint32_t span)
 // histogram filled two passes earlier is cleared while the next one fills.
 template <int NT, class Src>
 __device__ __forceinline__ void radix_select_range(const Src &src, int n, uint32_t rank, uint32_t kmin,
-                                                   uint32_t kmax, SelectShared<NT> &sh, uint32_t &T,
+                                                   uint32_t kmax, SelectShared &sh, uint32_t &T,
                                                    uint32_t &n_above)
 {
     uint32_t lo = kmin, span = kmax - kmin, r = rank, above = 0;
@@ -418,7 +419,7 @@ __device__ __forceinline__ void radix_select_range(const Src &src, int n, uint32
 
 // Sum over the workgroup of one value per thread (all threads call).
 template <int NT>
-__device__ __forceinline__ uint32_t wg_sum(uint32_t v, SelectShared<NT> &sh)
+__device__ __forceinline__ uint32_t wg_sum(uint32_t v, SelectShared &sh)
 {
     constexpr int NW = NT / kWave;
     v = wave_sum(v);
@@ -435,7 +436,7 @@ __device__ __forceinline__ uint32_t wg_sum(uint32_t v, SelectShared<NT> &sh)
 
 // Number of keys of src[0..n) that are >= kp (all threads call).
 template <int NT, class Src>
-__device__ __forceinline__ uint32_t count_at_least(const Src &src, int n, uint32_t kp, SelectShared<NT> &sh)
+__device__ __forceinline__ uint32_t count_at_least(const Src &src, int n, uint32_t kp, SelectShared &sh)
 {
     uint32_t c = 0;
     for_each_key<NT>(src, n, [&](uint32_t k) { c += k >= kp ? 1u : 0u; });
@@ -444,7 +445,7 @@ __device__ __forceinline__ uint32_t count_at_least(const Src &src, int n, uint32
 
 // Min and max key of src[0..n).
 template <int NT, class Src>
-__device__ __forceinline__ void key_range(const Src &src, int n, SelectShared<NT> &sh, uint32_t &mn, uint32_t &mx)
+__device__ __forceinline__ void key_range(const Src &src, int n, SelectShared &sh, uint32_t &mn, uint32_t &mx)
 {
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
     for_each_key<NT>(src, n, [&](uint32_t k) {
@@ -465,7 +466,7 @@ __device__ __forceinline__ uint32_t value_fine_bin(uint32_t k, float lh, float i
     return (uint32_t)min(kFineBins - 1, max(0, (int)t));
 }
 
-// Rank-th largest key of src (see radix_select_range) without a known range.
+// Rank-th largest key of src (see radix_select_range) among keys in [mn, mx].
 // Ranges of more than 2^16 keys take one pass of 2,048 fine bins (in 256
 // coarse ones) instead of 8-bit digits. Up to 2^27 keys (a few binades) the
 // fine bins are the top bits of (key - min); wider ranges, such as signed
@@ -474,11 +475,9 @@ __device__ __forceinline__ uint32_t value_fine_bin(uint32_t k, float lh, float i
 // that holds the rank usually holds a handful of keys, which one wave ranks
 // exactly; a crowded one is an interval of keys, which radix digits finish.
 template <int NT, class Src>
-__device__ __forceinline__ void radix_select(const Src &src, int n, uint32_t rank, SelectShared<NT> &sh,
-                                             uint32_t &T, uint32_t &n_above)
+__device__ __forceinline__ void radix_select_in(const Src &src, int n, uint32_t rank, uint32_t mn, uint32_t mx,
+                                                SelectShared &sh, uint32_t &T, uint32_t &n_above)
 {
-    uint32_t mn, mx;
-    key_range<NT>(src, n, sh, mn, mx);
     const uint32_t span = mx - mn;
     const float lo = float_of(mn), hi = float_of(mx);
     const float lh = 0.5f * lo, d2 = 0.5f * hi - lh;
@@ -522,6 +521,16 @@ __device__ __forceinline__ void radix_select(const Src &src, int n, uint32_t ran
     n_above = h + a2;
 }
 
+// radix_select_in over the keys' own range, found with one pass.
+template <int NT, class Src>
+__device__ __forceinline__ void radix_select(const Src &src, int n, uint32_t rank, SelectShared &sh,
+                                             uint32_t &T, uint32_t &n_above)
+{
+    uint32_t mn, mx;
+    key_range<NT>(src, n, sh, mn, mx);
+    radix_select_in<NT>(src, n, rank, mn, mx, sh, T, n_above);
+}
+
 // Walk items 0..n-1 in order and take every item with key > T plus the first
 // `tie_budget` items with key == T (tie_budget >= 1). Taken item i gets the
 // output slot `first` (a running sum of weights: `unit` per taken item, except
@@ -530,7 +539,7 @@ __device__ __forceinline__ void radix_select(const Src &src, int n, uint32_t ran
 // (four per lane); the only workgroup exchange is one round of per-wave counts.
 template <int NT, class Src, class Emit>
 __device__ __forceinline__ void ordered_take(const Src &src, int n, uint32_t T, uint32_t tie_budget, uint32_t unit,
-                             uint32_t last_unit, SelectShared<NT> &sh, Emit emit)
+                             uint32_t last_unit, SelectShared &sh, Emit emit)
 {
     constexpr int NW = NT / kWave;
     constexpr int STEP = 4 * kWave;
@@ -654,7 +663,7 @@ __device__ __forceinline__ void ordered_take(const Src &src, int n, uint32_t T, 
 // barrier.
 template <int NT, int PER, class Src, class Emit>
 __device__ __forceinline__ void take_in_order(const Src &src, int n, uint32_t T, uint32_t tie_budget,
-                                              uint32_t unit, uint32_t last_unit, SelectShared<NT> &sh, Emit emit)
+                                              uint32_t unit, uint32_t last_unit, SelectShared &sh, Emit emit)
 {
     static_assert(PER % 4 == 0, "16-byte loads of each thread's items");
     constexpr int NW = NT / kWave;
@@ -718,7 +727,7 @@ __device__ __forceinline__ void take_in_order(const Src &src, int n, uint32_t T,
 // walked in ranges (ordered_take).
 template <int NT, class Src, class Emit>
 __device__ __forceinline__ void take_ordered(const Src &src, int n, uint32_t T, uint32_t tie_budget, uint32_t unit,
-                                             uint32_t last_unit, SelectShared<NT> &sh, Emit emit)
+                                             uint32_t last_unit, SelectShared &sh, Emit emit)
 {
     if (n <= 8 * NT)
         take_in_order<NT, 8>(src, n, T, tie_budget, unit, last_unit, sh, emit);

@@ -28,6 +28,7 @@
 
 #include "qsa_internal.h"
 #include "topk_device.h"
+#include "topk_select.h"
 
 namespace qsa {
 
@@ -36,106 +37,6 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 
-// Hand-off slot of one one-read part: {count, largest key, 2 unused}, then
-// kOneReadCap keys and kOneReadCap blocks (16-byte aligned sections).
-constexpr int kPartHeader = 4;
-
-struct QuerySel {
-    int n_vis;      // visible blocks
-    int wq;         // cells selected: min(width, visible cells)
-    int r;          // blocks the selection touches, every block taken whole
-    int last_unit;  // cells of the last block in (key desc, block asc) order
-    int tail;       // cells of the last visible block when it is partial, else 0
-};
-
-// r and last_unit of a selection of w cells from whole blocks of bs cells.
-__device__ __forceinline__ void set_width(QuerySel &s, int w, int bs)
-{
-    s.r = (w + bs - 1) / bs;
-    s.last_unit = s.r > 0 ? w - bs * (s.r - 1) : 0;
-}
-
-__device__ __forceinline__ QuerySel query_sel(const TopkGeom &g, int q)
-{
-    QuerySel s;
-    int64_t cells;
-    if (g.cells) {
-        const int64_t all = (int64_t)g.n_blocks * g.bs;
-        const int64_t c = g.cells[q];
-        cells = c < 0 ? 0 : (c > all ? all : c);
-        s.n_vis = (int)((cells + g.bs - 1) / g.bs);
-        s.tail = (int)(cells % g.bs);
-    } else {
-        int nv = g.n_blocks;
-        if (g.active) {
-            const int a = g.active[q];
-            nv = a < 0 ? 0 : (a > g.n_blocks ? g.n_blocks : a);
-        }
-        s.n_vis = nv;
-        s.tail = 0;
-        cells = (int64_t)nv * g.bs;
-    }
-    s.wq = (int)(cells < g.width ? cells : (int64_t)g.width);
-    set_width(s, s.wq, g.bs);
-    return s;
-}
-
-// A partial last visible block p (qs.tail cells). Counted as a whole block,
-// p is the last of the blocks with its key in (key desc, block asc) order, so
-// whole-block cells precede it exactly for the n_ge - 1 other blocks with key
-// >= key(p). If fewer than wq such cells precede it, p is taken, and the
-// selection is the whole-block selection of wq + bs - tail cells cut to its
-// first wq cells in cell order (p's cells past the visible ones are the
-// highest ids); otherwise p is not taken and the whole-block selection of wq
-// cells is the selection. Every emit writes at most qs.wq cells.
-__device__ __forceinline__ void widen_for_tail(QuerySel &qs, int bs, uint32_t n_ge)
-{
-    if (qs.tail != 0 && n_ge >= 1 && (int64_t)(n_ge - 1) * bs < qs.wq)
-        set_width(qs, qs.wq + bs - qs.tail, bs);
-}
-
-template <int NT>
-__device__ __forceinline__ void write_empty(const TopkGeom &g, int q)
-{
-    int32_t *out = g.ids + (int64_t)q * g.width;
-    for (int p = threadIdx.x; p < g.width; p += NT)
-        out[p] = -1;
-    if (g.counts && threadIdx.x == 0)
-        g.counts[q] = 0;
-}
-
-// Writes a query's selection from n candidate blocks in ascending block order
-// that contain it, given T (the r-th largest candidate key) and the number of
-// candidates above T: the cells, the -1 tail and the count.
-template <int NT, class Src, class BlockAt>
-__device__ __forceinline__ void emit_selection(const Src &src, int n, const QuerySel &qs, BlockAt block_at,
-                                               const TopkGeom &g, int q, SelectShared<NT> &sh, uint32_t T,
-                                               uint32_t above)
-{
-    int32_t *out = g.ids + (int64_t)q * g.width;
-    const int bs = g.bs;
-    const uint32_t limit = (uint32_t)qs.wq;
-    take_ordered<NT>(src, n, T, (uint32_t)qs.r - above, (uint32_t)bs, (uint32_t)qs.last_unit, sh,
-                     [&](int i, uint32_t first, uint32_t cnt) {
-                         write_cells(out, first, cnt, block_at(i) * bs, limit);
-                     });
-    for (int p = qs.wq + (int)threadIdx.x; p < g.width; p += NT)
-        out[p] = -1;
-    if (g.counts && threadIdx.x == 0)
-        g.counts[q] = qs.wq;
-}
-
-// Final selection over n candidate blocks (n >= qs.r) that contain the
-// query's whole selection, in ascending block order: writes the cells, the -1
-// tail and the count. Histograms must be zero on entry.
-template <int NT, class Src, class BlockAt>
-__device__ __forceinline__ void select_cells(const Src &src, int n, const QuerySel &qs, BlockAt block_at,
-                                             const TopkGeom &g, int q, SelectShared<NT> &sh)
-{
-    uint32_t T, above;
-    radix_select<NT>(src, n, (uint32_t)qs.r, sh, T, above);
-    emit_selection<NT>(src, n, qs, block_at, g, q, sh, T, above);
-}
 
 // Keys of blocks [b0, b0+n) of row q into LDS.
 template <int NT>
@@ -169,7 +70,7 @@ template <int NT>
 __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint32_t s_keys[];
-    __shared__ SelectShared<NT> sh;
+    __shared__ SelectShared sh;
     __shared__ uint32_t s_flag[1];
     const TopkGeom g = a.g;
     const int q = blockIdx.y;
@@ -177,7 +78,7 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
     QuerySel qs = query_sel(g, q);
     if (qs.r == 0) {
         if (c == 0)
-            write_empty<NT>(g, q);
+            write_first_cells<NT>(g, q, 0);
         return;
     }
     const int nchq = (qs.n_vis + a.chunk - 1) / a.chunk;
@@ -267,66 +168,6 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
 }
 
 // ------------------------------------------------------------------ one read
-// Lower bound for the one-read filter from a sample of the row (SPT values per
-// thread, sample index threadIdx.x + u*NT, valid below ns). The pages take the
-// KS-th largest sample key. Here the sample's value range is cut into 256
-// equal bins and the bound is the lower edge of the bin holding the KS-th
-// largest sample value; a bin that holds more than KS/2 samples is cut again,
-// at most three levels deep. Any bound gives the exact result (the kept blocks
-// either hold the selection or the row takes the exact path), so the bound
-// only steers how many blocks the stream keeps. Bins of equal value width
-// spread normal-like data evenly, where digits of the key bits would pile a
-// quarter of the sample onto one LDS counter.
-// Uses sh.hist[0..2] (zero on entry) and leaves them dirty; ends with a
-// barrier after the last read of them.
-template <int NT, int SPT>
-__device__ __forceinline__ float sample_bound(const float (&smp)[SPT], int ns, uint32_t ks, SelectShared<NT> &sh)
-{
-    bool in[SPT];
-    uint32_t klo = 0xFFFFFFFFu, khi = 0u;
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-        in[u] = (int)threadIdx.x + u * NT < ns;
-        const uint32_t k = key_of(smp[u]);
-        klo = in[u] ? min(klo, k) : klo;
-        khi = in[u] ? max(khi, k) : khi;
-    }
-    uint32_t mn, mx;
-    wg_minmax<NT>(klo, khi, sh, mn, mx);
-    float lo = float_of(mn), hi = float_of(mx);
-    uint32_t r = ks;
-    for (int level = 0; level < 3; ++level) {
-        // Halved operands keep the width finite for any finite range.
-        const float lh = 0.5f * lo, d2 = 0.5f * hi - lh;
-        const float inv = 256.0f / d2;
-        if (!(d2 > 0.0f) || !(inv < __builtin_inff()))
-            break;  // nothing left to cut
-        uint32_t *hist = sh.hist[level];
-        int bin[SPT];
-#pragma unroll
-        for (int u = 0; u < SPT; ++u) {
-            bin[u] = min(255, max(0, (int)((0.5f * smp[u] - lh) * inv)));
-            if (in[u])
-                hist_add(hist, (uint32_t)bin[u]);
-        }
-        lds_barrier();
-        uint32_t b, h;
-        wave_pick(hist, r, b, h);
-        const uint32_t cnt = hist[b];
-        const float step = d2 * (1.0f / 256.0f);
-        lo = 2.0f * (lh + (float)b * step);
-        if (cnt <= ks / 2 || level == 2)
-            break;
-        hi = 2.0f * (lh + (float)(b + 1) * step);
-        r -= h;
-#pragma unroll
-        for (int u = 0; u < SPT; ++u)
-            in[u] = in[u] && bin[u] == (int)b;
-    }
-    lds_barrier();  // every wave is done reading the histograms
-    return lo;
-}
-
 // The workgroup streams the row in slices of STEP blocks, F4 float4 loads per
 // lane and kOneReadBuffers slices in flight per wave. The first slices are
 // dealt out in order; after that a wave claims the next slice from an LDS
@@ -343,28 +184,30 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     constexpr int STEP = kWave * 4 * F4;                  // blocks per slice
     constexpr int MAXS = kOneReadMaxBatches * NW;         // slices of the longest row taken here
     constexpr int WCAP = kOneReadCap / NW;                // candidates a wave may keep
+    constexpr int SPT = kOneReadSample / NT;              // sample keys per thread
     static_assert(kOneReadBatch == NW * STEP, "a batch is one slice per wave");
     __shared__ __attribute__((aligned(16))) uint32_t s_wkey[kOneReadCap];  // per-wave candidates: FP32 bits
     __shared__ __attribute__((aligned(16))) int32_t s_wblk[kOneReadCap];
     __shared__ __attribute__((aligned(16))) uint32_t s_ckey[kOneReadCap];  // candidates in block order
     __shared__ __attribute__((aligned(16))) int32_t s_cblk[kOneReadCap];
-    __shared__ SelectShared<NT> sh;
+    __shared__ SelectShared sh;
     __shared__ uint32_t s_scnt[MAXS];   // per slice: candidates kept ...
     __shared__ uint32_t s_ssrc[MAXS];   // ... where they start in the list of ...
     __shared__ uint32_t s_swave[MAXS];  // ... this wave
     __shared__ uint32_t s_next;         // next slice to claim
-    __shared__ uint32_t s_gcnt[NW];     // candidates at or above a partial last block's key
     __shared__ uint32_t s_wtot[NW];
     __shared__ uint32_t s_wmax[NW];
-    __shared__ uint32_t s_flag[1];
+    __shared__ uint32_t s_wmin[NW];
 
     const TopkGeom g = a.g;
-    const int q = blockIdx.x / a.parts;
-    const int part = blockIdx.x - q * a.parts;
+    const int q = blockIdx.x;
     QuerySel qs = query_sel(g, q);
     if (qs.r == 0) {
-        if (part == 0)
-            write_empty<NT>(g, q);
+        write_first_cells<NT>(g, q, 0);
+        return;
+    }
+    if (visible_cells(qs, g.bs) <= qs.wq) {
+        write_first_cells<NT>(g, q, qs.wq);  // every visible cell
         return;
     }
     const int n = qs.n_vis;
@@ -374,33 +217,9 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     // candidates must hold in that case: the selection may take it whole.
     const uint32_t kp = qs.tail != 0 ? key_of(row[n - 1]) : 0u;
     const int64_t w_need = (int64_t)qs.wq + (qs.tail != 0 ? g.bs - qs.tail : 0);
-
-    // Sample of the block keys for the bound.
-    int ns;
-    if (a.mode == QSA_SAMPLE_STRIDE) {
-        ns = (n + kSampleStride - 1) / kSampleStride;
-    } else {
-        const int full = n / 1024, rem = n % 1024;
-        ns = full * kSampleStride + min(rem, kSampleStride);
-    }
-    ns = min(ns, kOneReadSample);
-    const uint32_t ks = 2u * (uint32_t)qs.r / kSampleStride + 16u;
-    const bool all_cells = (int64_t)n * g.bs <= (int64_t)qs.wq;
-    const bool use_bound = !all_cells && !a.force_flag && (uint32_t)ns >= ks;
-    // Parts: the row's slices split evenly over the workgroups of the query
-    // (a query without a bound is one part). Each part streams its own range
-    // behind the same bound and hands its candidates to the part that
-    // finishes last, which selects over all of them.
-    const int rslices = (n + STEP - 1) / STEP;
-    const int sper0 = (rslices + min(a.parts, rslices) - 1) / min(a.parts, rslices);
-    const int sper = use_bound ? sper0 : rslices;
-    const int nparts = (rslices + sper - 1) / sper;
-    if (part >= nparts)
-        return;
-    const int p0 = part * sper * STEP;                  // first block of this part
-    const int np = min(n, (part + 1) * sper * STEP) - p0;  // blocks of this part
-    const float *prow = row + p0;
-    const int nslices = (np + STEP - 1) / STEP;  // <= MAXS (the dispatch sees to it)
+    const SampleGeom sg = sample_geom(n, qs.r, a.mode);
+    const bool use_bound = !a.force_flag && (uint32_t)sg.ns >= sg.ks;
+    const int nslices = (n + STEP - 1) / STEP;  // <= MAXS (the dispatch sees to it)
 
     // Every load below is unconditional: a lane with nothing to read re-reads
     // block 0 (the row has at least one visible block here) and the value is
@@ -412,13 +231,13 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             const int i0 = sl * STEP + j * 4 * kWave + 4 * lane;
             if constexpr (VEC) {
                 // Streamed once: nontemporal loads keep it from displacing cached data.
-                const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(prow + (i0 < np ? i0 : 0)));
+                const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + (i0 < n ? i0 : 0)));
                 v[j] = make_float4(t[0], t[1], t[2], t[3]);
             } else {
-                v[j].x = prow[i0 < np ? i0 : 0];
-                v[j].y = prow[i0 + 1 < np ? i0 + 1 : 0];
-                v[j].z = prow[i0 + 2 < np ? i0 + 2 : 0];
-                v[j].w = prow[i0 + 3 < np ? i0 + 3 : 0];
+                v[j].x = row[i0 < n ? i0 : 0];
+                v[j].y = row[i0 + 1 < n ? i0 + 1 : 0];
+                v[j].z = row[i0 + 2 < n ? i0 + 2 : 0];
+                v[j].w = row[i0 + 3 < n ? i0 + 3 : 0];
             }
             // Issue order = use order: loads complete in order, so a load
             // the scheduler moved ahead would make the first use wait for it.
@@ -427,16 +246,13 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     };
 
     // The sample goes into registers first (SPT per thread), then the first
-    // NBUF slices of every wave are issued behind it.
-    constexpr int SPT = kOneReadSample / NT;
+    // slice of every wave is issued behind it: a wave stalls while the memory
+    // queue is full, and the bound needs every wave.
     float smp[SPT];
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
         const int i = (int)threadIdx.x + u * NT;
-        const int ic = (use_bound && i < ns) ? i : 0;
-        const int b = a.mode == QSA_SAMPLE_STRIDE ? ic * kSampleStride
-                                                  : (ic / kSampleStride) * 1024 + (ic % kSampleStride);
-        smp[u] = row[b];
+        smp[u] = row[sample_block(sg, (use_bound && i < sg.ns) ? i : 0)];
     }
     clear_hists<NT>(sh);
     float4 buf[NBUF][F4];
@@ -444,8 +260,6 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
 #pragma unroll
     for (int u = 0; u < NBUF; ++u)
         cs[u] = u * NW + wid;
-    // Only the first slice goes out before the bound: a wave stalls while
-    // the memory queue is full, and the bound needs every wave.
     load_slice(cs[0], buf[0]);
     if (threadIdx.x == 0)
         s_next = NBUF * NW;
@@ -453,16 +267,16 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     // One read: keep blocks with value >= fbound (every block without a
     // bound), in block order, up to WCAP per wave. The key map preserves order
     // and equates -0.0 with +0.0, exactly as float comparison does, so the
-    // kept keys are those >= key_of(fbound); keys must be finite, so the
-    // largest kept float has the largest key.
-    const float fbound = use_bound ? sample_bound<NT>(smp, ns, ks, sh) : -__builtin_inff();
-    clear_hists<NT>(sh);  // ordered before their next use by the barrier after the stream
+    // kept keys are those >= key_of(fbound).
+    const float fbound = use_bound ? bound_from_sample<NT, SPT>(smp, sg.ns, sg.ks, sh) : -__builtin_inff();
+    clear_fine<NT>(sh);  // ordered before the selection by the barrier after the stream
 #pragma unroll
     for (int u = 1; u < NBUF; ++u)
         load_slice(cs[u], buf[u]);
 
     uint32_t wcnt = 0;               // wave-uniform
-    float fmx = -__builtin_inff();   // largest value this lane kept
+    float fmx = -__builtin_inff();   // largest and smallest value this lane kept
+    float fmn = __builtin_inff();
     uint32_t *wkey = s_wkey + wid * WCAP;
     int32_t *wblk = s_wblk + wid * WCAP;
     auto consume = [&](int sl, const float4 (&v)[F4], auto full_tag) {
@@ -477,7 +291,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             uint64_t m[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                keep[s] = f[s] >= fbound && (FULL || i0 + s < np);
+                keep[s] = f[s] >= fbound && (FULL || i0 + s < n);
                 m[s] = __ballot(keep[s]);
             }
             const uint64_t any = m[0] | m[1] | m[2] | m[3];
@@ -494,8 +308,9 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
                     const int sel = keep[0] ? 0 : (keep[1] ? 1 : (keep[2] ? 2 : 3));
                     const uint32_t pos = min(wcnt + count_below(any), (uint32_t)(WCAP - 1));
                     wkey[pos] = __float_as_uint(x);
-                    wblk[pos] = p0 + i0 + sel;
+                    wblk[pos] = i0 + sel;
                     fmx = x > fmx ? x : fmx;
+                    fmn = x < fmn ? x : fmn;
                 }
                 wcnt += (uint32_t)__popcll(any);
                 continue;
@@ -512,8 +327,9 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
                 if (keep[s]) {
                     const uint32_t p = min(pos, (uint32_t)(WCAP - 1));
                     wkey[p] = __float_as_uint(f[s]);
-                    wblk[p] = p0 + i0 + s;
+                    wblk[p] = i0 + s;
                     fmx = f[s] > fmx ? f[s] : fmx;
+                    fmn = f[s] < fmn ? f[s] : fmn;
                     ++pos;
                 }
             }
@@ -537,7 +353,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             if (lane == 0)
                 nxt = __hip_atomic_fetch_add(&s_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             if (cs[u] < nslices) {
-                if (cs[u] * STEP + STEP <= np)
+                if (cs[u] * STEP + STEP <= n)
                     consume(cs[u], buf[u], std::true_type{});
                 else
                     consume(cs[u], buf[u], std::false_type{});
@@ -549,15 +365,19 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         if (done)
             break;
     }
+    // Keys must be finite, so the largest (smallest) kept float has the
+    // largest (smallest) key.
     const uint32_t wmax = wave_max(key_of(fmx));
+    const uint32_t wmin = wave_min(key_of(fmn));
     if (lane == 0) {
         s_wtot[wid] = wcnt;
         s_wmax[wid] = wmax;
+        s_wmin[wid] = wmin;
     }
     lds_barrier();
 
-    // Totals, overflow and the largest candidate key.
-    uint32_t total = 0, kmax = 0;
+    // Totals, overflow and the kept keys' range.
+    uint32_t total = 0, kmax = 0, kmin = 0xFFFFFFFFu;
     bool over = false;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -565,19 +385,15 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         total += c;
         over = over || c > (uint32_t)WCAP;
         kmax = max(kmax, s_wmax[w]);
+        kmin = min(kmin, s_wmin[w]);
     }
-    const bool multi = nparts > 1;
-    bool ok = !a.force_flag && !over && (multi || (int64_t)total * g.bs >= w_need);
-    // Every candidate key lies in [kmin, kmax]; the fine bins take the top
-    // kFineBits bits of (key - kmin) (with one part, counted during the copy
-    // into block order; with several, after the merge).
-    const uint32_t kmin = use_bound ? key_of(fbound) : 0u;
-    uint32_t span = kmax - kmin;
-    auto fine_shift = [](uint32_t sp) {
-        const int fbits = sp != 0 ? 32 - __clz(sp) : 0;
-        return fbits > kFineBits ? fbits - kFineBits : 0;
-    };
-    int sF = fine_shift(span);
+    // Every visible block kept and all of one key: ties go to the lowest
+    // cells, so the selection is the first cells.
+    if (total == (uint32_t)n && kmin == kmax) {
+        write_first_cells<NT>(g, q, qs.wq);
+        return;
+    }
+    const bool ok = !a.force_flag && !over && (int64_t)total * g.bs >= w_need;
     if (ok) {
         // Slices in order are block order: every wave scans the slice counts
         // itself and leaves, for each of its own slices, how far its run moves
@@ -585,13 +401,13 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         // other wave touches those); a candidate's slice is its block / STEP.
         {
             uint32_t carry = 0;
+#pragma unroll 1
             for (int s0 = 0; s0 < nslices; s0 += kWave) {
                 const int sl = s0 + lane;
-                const bool ok = sl < nslices;
-                const uint32_t c = ok ? s_scnt[sl] : 0u;
+                const bool in = sl < nslices;
+                const uint32_t c = in ? s_scnt[sl] : 0u;
                 const uint32_t incl = wave_incl_sum(c);
-                const bool mine = ok && s_swave[sl] == (uint32_t)wid;
-                if (mine)
+                if (in && s_swave[sl] == (uint32_t)wid)
                     s_ssrc[sl] = carry + incl - c - s_ssrc[sl];
                 carry += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
             }
@@ -599,225 +415,53 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+        // The copy into block order also counts every candidate into the
+        // fine bins over [kmin, kmax] (every candidate key lies there) and
+        // the candidates at or above a partial last block's key.
+        const uint32_t kbase = use_bound ? key_of(fbound) : kmin;
+        const int sF = cand_fine_shift(kmax - kbase);
+        const bool bins = kmax != kbase;
         const uint32_t wtot = s_wtot[wid];
         uint32_t gcnt = 0;
         // Four items per lane per round, all reads issued before any write.
+#pragma unroll 1
         for (uint32_t i0 = (uint32_t)lane; i0 < wtot; i0 += 4 * kWave) {
             int32_t blk[4];
             uint32_t raw[4], shift[4];
-            bool ok[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                ok[u] = i0 + u * kWave < wtot;
-                const uint32_t i = ok[u] ? i0 + u * kWave : 0u;
+                const uint32_t i = i0 + u * kWave < wtot ? i0 + u * kWave : 0u;
                 blk[u] = wblk[i];
                 raw[u] = wkey[i];
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                shift[u] = s_ssrc[(blk[u] - p0) / STEP];
+                shift[u] = s_ssrc[blk[u] / STEP];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                if (ok[u]) {
-                    const uint32_t k = key_of(__uint_as_float(raw[u]));
+                if (i0 + u * kWave < wtot) {
                     const uint32_t d = i0 + u * kWave + shift[u];
+                    const uint32_t k = key_of(__uint_as_float(raw[u]));
                     s_ckey[d] = k;
                     s_cblk[d] = blk[u];
                     gcnt += k >= kp ? 1u : 0u;
-                    if (!multi && span != 0) {
-                        const uint32_t fb = (k - kmin) >> sF;
-                        lds_add(&sh.fine[fb], 1u);
-                        lds_add(&sh.coarse[fb / kFinePerCoarse], 1u);
-                    }
+                    if (bins)
+                        count_candidate(k, kbase, sF, sh);
                 }
             }
         }
-        gcnt = wave_sum(gcnt);
-        if (lane == 0)
-            s_gcnt[wid] = gcnt;
-        lds_barrier();
-    }
-    if (multi) {
-        // Publish this part's candidates (or an overflow mark) with
-        // device-coherent stores; the part that arrives last merges them in
-        // part order, which is block order.
-        uint32_t *slot = a.part_ws + ((int64_t)q * a.parts + part) * kPartWords;
-        if (ok) {
-            for (int i = threadIdx.x; i < (int)total; i += NT) {
-                store_dev(slot + kPartHeader + i, s_ckey[i]);
-                store_dev(slot + kPartHeader + kOneReadCap + i, (uint32_t)s_cblk[i]);
-            }
-        }
-        if (threadIdx.x == 0) {
-            store_dev(slot, ok ? total : 0xFFFFFFFFu);
-            store_dev(slot + 1, kmax);
-        }
-        if (!last_to_arrive(&a.part_tickets[q], (uint32_t)nparts, s_flag))
-            return;
-        if (threadIdx.x == 0)
-            store_dev(&a.part_tickets[q], 0u);  // zero again for the next call
-        const uint32_t *base = a.part_ws + (int64_t)q * a.parts * kPartWords;
-        total = 0;
-        kmax = 0;
-        ok = true;
-        for (int j = 0; j < nparts; ++j) {
-            const uint32_t c = load_dev(base + (int64_t)j * kPartWords);
-            ok = ok && c != 0xFFFFFFFFu;
-            total += ok ? c : 0u;
-            kmax = max(kmax, load_dev(base + (int64_t)j * kPartWords + 1));
-        }
-        ok = ok && total <= (uint32_t)kOneReadCap && (int64_t)total * g.bs >= w_need;
-        if (ok) {
-            uint32_t o = 0;
-            for (int j = 0; j < nparts; ++j) {
-                const uint32_t *src = base + (int64_t)j * kPartWords;
-                const int c = (int)load_dev(src);
-                for (int i = threadIdx.x; i < c; i += NT) {
-                    s_ckey[o + i] = load_dev(src + kPartHeader + i);
-                    s_cblk[o + i] = (int32_t)load_dev(src + kPartHeader + kOneReadCap + i);
-                }
-                o += (uint32_t)c;
-            }
-            lds_barrier();
-            span = kmax - kmin;
-            sF = fine_shift(span);
-            uint32_t gcnt = 0;
-            for (int i = threadIdx.x; i < (int)total; i += NT) {
-                const uint32_t k = s_ckey[i];
-                gcnt += k >= kp ? 1u : 0u;
-                if (span != 0) {
-                    const uint32_t fb = (k - kmin) >> sF;
-                    lds_add(&sh.fine[fb], 1u);
-                    lds_add(&sh.coarse[fb / kFinePerCoarse], 1u);
-                }
-            }
+        if (qs.tail != 0) {
             gcnt = wave_sum(gcnt);
             if (lane == 0)
-                s_gcnt[wid] = gcnt;
-            lds_barrier();
+                sh.red[1][wid] = gcnt;
         }
-    }
-    if (ok) {
-        if (qs.tail != 0) {
-            // The partial last block is a candidate iff its key is >= kmin, and
-            // then every block at or above its key is one; if it is not, it is
-            // below the threshold (the candidates hold w_need cells).
-            uint32_t n_ge = 0;
-#pragma unroll
-            for (int w = 0; w < NW; ++w)
-                n_ge += s_gcnt[w];
-            widen_for_tail(qs, g.bs, kp >= kmin ? n_ge : 0xFFFFFFFFu);
-        }
-
-        // Each thread holds the candidates [per*t, per*t + per) of the block
-        // order in registers from here on (per = ceil(total / NT), at most
-        // PER; slots j >= per are skipped as a whole): the threshold's gather
-        // and the emit both use them without another pass over the LDS, and
-        // the candidates are spread over every wave.
-        constexpr int PER = kOneReadCap / NT;
-        const int per = ((int)total + NT - 1) / NT;
-        uint32_t ck[PER];
-        int32_t cb[PER];
-        bool cv[PER];
-        const int c0 = (int)threadIdx.x * per;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            cv[j] = false;
-            ck[j] = 0;
-            cb[j] = 0;
-            if (j < per) {  // workgroup-uniform
-                cv[j] = c0 + j < (int)total;
-                const int i = cv[j] ? c0 + j : 0;
-                ck[j] = s_ckey[i];
-                cb[j] = s_cblk[i];
-            }
-        }
-
-        // Threshold: the fine bin holding rank r usually holds a handful of
-        // keys, which one wave ranks exactly; a crowded one goes on with radix
-        // digits over its keys.
-        uint32_t T = kmin, above = 0;
-        if (span != 0) {
-            uint32_t b, c, h;
-            pick_fine<NT>(sh, (uint32_t)qs.r, b, c, h);
-            const uint32_t blo = kmin + (b << sF);
-            const uint32_t bspan = sF == 0 ? 0u : min(span - (b << sF), (1u << sF) - 1u);
-            const uint32_t r2 = (uint32_t)qs.r - h;
-            uint32_t a2 = 0;
-            if (bspan == 0) {
-                T = blo;
-            } else if (c <= (uint32_t)kWave) {
-                // The bin's keys into sh.small, then one wave ranks them.
-#pragma unroll
-                for (int j = 0; j < PER; ++j) {
-                    if (j < per && cv[j] && ck[j] - blo <= bspan) {
-                        const uint32_t pos =
-                            __hip_atomic_fetch_add(&sh.small_n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                        if (pos < (uint32_t)kWave)
-                            sh.small[pos] = ck[j];
-                    }
-                }
-                lds_barrier();
-                wave_rank_small(sh.small, c, r2, T, a2);
-            } else {
-                radix_select_range<NT>(LdsKeys{s_ckey}, (int)total, r2, blo, blo + bspan, sh, T, a2);
-            }
-            above = h + a2;
-        }
-
-        // Emit: one workgroup scan of (blocks above T, blocks equal to T) in
-        // block order gives every taken block its output slot: bs cells per
-        // taken block, except the last tie taken (rank budget - 1), which
-        // takes last_unit cells and moves every later block down.
-        const uint32_t budget = (uint32_t)qs.r - above;  // >= 1
-        uint32_t gt = 0, tie = 0;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            if (j < per) {  // workgroup-uniform
-                gt += cv[j] && ck[j] > T ? 1u : 0u;
-                tie += cv[j] && ck[j] == T ? 1u : 0u;
-            }
-        }
-        const uint32_t packed = gt | (tie << 16);  // both <= kOneReadCap < 2^16
-        const uint32_t incl = wave_incl_sum(packed);
-        if (lane == kWave - 1)
-            sh.red[0][wid] = incl;
         lds_barrier();
-        uint32_t before = incl - packed;
-#pragma unroll
-        for (int w = 0; w < NW; ++w)
-            before += w < wid ? sh.red[0][w] : 0u;
-        uint32_t ties_before = before >> 16;
-        const uint32_t bs = (uint32_t)g.bs;
-        const uint32_t shortfall = bs - (uint32_t)qs.last_unit;
-        const uint32_t limit = (uint32_t)qs.wq;
-        int32_t *out = g.ids + (int64_t)q * g.width;
-        uint32_t pos = bs * ((before & 0xFFFFu) + min(ties_before, budget)) - (ties_before >= budget ? shortfall : 0u);
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            if (j >= per)  // workgroup-uniform
-                break;
-            uint32_t cells = 0;
-            if (cv[j] && ck[j] > T) {
-                cells = bs;
-            } else if (cv[j] && ck[j] == T) {
-                if (ties_before < budget)
-                    cells = ties_before == budget - 1u ? (uint32_t)qs.last_unit : bs;
-                ++ties_before;
-            }
-            if (cells != 0u) {
-                write_cells(out, pos, cells, cb[j] * (int32_t)bs, limit);
-                pos += cells;
-            }
-        }
-        for (int p = qs.wq + (int)threadIdx.x; p < g.width; p += NT)
-            out[p] = -1;
-        if (g.counts && threadIdx.x == 0)
-            g.counts[q] = qs.wq;
+        widen_from_counts<NT>(qs, g.bs, kp, kbase, sh);
+        select_from_candidates<NT>(s_ckey, s_cblk, (int)total, kbase, kmax, qs, g, q, sh);
         return;
     }
     // Flagged: the exact rule over the whole row, read from global memory (the
-    // histograms are still zero: no histogram pass ran).
+    // histograms are zero: no histogram pass ran).
     if (qs.tail != 0)
         widen_for_tail(qs, g.bs, count_at_least<NT>(RowKeys{row, VEC}, n, kp, sh));
     select_cells<NT>(RowKeys{row, VEC}, n, qs, [&](int i) { return i; }, g, q, sh);
@@ -861,7 +505,7 @@ hipError_t launch_split(const SplitArgs &a, hipStream_t s)
 
 hipError_t launch_oneread(const OneReadArgs &a, hipStream_t s)
 {
-    const dim3 grid((unsigned)(a.g.nq * a.parts));
+    const dim3 grid((unsigned)a.g.nq);
     if (a.g.vec4)
         hipLaunchKernelGGL((oneread_kernel<kOneReadThreads, kOneReadF4, true>), grid, dim3(kOneReadThreads), 0, s, a);
     else

@@ -52,13 +52,23 @@ def test_dispatch_rule():
         assert qsa.topk_plan(nq, 32768, 4, 2048, call)["path"] == qsa.PATH_ONEREAD
 
 
-def test_oneread_parts_are_opt_in():
-    assert qsa.topk_plan(3, 64512, 4, 2048, "decode")["oneread_groups"] == 1
-    o = qsa.make_options(oneread_parts=4)
-    p = qsa.topk_plan(3, 64512, 4, 2048, "decode", o)
-    assert p["path"] == qsa.PATH_ONEREAD and p["oneread_groups"] == 4
-    assert qsa.topk_workspace_bytes(256, 130048, 4, 2048, "prompt") <= 256
-    assert qsa.topk_workspace_bytes(3, 64512, 4, 2048, "decode", o) >= 3 * 4 * (4 + 2 * 4096) * 4
+def test_filter_geometry():
+    # Chunks of 1,024-8,192 blocks: the largest that still gives about 1,024
+    # first-launch workgroups; slots of twice an even share of the 8,192-block
+    # cap (at least 512, at most a chunk).
+    p = qsa.topk_plan(256, 32768, 4, 2048, "prompt", qsa.make_options(topk_path=qsa.PATH_FILTER))
+    assert p["path"] == qsa.PATH_FILTER and p["filter_blocks"] == 8192 and p["filter_chunks"] == 4
+    assert p["filter_slot"] == 4096 and p["filter_groups"] == 1024
+    p = qsa.topk_plan(3, 64512, 4, 2048, "decode", qsa.make_options(topk_path=qsa.PATH_FILTER))
+    assert p["filter_blocks"] == 1024 and p["filter_chunks"] == 63 and p["filter_slot"] == 512
+    p = qsa.topk_plan(16, 65536, 4, 2048, "decode", qsa.make_options(topk_path=qsa.PATH_FILTER, filter_blocks=4096))
+    assert p["filter_blocks"] == 4096 and p["filter_chunks"] == 16 and p["filter_slot"] == 1024
+    heads, slots = 16 * 16 * 16, 16 * 16 * 2 * 1024 * 4
+    assert p["workspace_bytes"] >= heads + slots
+    # more than 1,024 chunks of the largest size: the split instead
+    big = 1024 * 8192 + 1
+    assert qsa.topk_plan(1, big, 1, 64, "decode", qsa.make_options(topk_path=qsa.PATH_FILTER))["path"] == \
+        qsa.PATH_SPLIT
 
 
 def test_prompt_ks_and_cap():
@@ -99,11 +109,11 @@ def test_width_larger_than_context():
     (dict(chunk_blocks=15364), B.QSA_EINVAL),
     (dict(topk_path=7), B.QSA_EINVAL),
     (dict(sample=9), B.QSA_EINVAL),
-    (dict(oneread_blocks=2048), B.QSA_EUNSUPPORTED),
-    (dict(reserved=(1, 0)), B.QSA_EINVAL),
-    (dict(reserved=(0, 1)), B.QSA_EINVAL),
-    (dict(oneread_parts=17), B.QSA_EINVAL),
-    (dict(oneread_parts=-1), B.QSA_EINVAL),
+    (dict(reserved=(1,)), B.QSA_EINVAL),
+    (dict(filter_blocks=3000), B.QSA_EINVAL),
+    (dict(filter_blocks=512), B.QSA_EINVAL),
+    (dict(topk_path=4), B.QSA_EINVAL),
+    (dict(reserved=(0, 0, 1)), B.QSA_EINVAL),
 ])
 def test_bad_options_rejected(kw, status):
     with pytest.raises(B.QSAError) as e:
@@ -168,7 +178,7 @@ def test_scores_empty_is_a_no_op():
 
 
 def test_plan_struct_size_matches_header():
-    assert ctypes.sizeof(B.Plan) == 12 * 4 + 8
+    assert ctypes.sizeof(B.Plan) == 16 * 4 + 8
     assert ctypes.sizeof(B.Options) == 8 * 4
 
 

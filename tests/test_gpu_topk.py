@@ -30,9 +30,12 @@ PATHS = {
     "oneread_stride": dict(topk_path=qsa.PATH_ONEREAD, sample=qsa.SAMPLE_STRIDE),
     "fallback": dict(topk_path=qsa.PATH_ONEREAD, force_fallback=1),
     "fallback64": dict(topk_path=qsa.PATH_ONEREAD, force_fallback=1, chunk_blocks=64),
-    "parts2": dict(topk_path=qsa.PATH_ONEREAD, oneread_parts=2),
-    "parts5": dict(topk_path=qsa.PATH_ONEREAD, oneread_parts=5),
-    "parts16": dict(topk_path=qsa.PATH_ONEREAD, oneread_parts=16, sample=qsa.SAMPLE_STRIDE),
+    "filter2k_stride": dict(topk_path=qsa.PATH_FILTER, filter_blocks=2048, sample=qsa.SAMPLE_STRIDE),
+    "filter4k": dict(topk_path=qsa.PATH_FILTER, filter_blocks=4096),
+    "filter": dict(topk_path=qsa.PATH_FILTER),
+    "filter1k": dict(topk_path=qsa.PATH_FILTER, filter_blocks=1024),
+    "filter8k_stride": dict(topk_path=qsa.PATH_FILTER, filter_blocks=8192, sample=qsa.SAMPLE_STRIDE),
+    "filter_fallback": dict(topk_path=qsa.PATH_FILTER, force_fallback=1),
 }
 
 
@@ -123,12 +126,12 @@ def _branch_keys(kind, nq, n):
     raise ValueError(kind)
 
 
-@pytest.mark.parametrize("path", ["split", "split516", "fallback"])
+@pytest.mark.parametrize("path", ["split", "split516", "fallback", "filter", "filter_fallback"])
 @pytest.mark.parametrize("kind", ["tiny_span", "bits_few", "bits_crowded", "value_few", "value_crowded"])
 def test_threshold_select_branches(kind, path):
     nq, n = 3, 20000
     s = _branch_keys(kind, nq, n)
-    call = "prompt" if path == "fallback" else "decode"
+    call = "prompt" if "fallback" in path else "decode"
     active = np.full(nq, n, np.int32) if call == "prompt" else None
     say(f"threshold branch {kind} path={path}")
     for width in (2048, 40000):
@@ -141,7 +144,8 @@ def test_decode_contexts_full_size(n_blocks):
     wl = synth.c2(n_blocks)
     s = wl.scores()
     exp = oracle.topk_sort(s, n_blocks, wl.block_size, wl.width)
-    for path in ("auto", "split", "split64", "oneread_lines", "parts2", "parts16"):
+    for path in ("auto", "split", "split64", "oneread_lines", "oneread_stride", "fallback", "filter", "filter1k",
+                 "filter8k_stride", "filter_fallback"):
         say(f"C2 decode nb={n_blocks} path={path}")
         got = gpu_topk(s, n_blocks, wl.block_size, wl.width, "decode", options=_opts(path))
         assert_ids_equal(got, exp, f"C2 nb={n_blocks} {path}")
@@ -153,12 +157,17 @@ def test_prompt_contexts_full_size(n_blocks, variant):
     wl = synth.c4(n_blocks, variant)
     s = wl.scores()
     active = np.full(wl.nq, n_blocks, np.int32)
-    rows = np.arange(0, wl.nq, 17)  # the oracle redoes 16 of the 256 queries
-    exp = oracle.topk_sort(s[rows], n_blocks, wl.block_size, wl.width, active[rows])
-    for path in ("auto", "split", "parts5"):
+    # Every one of the 256 queries against the oracle's threshold-rule top-k
+    # (pinned equal to its full sort on the CPU), and 16 of them against the
+    # full sort itself.
+    exp = oracle.topk_rule(s, n_blocks, wl.block_size, wl.width, active)
+    rows = np.arange(0, wl.nq, 17)
+    assert_ids_equal(exp, oracle.topk_sort(s[rows], n_blocks, wl.block_size, wl.width, active[rows]),
+                     "oracle rule vs sort", rows=rows)
+    for path in ("auto", "split", "oneread_lines", "fallback", "filter", "filter1k", "filter_fallback"):
         say(f"C4 prompt nb={n_blocks} {variant} path={path}")
         got = gpu_topk(s, n_blocks, wl.block_size, wl.width, "prompt", active=active, options=_opts(path))
-        assert_ids_equal(got, exp, f"C4 nb={n_blocks} {variant} {path}", rows=rows)
+        assert_ids_equal(got, exp, f"C4 nb={n_blocks} {variant} {path}")
         assert (got[1] == wl.width).all()
 
 
@@ -271,7 +280,7 @@ def test_cells_decode_contexts_full_size(n_blocks):
     full = n_blocks * wl.block_size
     cells = np.array([full - 1, full - 3, full - 4 * 999 - 2], np.int32)
     exp = oracle.topk_sort_cells(s, n_blocks, wl.block_size, wl.width, cells)
-    for path in ("auto", "split", "split64", "parts5"):
+    for path in ("auto", "split", "split64", "oneread_lines", "fallback", "filter", "filter1k", "filter_fallback"):
         say(f"C2 cells nb={n_blocks} path={path}")
         got = gpu_topk_cells(s, n_blocks, wl.block_size, wl.width, "decode", cells, options=_opts(path))
         assert_ids_equal(got, exp, f"C2 cells nb={n_blocks} {path}")
@@ -285,12 +294,14 @@ def test_cells_prompt_full_size(variant):
     full = n_blocks * wl.block_size
     cells = synth.integers(f"gpu/topk/cells/c4/{variant}", wl.nq, full // 2, full).astype(np.int32)
     cells[::3] = full - 1 - (np.arange(0, wl.nq, 3) % 3)  # partial last blocks
+    exp = oracle.topk_rule_cells(s, n_blocks, wl.block_size, wl.width, cells)
     rows = np.arange(0, wl.nq, 17)
-    exp = oracle.topk_sort_cells(s[rows], n_blocks, wl.block_size, wl.width, cells[rows])
-    for path in ("auto", "split", "parts2"):
+    assert_ids_equal(exp, oracle.topk_sort_cells(s[rows], n_blocks, wl.block_size, wl.width, cells[rows]),
+                     "oracle rule vs sort", rows=rows)
+    for path in ("auto", "split", "oneread_lines", "fallback", "filter", "filter_fallback"):
         say(f"C4 cells {variant} path={path}")
         got = gpu_topk_cells(s, n_blocks, wl.block_size, wl.width, "prompt", cells, options=_opts(path))
-        assert_ids_equal(got, exp, f"C4 cells {variant} {path}", rows=rows)
+        assert_ids_equal(got, exp, f"C4 cells {variant} {path}")
 
 
 def test_cells_length_changes_between_graph_replays():
