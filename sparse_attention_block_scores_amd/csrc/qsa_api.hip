@@ -111,14 +111,19 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
     }
 
     // Dispatch (measured on MI355X; results never depend on it). A row that
-    // fits one chunk is selected in LDS by one workgroup. Longer rows take the
-    // one-read path while its candidates are a small share of the row (the
-    // bound keeps about 3r blocks); otherwise the split.
+    // fits one chunk is selected in LDS by one workgroup. Longer rows take a
+    // sampled-bound path while its candidates are a small share of the row
+    // (the bound keeps about 3r blocks); otherwise the split. Among those, a
+    // few queries with long rows spread each row over chunk workgroups (the
+    // filtered split: one workgroup per query streams too slowly to fill the
+    // GPU); many queries take one workgroup each (one read, one launch).
     int path = opt ? opt->topk_path : QSA_PATH_AUTO;
-    if (path == QSA_PATH_AUTO)
-        path = (n_blocks > kChunkBound && (int64_t)n_blocks >= (int64_t)kOneReadMinRatio * p.r_blocks)
-                   ? QSA_PATH_ONEREAD
-                   : QSA_PATH_SPLIT;
+    if (path == QSA_PATH_AUTO) {
+        if (n_blocks > kChunkBound && (int64_t)n_blocks >= (int64_t)kOneReadMinRatio * p.r_blocks)
+            path = (nq <= kFilterMaxQueries && n_blocks >= kFilterMinBlocks) ? QSA_PATH_FILTER : QSA_PATH_ONEREAD;
+        else
+            path = QSA_PATH_SPLIT;
+    }
     if (path == QSA_PATH_ONEREAD && n_blocks > kOneReadMaxBatches * kOneReadBatch)
         path = QSA_PATH_SPLIT;  // per-batch counts of longer rows do not fit the LDS table
     if (path == QSA_PATH_FILTER && p.filter_chunks > kFilterMaxChunks)

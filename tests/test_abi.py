@@ -43,22 +43,31 @@ def test_split_geometry_with_page_chunks():
 
 def test_dispatch_rule():
     # One chunk: the split's single workgroup; longer rows where the bound
-    # keeps a small share of the blocks (n >= 16 r): one-read; else the split.
+    # keeps a small share of the blocks (n >= 16 r): the filtered split for a
+    # few queries with long rows, else one-read; anything else: the split.
     assert qsa.topk_plan(3, 4104, 4, 2048, "decode")["path"] == qsa.PATH_SPLIT
     assert qsa.topk_plan(3, 8191, 4, 2048, "decode")["path"] == qsa.PATH_SPLIT
     assert qsa.topk_plan(3, 8192, 4, 2048, "decode")["path"] == qsa.PATH_ONEREAD
     assert qsa.topk_plan(3, 4105, 4, 256, "decode")["path"] == qsa.PATH_ONEREAD
-    for nq, call in ((3, "decode"), (16, "decode"), (16, "prompt"), (256, "prompt")):
-        assert qsa.topk_plan(nq, 32768, 4, 2048, call)["path"] == qsa.PATH_ONEREAD
+    for nq, nb, call in ((3, 10240, "decode"), (3, 16384, "decode"), (256, 32768, "prompt"),
+                         (256, 130048, "prompt"), (33, 65536, "decode")):
+        assert qsa.topk_plan(nq, nb, 4, 2048, call)["path"] == qsa.PATH_ONEREAD, (nq, nb)
+    for nq, nb, call in ((3, 32768, "decode"), (3, 64512, "decode"), (16, 65536, "decode"), (32, 40000, "prompt")):
+        assert qsa.topk_plan(nq, nb, 4, 2048, call)["path"] == qsa.PATH_FILTER, (nq, nb)
+    # chunk sizes for about 512 first-launch workgroups
+    assert qsa.topk_plan(3, 64512, 4, 2048, "decode")["filter_blocks"] == 1024
+    assert qsa.topk_plan(16, 65536, 4, 2048, "decode")["filter_blocks"] == 2048
 
 
 def test_filter_geometry():
-    # Chunks of 1,024-8,192 blocks: the largest that still gives about 1,024
+    # Chunks of 1,024-8,192 blocks: the largest that still gives about 512
     # first-launch workgroups; slots of twice an even share of the 8,192-block
     # cap (at least 512, at most a chunk).
     p = qsa.topk_plan(256, 32768, 4, 2048, "prompt", qsa.make_options(topk_path=qsa.PATH_FILTER))
     assert p["path"] == qsa.PATH_FILTER and p["filter_blocks"] == 8192 and p["filter_chunks"] == 4
     assert p["filter_slot"] == 4096 and p["filter_groups"] == 1024
+    p = qsa.topk_plan(8, 65536, 4, 2048, "prompt", qsa.make_options(topk_path=qsa.PATH_FILTER))
+    assert p["filter_blocks"] == 1024 and p["filter_groups"] == 512
     p = qsa.topk_plan(3, 64512, 4, 2048, "decode", qsa.make_options(topk_path=qsa.PATH_FILTER))
     assert p["filter_blocks"] == 1024 and p["filter_chunks"] == 63 and p["filter_slot"] == 512
     p = qsa.topk_plan(16, 65536, 4, 2048, "decode", qsa.make_options(topk_path=qsa.PATH_FILTER, filter_blocks=4096))
@@ -226,3 +235,4 @@ def test_attention_workspace_sizes():
     parts = 16 * 8 * 16
     assert qsa.attention_workspace_bytes(16, 16, 1, 2048) == (parts * 8 + 255) // 256 * 256 + parts * 512
     assert qsa.attention_workspace_bytes(16, 16, 3, 2048) == 0  # invalid grouping
+
