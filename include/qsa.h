@@ -210,6 +210,29 @@ qsa_status qsa_block_topk_cells(const float *scores, int64_t ld_scores, int32_t 
                                 const qsa_options *opt);
 
 /*
+ * qsa_block_topk_noalloc - qsa_block_topk for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same selection with the default options, its
+ * workspace taken from a fixed array of QSA_NOALLOC_SCRATCH_BYTES per GPU
+ * inside the library (held until the process ends) instead of a caller's
+ * buffer. Nothing is allocated; the first call on a device zero-fills that
+ * device's array on `stream`.
+ *
+ *   Arguments and results as qsa_block_topk without workspace and options.
+ *   A call whose workspace (qsa_topk_workspace_bytes with NULL options) is
+ *   larger than QSA_NOALLOC_SCRATCH_BYTES returns QSA_EUNSUPPORTED and
+ *   enqueues nothing.
+ *   Every call on one GPU shares that GPU's array: calls that may overlap on
+ *   one GPU (several streams, several host threads) race and must be ordered
+ *   by the caller. A completed call leaves the array ready for the next.
+ */
+#define QSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+qsa_status qsa_block_topk_noalloc(const float *scores, int64_t ld_scores, int32_t nq,
+                                  int32_t n_blocks, int32_t block_size, int32_t width,
+                                  qsa_call call, const int32_t *active_blocks,
+                                  int32_t *cell_ids, int32_t *counts, void *stream);
+
+/*
  * qsa_select - qsa_block_scores followed by qsa_block_topk on the scores it
  * wrote (`scores` is the caller's buffer and holds the scores afterwards).
  * Same argument rules as the two calls above.

@@ -8,6 +8,6 @@ This package is the thin Python binding over libqsa.so.
 """
 from ._binding import (DECODE, PATH_AUTO, PATH_FILTER, PATH_ONEREAD, PATH_SPLIT, PROMPT, SAMPLE_AUTO,  # noqa: F401
                        SAMPLE_LINES, SAMPLE_STRIDE, Options, QSAError, attention_workspace_bytes, block_scores,
-                       block_scores_bf16, block_topk, selection_attention,
+                       block_scores_bf16, block_topk, block_topk_noalloc, selection_attention,
                        declared_functions, lib, make_options, select, status_str, topk_plan,
                        topk_workspace_bytes, workspace)

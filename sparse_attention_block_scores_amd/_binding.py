@@ -90,13 +90,15 @@ def lib() -> ctypes.CDLL:
         L.qsa_block_topk.argtypes = [P, i64, i32, i32, i32, i32, i32, P, P, P, P, sz, P, P]
         L.qsa_select.argtypes = [P, P, P, i32, i32, P, i64, i32, i32, i32, i32, i32, P, P, P, P, sz, P, P]
         L.qsa_block_topk_cells.argtypes = L.qsa_block_topk.argtypes
+        L.qsa_block_topk_noalloc.argtypes = [P, i64, i32, i32, i32, i32, i32, P, P, P, P]
         L.qsa_select_cells.argtypes = L.qsa_select.argtypes
         L.qsa_selection_attention_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.qsa_selection_attention_workspace_bytes.restype = sz
         L.qsa_selection_attention.argtypes = [P, P, P, P, i64, P, P, i32, i32, i32, i32, i32, i32,
                                               ctypes.c_float, P, sz, P]
         for name in ("qsa_block_scores", "qsa_block_scores_bf16", "qsa_topk_plan_get", "qsa_workspace_init", "qsa_block_topk",
-                     "qsa_select", "qsa_block_topk_cells", "qsa_select_cells", "qsa_selection_attention"):
+                     "qsa_select", "qsa_block_topk_cells", "qsa_select_cells", "qsa_selection_attention",
+                     "qsa_block_topk_noalloc"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -355,6 +357,27 @@ def block_topk(scores, n_blocks, block_size, width, call, active=None, ids=None,
     _check(getattr(lib(), name)(_ptr(scores), ld, nq, n_blocks, block_size, width, code,
                                 _ptr(lengths), _ptr(ids), _ptr(counts), _ptr(ws), _nbytes(ws),
                                 _stream(stream), _opt(options)), name)
+    return ids, counts
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # QSA_NOALLOC_SCRATCH_BYTES in include/qsa.h
+
+
+def block_topk_noalloc(scores, n_blocks, block_size, width, call, active=None, ids=None, counts=None,
+                       stream=None):
+    """block_topk through qsa_block_topk_noalloc: no workspace argument, the
+    library's fixed per-GPU array instead (default options). Outputs are
+    allocated here only when not given."""
+    _dev(scores, torch.float32, "scores")
+    if scores.dim() != 2:
+        raise ValueError("scores must be [nq, ld] with unit column stride")
+    nq = scores.shape[0]
+    ld = score_matrix_shape(scores.shape, scores.stride(), nq, n_blocks)
+    code = _call_code(call)
+    act = _active(active, nq)
+    ids, counts = _topk_outputs(nq, width, scores.device, ids, counts)
+    _check(lib().qsa_block_topk_noalloc(_ptr(scores), ld, nq, n_blocks, block_size, width, code, _ptr(act),
+                                        _ptr(ids), _ptr(counts), _stream(stream)), "qsa_block_topk_noalloc")
     return ids, counts
 
 

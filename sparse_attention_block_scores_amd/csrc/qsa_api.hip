@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -305,9 +307,73 @@ qsa_status select_call(const float *q, const float *k, const float *w, int32_t n
     return run_topk(g, plan, workspace, (hipStream_t)stream, opt);
 }
 
+// ------------------------------------------------------------ static scratch
+// The workspace of qsa_block_topk_noalloc: one fixed array per GPU, in device
+// memory for as long as the library is loaded. In host code `scratch` names a
+// host-side stand-in, never the device array: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kStaticScratchBytes = (size_t)QSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceScratch {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+
+DeviceScratch g_scratch[kMaxDevices];
+
+// The current device's scratch address; the first call on a device looks it
+// up (with that device current) and zero-fills the array on `s` (a kernel,
+// ordered before the caller's launches on the same stream).
+qsa_status device_scratch(hipStream_t s, void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return QSA_EHIP;
+    DeviceScratch &d = g_scratch[dev];
+    std::call_once(d.once, [&] {
+        d.err = hipGetSymbolAddress(&d.ptr, HIP_SYMBOL(scratch));
+        if (d.err == hipSuccess)
+            d.err = launch_zero(d.ptr, kStaticScratchBytes, s);
+        if (d.err != hipSuccess)
+            d.ptr = nullptr;
+    });
+    if (d.err != hipSuccess || !d.ptr)
+        return QSA_EHIP;
+    *out = d.ptr;
+    return QSA_OK;
+}
+
 } // namespace
 
 extern "C" {
+
+qsa_status qsa_block_topk_noalloc(const float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks,
+                                  int32_t block_size, int32_t width, qsa_call call, const int32_t *active_blocks,
+                                  int32_t *cell_ids, int32_t *counts, void *stream)
+{
+    TopkPlan plan;
+    qsa_status st = make_topk_plan(nq, n_blocks, block_size, width, call, nullptr, plan);
+    if (st != QSA_OK)
+        return st;
+    st = check_topk_args(scores, ld_scores, nq, n_blocks, call, active_blocks, nullptr, cell_ids, counts);
+    if (st != QSA_OK)
+        return st;
+    if (plan.lay.bytes > kStaticScratchBytes)
+        return QSA_EUNSUPPORTED;  // the call needs more workspace than the fixed array holds
+    if (nq == 0)
+        return QSA_OK;
+    void *ws = nullptr;
+    st = device_scratch((hipStream_t)stream, &ws);
+    if (st != QSA_OK)
+        return st;
+    const TopkGeom g = make_geom(scores, ld_scores, nq, n_blocks, block_size, width, active_blocks, nullptr,
+                                 cell_ids, counts);
+    return run_topk(g, plan, ws, (hipStream_t)stream, nullptr);
+}
 
 const char *qsa_status_str(qsa_status status)
 {

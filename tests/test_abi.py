@@ -236,3 +236,33 @@ def test_attention_workspace_sizes():
     assert qsa.attention_workspace_bytes(16, 16, 1, 2048) == (parts * 8 + 255) // 256 * 256 + parts * 512
     assert qsa.attention_workspace_bytes(16, 16, 3, 2048) == 0  # invalid grouping
 
+
+def _noalloc(L, **over):
+    a = dict(scores=FAKE, ld=1000, nq=4, n_blocks=1000, bs=4, width=64, call=0, active=None, ids=FAKE,
+             counts=None, stream=None)
+    a.update(over)
+    return L.qsa_block_topk_noalloc(a["scores"], a["ld"], a["nq"], a["n_blocks"], a["bs"], a["width"], a["call"],
+                                    a["active"], a["ids"], a["counts"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ld=999), B.QSA_EINVAL),
+    (dict(width=0), B.QSA_EINVAL),
+    (dict(active=FAKE), B.QSA_EINVAL),
+    (dict(ids=None), B.QSA_EINVAL),
+    # a split needing 256 x 25 chunks x 4,000 candidates x 8 bytes: more than the fixed array
+    (dict(nq=256, n_blocks=100000, ld=100000, width=40000), B.QSA_EUNSUPPORTED),
+])
+def test_noalloc_argument_errors(over, status):
+    # checked on the host before the library touches the device
+    assert _noalloc(qsa.lib(), **over) == status
+
+
+def test_noalloc_limit_matches_header():
+    text = open(B.HEADER).read()
+    assert "#define QSA_NOALLOC_SCRATCH_BYTES (16u << 20)" in text
+    assert B.NOALLOC_SCRATCH_BYTES == 16 << 20
+    # the workloads' calls fit
+    for nq, nb, call in ((3, 64512, "decode"), (16, 65536, "decode"), (256, 130048, "prompt"), (3, 1024, "decode")):
+        assert qsa.topk_workspace_bytes(nq, nb, 4, 2048, call) <= B.NOALLOC_SCRATCH_BYTES
+    assert qsa.topk_workspace_bytes(256, 100000, 4, 40000, "prompt") > B.NOALLOC_SCRATCH_BYTES
