@@ -30,8 +30,10 @@
  * launches depend only on the host arguments, so a stream capture replays).
  *
  * Memory and streams. Every pointer argument except `opt` and `out` structs
- * is caller-owned DEVICE memory; the library never allocates, frees or keeps
- * device memory of its own and holds no device globals. All work is enqueued
+ * is caller-owned DEVICE memory; the library never allocates or frees device
+ * memory, and the only device memory of its own is the fixed workspace array
+ * of qsa_block_topk_noalloc (one per GPU, for callers that cannot allocate).
+ * All work is enqueued
  * on `stream` (a hipStream_t; NULL = the default stream) and the calls return
  * without synchronising. Nothing is printed.
  *

@@ -57,8 +57,7 @@ def test_prompt_select_full_size():
     active = np.full(wl.nq, wl.n_blocks, np.int32)
     (q, k, w), s, ids, counts = run_select(wl, active=active)
     ref = oracle.block_scores(q, k, w)
-    rows = synth.integers("gpu/sel/C5/rows", 8, 0, wl.nq - 1)
-    assert_scores_close(s[rows], ref[rows], "C5 sampled rows")
+    assert_scores_close(s, ref, "C5 (every score of the 256 x 131,072 matrix)")
     near = 0
     for i in range(wl.nq):
         near += check_selection_near_threshold(ids[i], counts[i], ref[i], wl.block_size, wl.width, f"C5 q{i}")
