@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode / top-k-only figures")
     ap.add_argument("--only-attention", action="store_true",
                     help="time only the attention over the selected cells (for profiling runs)")
+    ap.add_argument("--only-topk", action="store_true",
+                    help="time only the top-k-only figures (for profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (to scale profiler byte counters)")
     return ap.parse_args()
@@ -168,20 +170,59 @@ def secondary(torch, qsa, synth, dev, reps=50):
     out["decode_nq16_select_us"] = round(time_us(lambda i: qsa.select(q3, k3, w3, 4, wl3.width, "decode",
                                                                        scores=s3, ids=ids3, counts=cnt3,
                                                                        ws=ws3, stream=cur())), 2)
-    dec, dec_split = {}, {}
+    out.update(topk_figures(torch, qsa, synth, dev, time_us, s3))
+
+    # The BF16-input scorer (qsa_block_scores_bf16) on the prompt-call and
+    # 16-query decode shapes; torch's float -> bfloat16 conversion rounds to
+    # nearest even, as the parity tests do.
+    bf = {}
+    for wlb in (synth.c5(), synth.c3()):
+        qh, kh, wh = wlb.tensors()
+        qb = torch.from_numpy(qh).to(dev).to(torch.bfloat16)
+        kb = torch.from_numpy(kh).to(dev).to(torch.bfloat16)
+        wb = torch.from_numpy(wh).to(dev)
+        sb = torch.empty((wlb.nq, wlb.n_blocks), device=dev)
+        us = time_us(lambda i: qsa.block_scores_bf16(qb, kb, wb, scores=sb, stream=cur()), n=20)
+        tf = wlb.flops() / (us * 1e-6) / 1e12
+        bf[wlb.name] = {"us": round(us, 2), "TFLOPs": round(tf, 1), "bf16_peak_frac": round(tf / PEAK_BF16_MFMA_TFLOPS, 4)}
+        del qb, kb, wb, sb
+    out["bf16_scorer"] = bf
+
+    out["selection_attention"] = attention_figures(torch, qsa, synth, dev, time_us)
+    return out
+
+
+def topk_figures(torch, qsa, synth, dev, time_us, c3_scores=None):
+    """Top-k-only figures: decode contexts (3 queries) as dispatched, with the
+    chunked split and with the filtered split forced; the 16-query decode
+    top-k on the scorer's C3 scores; prompt calls (256 queries) at each
+    context and key variant over rotated score buffers."""
+    cur = torch.cuda.current_stream
+    out = {}
+    dec, dec_split, dec_filter = {}, {}, {}
     split = qsa.make_options(topk_path=qsa.PATH_SPLIT)
+    filt = qsa.make_options(topk_path=qsa.PATH_FILTER)
     for nb in synth.C2_BLOCKS:
         t = synth.c2(nb)
         sc = torch.from_numpy(t.scores()).to(dev)
         idd = torch.empty((t.nq, t.width), dtype=torch.int32, device=dev)
         cd = torch.empty((t.nq,), dtype=torch.int32, device=dev)
-        for table, opt in ((dec, None), (dec_split, split)):
+        for table, opt in ((dec, None), (dec_split, split), (dec_filter, filt)):
             wsd = qsa.workspace(qsa.topk_workspace_bytes(t.nq, nb, 4, t.width, "decode", opt), dev)
             table[str(nb * 4)] = round(time_us(lambda i: qsa.block_topk(sc, nb, 4, t.width, "decode", ids=idd,
                                                                         counts=cd, ws=wsd, options=opt,
                                                                         stream=cur())), 2)
-    out["decode_nq3_topk_us_by_cells"] = dec              # the dispatch's choice (one-read for these rows)
-    out["decode_nq3_topk_split_us_by_cells"] = dec_split  # the multi-workgroup chunked split, forced
+    out["decode_nq3_topk_us_by_cells"] = dec                # the dispatch's choice
+    out["decode_nq3_topk_split_us_by_cells"] = dec_split    # the exact chunked split, forced
+    out["decode_nq3_topk_filter_us_by_cells"] = dec_filter  # the two-launch filtered split, forced
+    if c3_scores is not None:
+        wl3 = synth.c3()
+        ids3 = torch.empty((wl3.nq, wl3.width), dtype=torch.int32, device=dev)
+        cnt3 = torch.empty((wl3.nq,), dtype=torch.int32, device=dev)
+        ws3 = qsa.workspace(qsa.topk_workspace_bytes(wl3.nq, wl3.n_blocks, 4, wl3.width, "decode"), dev)
+        out["decode_nq16_topk_us"] = round(time_us(lambda i: qsa.block_topk(c3_scores, wl3.n_blocks, 4, wl3.width,
+                                                                          "decode", ids=ids3, counts=cnt3, ws=ws3,
+                                                                          stream=cur())), 2)
     prm = {}
     for nb in synth.C4_BLOCKS:
         entry = {}
@@ -207,29 +248,11 @@ def secondary(torch, qsa, synth, dev, reps=50):
                 entry.update({"us": round(us, 2), "scores_GBps": round(gbs, 1),
                               "hbm_frac": round(gbs / PEAK_HBM_GBS, 3), "rotated_buffers": nbuf,
                               "rotated_MiB": round(nbuf * touched / 2 ** 20), "warm_us": round(warm, 2)})
-            else:  # 64-level keys; all-equal keys (every query takes the exact fallback)
+            else:  # 64-level keys; all-equal keys (detected during the stream)
                 entry[variant + "_us"] = round(us, 2)
             del bufs
         prm[str(nb * 4)] = entry
     out["prompt_nq256_topk_by_cells"] = prm
-
-    # The BF16-input scorer (qsa_block_scores_bf16) on the prompt-call and
-    # 16-query decode shapes; torch's float -> bfloat16 conversion rounds to
-    # nearest even, as the parity tests do.
-    bf = {}
-    for wlb in (synth.c5(), synth.c3()):
-        qh, kh, wh = wlb.tensors()
-        qb = torch.from_numpy(qh).to(dev).to(torch.bfloat16)
-        kb = torch.from_numpy(kh).to(dev).to(torch.bfloat16)
-        wb = torch.from_numpy(wh).to(dev)
-        sb = torch.empty((wlb.nq, wlb.n_blocks), device=dev)
-        us = time_us(lambda i: qsa.block_scores_bf16(qb, kb, wb, scores=sb, stream=cur()), n=20)
-        tf = wlb.flops() / (us * 1e-6) / 1e12
-        bf[wlb.name] = {"us": round(us, 2), "TFLOPs": round(tf, 1), "bf16_peak_frac": round(tf / PEAK_BF16_MFMA_TFLOPS, 4)}
-        del qb, kb, wb, sb
-    out["bf16_scorer"] = bf
-
-    out["selection_attention"] = attention_figures(torch, qsa, synth, dev, time_us)
     return out
 
 
@@ -304,6 +327,10 @@ def main():
     if args.only_attention:
         att = attention_figures(torch, qsa, synth, dev, lambda fn, n: graph_us(torch, dev, fn, n))
         print(json.dumps({"selection_attention": att}), flush=True)
+        return
+    if args.only_topk:
+        tk = topk_figures(torch, qsa, synth, dev, lambda fn, n=50: graph_us(torch, dev, fn, n))
+        print(json.dumps(tk), flush=True)
         return
     wl = synth.c5()
     q_h, k_h, w_h = wl.tensors()
