@@ -42,10 +42,10 @@
  * a launch failed (work enqueued before the failure may still run).
  *
  * Workspace. The top-k needs a scratch area of qsa_topk_workspace_bytes()
- * bytes, 256-byte aligned. Its counter region must be zero before its first
- * use (qsa_workspace_init() zero-fills it, so does any zero fill); every call
- * that completes leaves it zero again. Calls that may run concurrently (two
- * streams) need separate workspaces.
+ * bytes, 256-byte aligned. It needs no set-up: every call writes what it
+ * reads back (qsa_workspace_init() zero-fills one all the same, for callers
+ * that want defined contents). Calls that may run concurrently (two streams)
+ * need separate workspaces.
  */
 #ifndef QSA_H
 #define QSA_H
@@ -218,7 +218,8 @@ qsa_status qsa_block_topk_cells(const float *scores, int64_t ld_scores, int32_t 
  * workspace taken from a fixed array of QSA_NOALLOC_SCRATCH_BYTES per GPU
  * inside the library (held until the process ends) instead of a caller's
  * buffer. Nothing is allocated; the first call on a device zero-fills that
- * device's array on `stream`.
+ * device's array on `stream` (nothing depends on it: every call writes what
+ * it reads back).
  *
  *   Arguments and results as qsa_block_topk without workspace and options.
  *   A call whose workspace (qsa_topk_workspace_bytes with NULL options) is
@@ -226,7 +227,7 @@ qsa_status qsa_block_topk_cells(const float *scores, int64_t ld_scores, int32_t 
  *   enqueues nothing.
  *   Every call on one GPU shares that GPU's array: calls that may overlap on
  *   one GPU (several streams, several host threads) race and must be ordered
- *   by the caller. A completed call leaves the array ready for the next.
+ *   by the caller.
  */
 #define QSA_NOALLOC_SCRATCH_BYTES (16u << 20)
 qsa_status qsa_block_topk_noalloc(const float *scores, int64_t ld_scores, int32_t nq,

@@ -171,19 +171,22 @@ def topk_workspace_bytes(nq, n_blocks, block_size, width, call, options=None) ->
     return n
 
 
-def workspace(nbytes: int, device=None, stream=None) -> torch.Tensor:
-    """A zero-filled workspace of nbytes (256-byte aligned), allocated and
-    zeroed on `stream` (default: the current stream). The caching allocator
-    ties a block to the stream it was allocated on, so a workspace the calls
-    below make for themselves, used on `stream` and dropped on return, is not
-    handed to other work until that stream's kernels are done with it."""
+def workspace(nbytes: int, device=None, stream=None, zero: bool = False) -> torch.Tensor:
+    """A workspace of nbytes (256-byte aligned) allocated on `stream` (default:
+    the current stream). The library needs no set-up of it (every call writes
+    what it reads back); zero=True zero-fills it with qsa_workspace_init. The
+    caching allocator ties a block to the stream it was allocated on, so a
+    workspace the calls below make for themselves, used on `stream` and
+    dropped on return, is not handed to other work until that stream's kernels
+    are done with it."""
     device = device or torch.device("cuda", torch.cuda.current_device())
     st = torch.cuda.current_stream(device) if stream is None else stream
     with torch.cuda.stream(st):
         buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
     off = (-buf.data_ptr()) % 256
     ws = buf[off:off + nbytes]
-    _check(lib().qsa_workspace_init(_ptr(ws), nbytes, _stream(st)), "qsa_workspace_init")
+    if zero:
+        _check(lib().qsa_workspace_init(_ptr(ws), nbytes, _stream(st)), "qsa_workspace_init")
     return ws
 
 

@@ -137,7 +137,6 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
     size_t off = 0;
     if (path == QSA_PATH_SPLIT) {
         const size_t q = (size_t)(nq > 0 ? nq : 1);
-        L.split_tickets = off; off = align_up(off + q * 4);
         L.split_keys = off;    off = align_up(off + q * (size_t)plan.cand_stride * 4);
         L.split_blocks = off;  off = align_up(off + q * (size_t)plan.cand_stride * 4);
     } else if (path == QSA_PATH_FILTER) {
@@ -219,14 +218,13 @@ qsa_status run_topk(const TopkGeom &g, const TopkPlan &plan, void *ws, hipStream
     const TopkLayout &L = plan.lay;
     SplitArgs sa;
     sa.g = g;
-    sa.tickets = at<uint32_t>(ws, L.split_tickets);
     sa.cand_keys = at<uint32_t>(ws, L.split_keys);
     sa.cand_blocks = at<int32_t>(ws, L.split_blocks);
     sa.cand_stride = plan.cand_stride;
     sa.chunk = p.chunk_blocks;
     sa.n_chunks = p.n_chunks;
     const int64_t stage_b = p.stage_b_lds ? plan.cand_stride : 0;
-    sa.lds_words = (int32_t)(stage_b > p.chunk_blocks ? stage_b : p.chunk_blocks);
+    sa.lds_words = p.chunk_blocks;
     sa.blk_words = (int32_t)stage_b;
     return launch_split(sa, s) == hipSuccess ? QSA_OK : QSA_EHIP;
 }

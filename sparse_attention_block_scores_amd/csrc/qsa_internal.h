@@ -11,7 +11,8 @@
 namespace qsa {
 
 // ---------------------------------------------------------------- top-k
-constexpr int kSplitThreads = 512;        // workgroup of the exact split kernel
+constexpr int kSplitThreads = 512;        // workgroup of the exact split's stage A
+constexpr int kSplitMergeThreads = 1024;  // workgroup of its stage B (one per query)
 constexpr int kOneReadThreads = 1024;     // one workgroup per query on the one-read path
 constexpr int kOneReadF4 = 4;             // float4 loads per lane and slice
 constexpr int kOneReadBuffers = 2;        // slices in flight per lane
@@ -39,7 +40,6 @@ constexpr uint32_t kFilterOverflow = 0xFFFFFFFFu;  // header count of a chunk wh
 
 // Workspace layout of the split (byte offsets, 256-byte aligned).
 struct TopkLayout {
-    size_t split_tickets;   // u32 [nq]
     size_t split_keys;      // u32 [nq][cand_stride]
     size_t split_blocks;    // i32 [nq][cand_stride]
     size_t filter_heads;    // u32 [nq][n_chunks][4]  (filtered split)
@@ -73,14 +73,13 @@ struct TopkGeom {
 
 struct SplitArgs {
     TopkGeom g;
-    uint32_t *tickets;
     uint32_t *cand_keys;
     int32_t *cand_blocks;
     int64_t cand_stride;
     int32_t chunk;
     int32_t n_chunks;
-    int32_t lds_words;      // dynamic LDS words for keys (>= chunk)
-    int32_t blk_words;      // dynamic LDS words after them for stage B's block ids (0: read from the workspace)
+    int32_t lds_words;      // stage A: dynamic LDS words for a chunk's keys (>= chunk)
+    int32_t blk_words;      // stage B: LDS words for candidate keys, as many again for their blocks (0: read from the workspace)
 };
 
 struct OneReadArgs {

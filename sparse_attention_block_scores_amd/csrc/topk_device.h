@@ -751,61 +751,4 @@ __device__ __forceinline__ void write_cells(int32_t *out, uint32_t first, uint32
             out[first + j] = cell0 + (int32_t)j;
 }
 
-// ------------------------------------------------------------ hand-off
-// Workgroups of one launch hand data to the last of them through global
-// memory without device-scope fences. On gfx950 each XCD has its own L2, and
-// a device-scope release or acquire writes back or invalidates that whole L2;
-// with many workgroups those serialise. Instead the data itself moves with
-// device-scope (sc1) accesses, as relaxed device-scope atomics are made
-// coherent: stores write through to the device level and loads read it.
-// Every thread waits for its own stores to complete before the ticket, so the
-// ticket is counted only after the data is there.
-
-// Fourth word of a raw buffer resource on gfx9-family GPUs (32-bit data
-// format, no swizzle); with stride 0 a load at or past num_records bytes
-// returns zero without a memory access.
-constexpr int kBufferWord3 = 0x00020000;
-// Cache-policy operand of a buffer load: sc1, device scope (the access a
-// relaxed device-scope atomic load makes).
-constexpr int kBufferDevice = 16;
-
-// Device-coherent store / load of one 32-bit word.
-__device__ __forceinline__ void store_dev(uint32_t *p, uint32_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t load_dev(const uint32_t *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Keys already mapped, in global memory written by other workgroups of the
-// same launch (device-coherent loads).
-struct DevKeys {
-    const uint32_t *p;
-    static constexpr bool vec = true;
-    __device__ __forceinline__ uint4 load4(int i) const
-    {
-        return make_uint4(load_dev(p + i), load_dev(p + i + 1), load_dev(p + i + 2), load_dev(p + i + 3));
-    }
-    __device__ __forceinline__ uint32_t load1(int i) const { return load_dev(p + i); }
-};
-
-// After this workgroup's store_dev writes: one ticket on `ticket`. Returns
-// true (in every thread) for the workgroup that arrives last, which may then
-// read everyone's data with load_dev.
-__device__ __forceinline__ bool last_to_arrive(uint32_t *ticket, uint32_t expected, uint32_t *s_flag)
-{
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores have completed
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_flag[0] = (prev == expected - 1) ? 1u : 0u;
-    }
-    __syncthreads();
-    return s_flag[0] != 0;
-}
-
 } // namespace qsa

@@ -1,17 +1,20 @@
 // topk_kernels.hip - block top-k kernels for gfx950.
 //
-//  * split_kernel: the exact chunked split (Strata pull #3987, section
-//    Approach). Stage A: one workgroup per (query, chunk) loads the chunk's
-//    block keys into LDS once and keeps the chunk's own top-r blocks, in block
-//    order, as candidates. Every block of the query's selection is among the
-//    candidates of its chunk: if a chunk held a selected block outside its own
-//    top r, r blocks of that chunk would precede it in (key desc, block asc)
-//    order, and the selection, which has r blocks, would not reach it. Stage
-//    B: the workgroup that finishes a query last (an atomic ticket, no
-//    waiting) selects over the candidates of all chunks with the same
-//    threshold rule and writes the cells. With one chunk the single workgroup
-//    writes the cells directly. Used for rows that fit one chunk and for rows
-//    where a sampled bound would keep a large share of the blocks.
+//  * split_kernel + split_merge_kernel: the exact chunked split (Strata pull
+//    #3987, section Approach), two launches. Stage A (split_kernel): one
+//    workgroup per (query, chunk) loads the chunk's block keys into LDS once
+//    and keeps the chunk's own top-r blocks, in block order, as candidates.
+//    Every block of the query's selection is among the candidates of its
+//    chunk: if a chunk held a selected block outside its own top r, r blocks
+//    of that chunk would precede it in (key desc, block asc) order, and the
+//    selection, which has r blocks, would not reach it. Stage B
+//    (split_merge_kernel, one workgroup per query, launched after stage A on
+//    the same stream so the kernel boundary orders the candidates' stores
+//    before their loads) selects over the candidates of all chunks with the
+//    same threshold rule and writes the cells. A row that fits one chunk is
+//    finished by its single stage-A workgroup. Used for rows that fit one
+//    chunk and for rows where a sampled bound would keep a large share of the
+//    blocks.
 //
 //  * oneread_kernel: the prompt path with one read of the scores (Strata
 //    pull #2093 "sm_75: the prompt path's top-k with one full read of the
@@ -71,7 +74,6 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint32_t s_keys[];
     __shared__ SelectShared sh;
-    __shared__ uint32_t s_flag[1];
     const TopkGeom g = a.g;
     const int q = blockIdx.y;
     const int c = blockIdx.x;
@@ -114,19 +116,33 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
     }
     take_ordered<NT>(lds, nc, T, budget, 1u, 1u, sh, [&](int i, uint32_t pos, uint32_t) {
         if (pos < (uint32_t)cap_q) {
-            store_dev(ckey + pos, s_keys[i]);
-            store_dev(reinterpret_cast<uint32_t *>(cblk) + pos, (uint32_t)(b0 + i));
+            ckey[pos] = s_keys[i];
+            cblk[pos] = b0 + i;
         }
     });
-    if (!last_to_arrive(&a.tickets[q], (uint32_t)nchq, s_flag))
-        return;
+}
 
-    // Stage B: candidates of all chunks, contiguous and in block order (every
-    // chunk but the last is full).
+// Stage B, one workgroup per query whose row spans more than one chunk: the
+// candidates of all chunks are contiguous and in block order (every chunk but
+// the last holds cap_q of them).
+template <int NT>
+__global__ __launch_bounds__(NT) void split_merge_kernel(SplitArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint32_t s_keys[];
+    __shared__ SelectShared sh;
+    const TopkGeom g = a.g;
+    const int q = blockIdx.x;
+    QuerySel qs = query_sel(g, q);
+    const int nchq = (qs.n_vis + a.chunk - 1) / a.chunk;
+    if (qs.r == 0 || nchq <= 1)
+        return;  // written by stage A
+    const int r_a = qs.r + (qs.tail != 0 ? 1 : 0);
+    const int cap_q = min(r_a, a.chunk);
     const int last_n = min(r_a, qs.n_vis - (nchq - 1) * a.chunk);
     const int total = (nchq - 1) * cap_q + last_n;
     const uint32_t *gkey = a.cand_keys + (int64_t)q * a.cand_stride;
     const int32_t *gblk = a.cand_blocks + (int64_t)q * a.cand_stride;
+    clear_hists<NT>(sh);
     // A partial last block: count the candidates at or above its key. If it is
     // taken, every block with key >= its key is among the top r_a of its chunk,
     // so the count is exact; if it is not, the count still shows that (a chunk
@@ -134,37 +150,27 @@ __global__ __launch_bounds__(NT) void split_kernel(SplitArgs a)
     const uint32_t kp = qs.tail != 0 ? key_of(g.scores[(int64_t)q * g.ld + qs.n_vis - 1]) : 0u;
     if (total <= a.blk_words) {
         // Keys and block ids both to LDS: the emit then reads no global memory.
-        int32_t *s_blks = reinterpret_cast<int32_t *>(s_keys + a.lds_words);
-        // Device-coherent 16-byte loads (a buffer resource with the sc1
-        // cache policy, the same access as load_dev) of both arrays.
-        const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(gkey), (short)0, total * 4, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rb =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(gblk), (short)0, total * 4, kBufferWord3);
-        const int n4 = total >> 2;
+        int32_t *s_blks = reinterpret_cast<int32_t *>(s_keys + a.blk_words);
+        const int n4 = total >> 2;  // the candidate arrays start 16-byte aligned
         for (int i = threadIdx.x; i < n4; i += NT) {
-            *reinterpret_cast<uint4 *>(s_keys + 4 * i) =
-                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * i, 0, kBufferDevice));
-            *reinterpret_cast<uint4 *>(s_blks + 4 * i) =
-                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * i, 0, kBufferDevice));
+            *reinterpret_cast<uint4 *>(s_keys + 4 * i) = reinterpret_cast<const uint4 *>(gkey)[i];
+            *reinterpret_cast<int4 *>(s_blks + 4 * i) = reinterpret_cast<const int4 *>(gblk)[i];
         }
         for (int i = (n4 << 2) + (int)threadIdx.x; i < total; i += NT) {
-            s_keys[i] = load_dev(gkey + i);
-            s_blks[i] = (int32_t)load_dev(reinterpret_cast<const uint32_t *>(gblk) + i);
+            s_keys[i] = gkey[i];
+            s_blks[i] = gblk[i];
         }
         lds_barrier();
+        const LdsKeys lds{s_keys};
         if (qs.tail != 0)
             widen_for_tail(qs, g.bs, count_at_least<NT>(lds, total, kp, sh));
         select_cells<NT>(lds, total, qs, [&](int i) { return s_blks[i]; }, g, q, sh);
     } else {
+        const GlobalKeys keys{gkey};
         if (qs.tail != 0)
-            widen_for_tail(qs, g.bs, count_at_least<NT>(DevKeys{gkey}, total, kp, sh));
-        select_cells<NT>(DevKeys{gkey}, total, qs,
-                         [&](int i) { return (int32_t)load_dev(reinterpret_cast<const uint32_t *>(gblk) + i); }, g,
-                         q, sh);
+            widen_for_tail(qs, g.bs, count_at_least<NT>(keys, total, kp, sh));
+        select_cells<NT>(keys, total, qs, [&](int i) { return gblk[i]; }, g, q, sh);
     }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&a.tickets[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ one read
@@ -492,14 +498,18 @@ hipError_t launch_split(const SplitArgs &a, hipStream_t s)
     // the default limit. The attribute belongs to the kernel function, so it
     // is set once per process; the function-local static is initialised by
     // exactly one thread (the C++ guarantee), others wait for its result.
-    static const hipError_t lds_limit = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&split_kernel<kSplitThreads>), hipFuncAttributeMaxDynamicSharedMemorySize,
-        2 * kStageBLdsWords * 4);
+    static const hipError_t lds_limit =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&split_merge_kernel<kSplitMergeThreads>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBLdsWords * 4);
     if (lds_limit != hipSuccess)
         return lds_limit;
     const dim3 grid((unsigned)a.n_chunks, (unsigned)a.g.nq);
-    hipLaunchKernelGGL(split_kernel<kSplitThreads>, grid, dim3(kSplitThreads),
-                       (size_t)(a.lds_words + a.blk_words) * 4, s, a);
+    hipLaunchKernelGGL(split_kernel<kSplitThreads>, grid, dim3(kSplitThreads), (size_t)a.lds_words * 4, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.n_chunks <= 1)
+        return e;
+    hipLaunchKernelGGL(split_merge_kernel<kSplitMergeThreads>, dim3((unsigned)a.g.nq), dim3(kSplitMergeThreads),
+                       (size_t)(2 * a.blk_words) * 4, s, a);
     return hipGetLastError();
 }
 

@@ -185,6 +185,25 @@ def test_workspace_reused_across_calls_of_different_sizes():
         assert_ids_equal(got, oracle.topk_sort(s, nb, 4, 2048), f"reuse {j}")
 
 
+@pytest.mark.parametrize("path", ["split", "split516", "filter", "filter_fallback", "fallback"])
+def test_workspace_needs_no_set_up(path):
+    """Every path reads back only what the same call wrote: a workspace full of
+    0xFF bytes gives the oracle's ids (prompt rows with a partial last block,
+    so the split's stage B also counts the tail's candidates)."""
+    dev = device()
+    nq, nb, bs, width = 6, 40000, 3, 3001
+    active = [nb, nb - 1, 39000, 12345, 4200, 1]
+    opt = _opts(path)
+    need = qsa.topk_workspace_bytes(nq, nb, bs, width, "prompt", opt)
+    ws = qsa.workspace(need, dev)
+    s = _keys(f"gpu/noset/{path}", "normal", nq, nb, nb)
+    for j in range(2):
+        ws.fill_(0xFF)
+        say(f"unset workspace path={path} call {j}")
+        got = gpu_topk(s, nb, bs, width, "prompt", active=active, options=opt, ws=ws)
+        assert_ids_equal(got, oracle.topk_sort(s, nb, bs, width, active), f"unset workspace {path} {j}")
+
+
 def test_two_streams_with_separate_workspaces():
     dev = device()
     a = _keys("gpu/streams/a", "normal", 4, 50000, 50000)
