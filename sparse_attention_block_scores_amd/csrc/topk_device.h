@@ -79,6 +79,16 @@ __device__ __forceinline__ uint32_t wave_incl_max(uint32_t x)
     return x;
 }
 
+// Sum of x over lanes 0-15 (the first row), in every lane.
+__device__ __forceinline__ uint32_t row0_sum(uint32_t x)
+{
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+}
+
 __device__ __forceinline__ uint32_t wave_sum(uint32_t x)
 {
     return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(x), 63);
@@ -113,6 +123,14 @@ __device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t d) { lds_add(&
 
 // ------------------------------------------------------------ key sources
 // Keys in LDS (16-byte aligned array).
+// Fourth word of a raw buffer resource on gfx9-family GPUs (32-bit data
+// format, no swizzle); with stride 0 a load at or past num_records bytes reads
+// zero without a memory access.
+constexpr int kRowBufferWord3 = 0x00020000;
+// Cache-policy operand of a buffer load: nontemporal (the hint a
+// __builtin_nontemporal_load gives a global load).
+constexpr int kCachePolicyNontemporal = 2;
+
 struct LdsKeys {
     const uint32_t *p;
     static constexpr bool vec = true;
@@ -201,6 +219,7 @@ struct SelectShared {
     uint32_t small[kWave];                // keys of one fine bin
     uint32_t small_n;
     uint32_t bcast;                       // one value from one wave to all
+    alignas(16) uint32_t pick[4];         // a pick from one wave to all
     uint32_t red[2][NW];
     uint32_t wave_ties[NW];
     uint32_t wave_gts[NW];

@@ -201,9 +201,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     __shared__ uint32_t s_ssrc[MAXS];   // ... where they start in the list of ...
     __shared__ uint32_t s_swave[MAXS];  // ... this wave
     __shared__ uint32_t s_next;         // next slice to claim
-    __shared__ uint32_t s_wtot[NW];
-    __shared__ uint32_t s_wmax[NW];
-    __shared__ uint32_t s_wmin[NW];
+    __shared__ uint4 s_tot;             // candidates, any wave over its cap, largest and smallest kept key
 
     const TopkGeom g = a.g;
     const int q = blockIdx.x;
@@ -227,17 +225,25 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     const bool use_bound = !a.force_flag && (uint32_t)sg.ns >= sg.ks;
     const int nslices = (n + STEP - 1) / STEP;  // <= MAXS (the dispatch sees to it)
 
-    // Every load below is unconditional: a lane with nothing to read re-reads
-    // block 0 (the row has at least one visible block here) and the value is
-    // ignored. A load under a branch makes the compiler lose count of the
-    // loads in flight and wait for all of them before the next use.
+    // Every load below is unconditional: a load under a branch makes the
+    // compiler lose count of the loads in flight and wait for all of them
+    // before the next use. 16-byte loads go through a buffer resource over
+    // the row's visible blocks, rounded up to whole float4 groups (inside the
+    // row: ld is a multiple of 4 here): a slice past the row lies outside it
+    // and reads zeros without a memory access, so the loads the last rounds
+    // issue past the row cost no memory round trip before the tail. The
+    // scalar path re-reads block 0 instead (the row has at least one visible
+    // block here); the values are ignored.
+    const __amdgpu_buffer_rsrc_t rrow = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(row), (short)0, ((n + 3) & ~3) * 4, kRowBufferWord3);
     auto load_slice = [&](int sl, float4 (&v)[F4]) {
 #pragma unroll
         for (int j = 0; j < F4; ++j) {
             const int i0 = sl * STEP + j * 4 * kWave + 4 * lane;
             if constexpr (VEC) {
                 // Streamed once: nontemporal loads keep it from displacing cached data.
-                const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + (i0 < n ? i0 : 0)));
+                const f32x4 t = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrow, 4 * i0, 0, kCachePolicyNontemporal));
                 v[j] = make_float4(t[0], t[1], t[2], t[3]);
             } else {
                 v[j].x = row[i0 < n ? i0 : 0];
@@ -267,8 +273,10 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     for (int u = 0; u < NBUF; ++u)
         cs[u] = u * NW + wid;
     load_slice(cs[0], buf[0]);
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
         s_next = NBUF * NW;
+        s_tot = make_uint4(0u, 0u, 0u, 0xFFFFFFFFu);
+    }
     lds_barrier();
     // One read: keep blocks with value >= fbound (every block without a
     // bound), in block order, up to WCAP per wave. The key map preserves order
@@ -373,26 +381,22 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     }
     // Keys must be finite, so the largest (smallest) kept float has the
     // largest (smallest) key.
+    // Totals, overflow and the kept keys' range, gathered by LDS atomics.
     const uint32_t wmax = wave_max(key_of(fmx));
     const uint32_t wmin = wave_min(key_of(fmn));
     if (lane == 0) {
-        s_wtot[wid] = wcnt;
-        s_wmax[wid] = wmax;
-        s_wmin[wid] = wmin;
+        __hip_atomic_fetch_add(&s_tot.x, wcnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_or(&s_tot.y, wcnt > (uint32_t)WCAP ? 1u : 0u, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_max(&s_tot.z, wmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_min(&s_tot.w, wmin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     lds_barrier();
-
-    // Totals, overflow and the kept keys' range.
-    uint32_t total = 0, kmax = 0, kmin = 0xFFFFFFFFu;
-    bool over = false;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const uint32_t c = s_wtot[w];
-        total += c;
-        over = over || c > (uint32_t)WCAP;
-        kmax = max(kmax, s_wmax[w]);
-        kmin = min(kmin, s_wmin[w]);
-    }
+    const uint4 tot = s_tot;
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readfirstlane((int)tot.x);
+    const bool over = __builtin_amdgcn_readfirstlane((int)tot.y) != 0;
+    const uint32_t kmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)tot.z);
+    const uint32_t kmin = (uint32_t)__builtin_amdgcn_readfirstlane((int)tot.w);
     // Every visible block kept and all of one key: ties go to the lowest
     // cells, so the selection is the first cells.
     if (total == (uint32_t)n && kmin == kmax) {
@@ -427,7 +431,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         const uint32_t kbase = use_bound ? key_of(fbound) : kmin;
         const int sF = cand_fine_shift(kmax - kbase);
         const bool bins = kmax != kbase;
-        const uint32_t wtot = s_wtot[wid];
+        const uint32_t wtot = wcnt;
         uint32_t gcnt = 0;
         // Four items per lane per round, all reads issued before any write.
 #pragma unroll 1

@@ -220,35 +220,45 @@ __device__ __forceinline__ void select_from_candidates(const uint32_t *ck, const
                                                        SelectShared &sh)
 {
     constexpr int NW = NT / kWave;
+    static_assert(NW <= 16 && (NW & (NW - 1)) == 0, "wave totals fit one row of lanes");
     constexpr int PER = kOneReadCap / NT;
     const int lane = lane_id(), wid = wave_id();
     const uint32_t span = kmax - kmin;
     const int sF = cand_fine_shift(span);
     const int per = (total + NT - 1) / NT;
+    // Slots j >= per (a workgroup-uniform bound) are never read.
     uint32_t k[PER];
     int32_t blk[PER];
     bool v[PER];
     const int c0 = (int)threadIdx.x * per;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        v[j] = false;
-        k[j] = 0;
-        blk[j] = 0;
-        if (j < per) {  // workgroup-uniform
-            v[j] = c0 + j < total;
-            const int i = v[j] ? c0 + j : 0;
-            k[j] = ck[i];
-            blk[j] = cb[i];
-        }
+        if (j >= per)
+            break;
+        v[j] = c0 + j < total;
+        const int i = v[j] ? c0 + j : 0;
+        k[j] = ck[i];
+        blk[j] = cb[i];
     }
 
     // Threshold: the fine bin holding rank r usually holds a handful of keys,
     // which one wave ranks exactly; a crowded one goes on with radix digits
-    // over its keys.
+    // over its keys. The tail's time is mostly instruction issue, shared by
+    // the four waves of each SIMD, so work that does not depend on a wave's
+    // own candidates runs in one wave and is handed on through LDS.
     uint32_t T = kmin, above = 0;
     if (span != 0) {
-        uint32_t b, c, h;
-        pick_fine<NT>(sh, (uint32_t)qs.r, b, c, h);
+        if (wid == 0) {
+            uint32_t pb, pc, ph;
+            pick_fine<NT>(sh, (uint32_t)qs.r, pb, pc, ph);
+            if (lane == 0)
+                *reinterpret_cast<uint4 *>(sh.pick) = make_uint4(pb, pc, ph, 0u);
+        }
+        lds_barrier();
+        const uint4 pk = *reinterpret_cast<const uint4 *>(sh.pick);
+        const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane((int)pk.x);
+        const uint32_t c = (uint32_t)__builtin_amdgcn_readfirstlane((int)pk.y);
+        const uint32_t h = (uint32_t)__builtin_amdgcn_readfirstlane((int)pk.z);
         const uint32_t blo = kmin + (b << sF);
         const uint32_t bspan = sF == 0 ? 0u : min(span - (b << sF), (1u << sF) - 1u);
         const uint32_t r2 = (uint32_t)qs.r - h;
@@ -292,10 +302,9 @@ __device__ __forceinline__ void select_from_candidates(const uint32_t *ck, const
     if (lane == kWave - 1)
         sh.red[0][wid] = incl;
     lds_barrier();
-    uint32_t before = incl - packed;
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-        before += w < wid ? sh.red[0][w] : 0u;
+    // The packed totals of the waves before this one: lane w < NW reads
+    // wave w's, and one row sum adds them.
+    uint32_t before = incl - packed + row0_sum(lane < wid ? sh.red[0][lane & (NW - 1)] : 0u);
     uint32_t ties_before = before >> 16;
     const uint32_t bs = (uint32_t)g.bs;
     const uint32_t shortfall = bs - (uint32_t)qs.last_unit;
