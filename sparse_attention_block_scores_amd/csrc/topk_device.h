@@ -89,6 +89,16 @@ __device__ __forceinline__ uint32_t row0_sum(uint32_t x)
     return (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
 }
 
+// Largest x over lanes 0-15, in every lane.
+__device__ __forceinline__ uint32_t row0_max(uint32_t x)
+{
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+}
+
 __device__ __forceinline__ uint32_t wave_sum(uint32_t x)
 {
     return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(x), 63);
@@ -269,13 +279,12 @@ __device__ __forceinline__ void wg_minmax(uint32_t lo, uint32_t hi, SelectShared
         sh.red[1][wave_id()] = hi;
     }
     lds_barrier();
-    mn = 0xFFFFFFFFu;
-    mx = 0u;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        mn = min(mn, sh.red[0][w]);
-        mx = max(mx, sh.red[1][w]);
-    }
+    // Lane w < NW reads wave w's; one row reduction each (max(~x) = ~min).
+    static_assert(NW <= 16, "wave results fit one row of lanes");
+    const int l = lane_id();
+    const bool in = l < NW;
+    mn = ~row0_max(in ? ~sh.red[0][l & 15] : 0u);
+    mx = row0_max(in ? sh.red[1][l & 15] : 0u);
     lds_barrier();
 }
 

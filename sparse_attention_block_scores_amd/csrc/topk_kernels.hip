@@ -192,8 +192,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     constexpr int WCAP = kOneReadCap / NW;                // candidates a wave may keep
     constexpr int SPT = kOneReadSample / NT;              // sample keys per thread
     static_assert(kOneReadBatch == NW * STEP, "a batch is one slice per wave");
-    __shared__ __attribute__((aligned(16))) uint32_t s_wkey[kOneReadCap];  // per-wave candidates: FP32 bits
-    __shared__ __attribute__((aligned(16))) int32_t s_wblk[kOneReadCap];
+    __shared__ __attribute__((aligned(16))) uint2 s_wlist[kOneReadCap];    // per-wave candidates: (FP32 bits, block)
     __shared__ __attribute__((aligned(16))) uint32_t s_ckey[kOneReadCap];  // candidates in block order
     __shared__ __attribute__((aligned(16))) int32_t s_cblk[kOneReadCap];
     __shared__ SelectShared sh;
@@ -201,7 +200,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     __shared__ uint32_t s_ssrc[MAXS];   // ... where they start in the list of ...
     __shared__ uint32_t s_swave[MAXS];  // ... this wave
     __shared__ uint32_t s_next;         // next slice to claim
-    __shared__ uint4 s_tot;             // candidates, any wave over its cap, largest and smallest kept key
+    __shared__ uint4 s_tot;             // candidates, any wave over its cap, largest kept key
 
     const TopkGeom g = a.g;
     const int q = blockIdx.x;
@@ -275,7 +274,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     load_slice(cs[0], buf[0]);
     if (threadIdx.x == 0) {
         s_next = NBUF * NW;
-        s_tot = make_uint4(0u, 0u, 0u, 0xFFFFFFFFu);
+        s_tot = make_uint4(0u, 0u, 0u, 0u);
     }
     lds_barrier();
     // One read: keep blocks with value >= fbound (every block without a
@@ -289,10 +288,10 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         load_slice(cs[u], buf[u]);
 
     uint32_t wcnt = 0;               // wave-uniform
-    float fmx = -__builtin_inff();   // largest and smallest value this lane kept
-    float fmn = __builtin_inff();
-    uint32_t *wkey = s_wkey + wid * WCAP;
-    int32_t *wblk = s_wblk + wid * WCAP;
+    // Largest value this lane kept (med3 with +inf is max for finite values,
+    // without the canonicalising steps fmaxf takes).
+    float fmx = -__builtin_inff();
+    uint2 *wlist = s_wlist + wid * WCAP;
     auto consume = [&](int sl, const float4 (&v)[F4], auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;  // every block of the slice is visible
         const int step0 = sl * STEP;
@@ -318,13 +317,14 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
                 // Common case: no lane keeps more than one of its four keys, so
                 // a lane's slot is the number of keeping lanes below it.
                 if (keep[0] || keep[1] || keep[2] || keep[3]) {
-                    const float x = keep[0] ? f[0] : (keep[1] ? f[1] : (keep[2] ? f[2] : f[3]));
-                    const int sel = keep[0] ? 0 : (keep[1] ? 1 : (keep[2] ? 2 : 3));
+                    // The kept key's place in the group as two bits (i0 is a
+                    // multiple of 4).
+                    const bool hi = keep[2] || keep[3], odd = keep[1] || keep[3];
+                    const float x = hi ? (odd ? f[3] : f[2]) : (odd ? f[1] : f[0]);
+                    const int sel = (hi ? 2 : 0) | (odd ? 1 : 0);
                     const uint32_t pos = min(wcnt + count_below(any), (uint32_t)(WCAP - 1));
-                    wkey[pos] = __float_as_uint(x);
-                    wblk[pos] = i0 + sel;
-                    fmx = x > fmx ? x : fmx;
-                    fmn = x < fmn ? x : fmn;
+                    wlist[pos] = make_uint2(__float_as_uint(x), (uint32_t)(i0 | sel));
+                    fmx = __builtin_amdgcn_fmed3f(x, fmx, __builtin_inff());
                 }
                 wcnt += (uint32_t)__popcll(any);
                 continue;
@@ -340,10 +340,8 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             for (int s = 0; s < 4; ++s) {
                 if (keep[s]) {
                     const uint32_t p = min(pos, (uint32_t)(WCAP - 1));
-                    wkey[p] = __float_as_uint(f[s]);
-                    wblk[p] = i0 + s;
-                    fmx = f[s] > fmx ? f[s] : fmx;
-                    fmn = f[s] < fmn ? f[s] : fmn;
+                    wlist[p] = make_uint2(__float_as_uint(f[s]), (uint32_t)(i0 + s));
+                    fmx = __builtin_amdgcn_fmed3f(f[s], fmx, __builtin_inff());
                     ++pos;
                 }
             }
@@ -379,27 +377,28 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         if (done)
             break;
     }
-    // Keys must be finite, so the largest (smallest) kept float has the
-    // largest (smallest) key.
-    // Totals, overflow and the kept keys' range, gathered by LDS atomics.
+    // Totals, overflow and the largest kept key, gathered by LDS atomics
+    // (keys are finite, so the largest kept float has the largest key).
     const uint32_t wmax = wave_max(key_of(fmx));
-    const uint32_t wmin = wave_min(key_of(fmn));
     if (lane == 0) {
         __hip_atomic_fetch_add(&s_tot.x, wcnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         __hip_atomic_fetch_or(&s_tot.y, wcnt > (uint32_t)WCAP ? 1u : 0u, __ATOMIC_RELAXED,
                               __HIP_MEMORY_SCOPE_WORKGROUP);
         __hip_atomic_fetch_max(&s_tot.z, wmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_fetch_min(&s_tot.w, wmin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     lds_barrier();
     const uint4 tot = s_tot;
     const uint32_t total = (uint32_t)__builtin_amdgcn_readfirstlane((int)tot.x);
     const bool over = __builtin_amdgcn_readfirstlane((int)tot.y) != 0;
     const uint32_t kmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)tot.z);
-    const uint32_t kmin = (uint32_t)__builtin_amdgcn_readfirstlane((int)tot.w);
+    // Every candidate key is >= kbase: the bound's key (the key map keeps
+    // order, so value >= bound means key >= key(bound)), or 0 without one.
+    const uint32_t kbase = use_bound ? key_of(fbound) : 0u;
     // Every visible block kept and all of one key: ties go to the lowest
-    // cells, so the selection is the first cells.
-    if (total == (uint32_t)n && kmin == kmax) {
+    // cells, so the selection is the first cells. With a bound, that is
+    // total == n and a largest key equal to the bound's (every key lies in
+    // [kbase, kmax]); without one, the exact rule below sees it.
+    if (use_bound && total == (uint32_t)n && kmax == kbase) {
         write_first_cells<NT>(g, q, qs.wq);
         return;
     }
@@ -426,29 +425,31 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
         // The copy into block order also counts every candidate into the
-        // fine bins over [kmin, kmax] (every candidate key lies there) and
-        // the candidates at or above a partial last block's key.
-        const uint32_t kbase = use_bound ? key_of(fbound) : kmin;
+        // fine bins over [kbase, kmax] and the candidates at or above a
+        // partial last block's key.
         const int sF = cand_fine_shift(kmax - kbase);
         const bool bins = kmax != kbase;
         const uint32_t wtot = wcnt;
         uint32_t gcnt = 0;
-        // Four items per lane per round, all reads issued before any write.
+        // CPR items per lane per round, all reads issued before any write (a
+        // wave keeps about 3r/16 candidates, so one round usually suffices).
+        constexpr int CPR = 2;
 #pragma unroll 1
-        for (uint32_t i0 = (uint32_t)lane; i0 < wtot; i0 += 4 * kWave) {
-            int32_t blk[4];
-            uint32_t raw[4], shift[4];
+        for (uint32_t i0 = (uint32_t)lane; i0 < wtot; i0 += CPR * kWave) {
+            int32_t blk[CPR];
+            uint32_t raw[CPR], shift[CPR];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < CPR; ++u) {
                 const uint32_t i = i0 + u * kWave < wtot ? i0 + u * kWave : 0u;
-                blk[u] = wblk[i];
-                raw[u] = wkey[i];
+                const uint2 e = wlist[i];
+                raw[u] = e.x;
+                blk[u] = (int32_t)e.y;
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < CPR; ++u)
                 shift[u] = s_ssrc[blk[u] / STEP];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < CPR; ++u) {
                 if (i0 + u * kWave < wtot) {
                     const uint32_t d = i0 + u * kWave + shift[u];
                     const uint32_t k = key_of(__uint_as_float(raw[u]));

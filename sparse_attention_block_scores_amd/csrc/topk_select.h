@@ -276,7 +276,17 @@ __device__ __forceinline__ void select_from_candidates(const uint32_t *ck, const
                 }
             }
             lds_barrier();
-            wave_rank_small(sh.small, c, r2, T, a2);
+            // One wave ranks the bin's keys and hands (T, above) on.
+            if (wid == 0) {
+                uint32_t t0, a0;
+                wave_rank_small(sh.small, c, r2, t0, a0);
+                if (lane == 0)
+                    *reinterpret_cast<uint2 *>(sh.pick) = make_uint2(t0, a0);
+            }
+            lds_barrier();
+            const uint2 ta = *reinterpret_cast<const uint2 *>(sh.pick);
+            T = (uint32_t)__builtin_amdgcn_readfirstlane((int)ta.x);
+            a2 = (uint32_t)__builtin_amdgcn_readfirstlane((int)ta.y);
         } else {
             // Digits over the bin's interval (sh.hist; the fine bins stay as they are).
             radix_select_range<NT>(LdsKeys{ck}, total, r2, blo, blo + bspan, sh, T, a2);
