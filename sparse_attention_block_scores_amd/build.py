@@ -24,6 +24,13 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+# The top-k kernels issue their few workgroup atomics from one lane; the
+# compiler's atomic optimizer would wrap each in a wave-wide reduction loop
+# (scalar instructions the tail pays for in every wave).
+SOURCE_FLAGS = {
+    "topk_kernels.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+    "topk_filter.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+}
 
 
 def hipcc() -> str:
@@ -39,7 +46,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objects.append(obj)
-        cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
