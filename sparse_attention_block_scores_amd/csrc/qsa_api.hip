@@ -115,14 +115,18 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
     // Dispatch (measured on MI355X; results never depend on it). A row that
     // fits one chunk is selected in LDS by one workgroup. Longer rows take a
     // sampled-bound path while its candidates are a small share of the row
-    // (the bound keeps about 3r blocks); otherwise the split. Among those, a
-    // few queries with long rows spread each row over chunk workgroups (the
-    // filtered split: one workgroup per query streams too slowly to fill the
-    // GPU); many queries take one workgroup each (one read, one launch).
+    // (the bound keeps about 3r blocks); otherwise the split. Among those, up
+    // to 16 queries with rows of at least 65,536 + 2,048 nq blocks spread
+    // each row over chunk workgroups (the filtered split: there one workgroup
+    // per query streams too long); the rest take one workgroup per query (one
+    // read, one launch).
     int path = opt ? opt->topk_path : QSA_PATH_AUTO;
     if (path == QSA_PATH_AUTO) {
         if (n_blocks > kChunkBound && (int64_t)n_blocks >= (int64_t)kOneReadMinRatio * p.r_blocks)
-            path = (nq <= kFilterMaxQueries && n_blocks >= kFilterMinBlocks) ? QSA_PATH_FILTER : QSA_PATH_ONEREAD;
+            path = (nq <= kFilterMaxQueries &&
+                    (int64_t)n_blocks >= (int64_t)kFilterMinBlocks + (int64_t)kFilterBlocksPerQuery * nq)
+                       ? QSA_PATH_FILTER
+                       : QSA_PATH_ONEREAD;
         else
             path = QSA_PATH_SPLIT;
     }

@@ -34,8 +34,9 @@ constexpr int kFilterMinChunk = 1024;     // blocks per stage-A chunk: 1024 * (1
 constexpr int kFilterMaxChunk = 8192;
 constexpr int kFilterMaxChunks = 1024;    // chunks per row (stage B scans one header per thread)
 constexpr int kFilterTargetGroups = 512;  // stage-A workgroups the chunk size aims for
-constexpr int kFilterMinBlocks = 32768;   // the dispatch's filtered split: rows of at least this many blocks ...
-constexpr int kFilterMaxQueries = 32;     // ... in calls of at most this many queries
+constexpr int kFilterMinBlocks = 65536;   // the dispatch's filtered split: rows of at least this many blocks ...
+constexpr int kFilterBlocksPerQuery = 2048;  // ... plus this many per query ...
+constexpr int kFilterMaxQueries = 16;     // ... in calls of at most this many queries
 constexpr uint32_t kFilterOverflow = 0xFFFFFFFFu;  // header count of a chunk whose slot overflowed
 
 // Workspace layout of the split (byte offsets, 256-byte aligned).

@@ -49,14 +49,18 @@ def test_dispatch_rule():
     assert qsa.topk_plan(3, 8191, 4, 2048, "decode")["path"] == qsa.PATH_SPLIT
     assert qsa.topk_plan(3, 8192, 4, 2048, "decode")["path"] == qsa.PATH_ONEREAD
     assert qsa.topk_plan(3, 4105, 4, 256, "decode")["path"] == qsa.PATH_ONEREAD
-    for nq, nb, call in ((3, 10240, "decode"), (3, 16384, "decode"), (256, 32768, "prompt"),
-                         (256, 130048, "prompt"), (33, 65536, "decode")):
+    # The filtered split for up to 16 queries with rows of at least
+    # 65,536 + 2,048 nq blocks.
+    for nq, nb, call in ((3, 10240, "decode"), (3, 16384, "decode"), (3, 32768, "decode"), (3, 64512, "decode"),
+                         (16, 65536, "decode"), (16, 98303, "decode"), (17, 130048, "decode"),
+                         (256, 32768, "prompt"), (256, 130048, "prompt"), (33, 65536, "decode")):
         assert qsa.topk_plan(nq, nb, 4, 2048, call)["path"] == qsa.PATH_ONEREAD, (nq, nb)
-    for nq, nb, call in ((3, 32768, "decode"), (3, 64512, "decode"), (16, 65536, "decode"), (32, 40000, "prompt")):
+    for nq, nb, call in ((1, 67584, "decode"), (3, 71680, "decode"), (3, 130048, "decode"), (16, 98304, "decode"),
+                         (8, 130048, "prompt")):
         assert qsa.topk_plan(nq, nb, 4, 2048, call)["path"] == qsa.PATH_FILTER, (nq, nb)
     # chunk sizes for about 512 first-launch workgroups
-    assert qsa.topk_plan(3, 64512, 4, 2048, "decode")["filter_blocks"] == 1024
-    assert qsa.topk_plan(16, 65536, 4, 2048, "decode")["filter_blocks"] == 2048
+    assert qsa.topk_plan(3, 130048, 4, 2048, "decode")["filter_blocks"] == 1024
+    assert qsa.topk_plan(16, 130048, 4, 2048, "decode")["filter_blocks"] == 4096
 
 
 def test_filter_geometry():

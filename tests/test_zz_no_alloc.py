@@ -9,6 +9,7 @@ import torch
 
 import oracle
 import sparse_attention_block_scores_amd as qsa
+from sparse_attention_block_scores_amd import _binding as B
 import synth
 from qsa_testutil import assert_ids_equal, device, say, to_dev
 
@@ -22,19 +23,19 @@ def _scores(tag, nq, nb, ld, quantized=False):
     return s
 
 
-# (nq, n_blocks, block_size, width, call, key variant): each call smaller than
-# the one before; the paths the dispatch takes are in the ids.
+# (nq, n_blocks, block_size, width, call, key variant, path the dispatch
+# takes): each call smaller than the one before.
 CALLS = [
-    (16, 65536, 4, 2048, "decode", False),   # filtered split (two launches)
-    (3, 40000, 4, 2048, "decode", True),     # filtered split, 64-level keys
-    (5, 20000, 3, 777, "prompt", False),     # one-read, ragged active counts
-    (2, 3000, 4, 256, "decode", False),      # split, one chunk
+    (8, 130048, 4, 2048, "decode", False, qsa.PATH_FILTER),   # filtered split (two launches)
+    (3, 100000, 4, 2048, "decode", True, qsa.PATH_FILTER),    # filtered split, 64-level keys
+    (5, 20000, 3, 777, "prompt", False, qsa.PATH_ONEREAD),    # one-read, ragged active counts
+    (2, 3000, 4, 256, "decode", False, qsa.PATH_SPLIT),       # split, one chunk
 ]
 
 
 def test_noalloc_matches_workspace_entry_point():
     dev = device()
-    for j, (nq, nb, bs, width, call, q64) in enumerate(CALLS):
+    for j, (nq, nb, bs, width, call, q64, path) in enumerate(CALLS):
         ld = nb + (j % 3) * 4
         s = _scores(f"gpu/noalloc/{j}", nq, nb, ld, q64)
         active = None
@@ -42,6 +43,8 @@ def test_noalloc_matches_workspace_entry_point():
             active = synth.integers(f"gpu/noalloc/{j}/active", nq, 0, nb + 3).astype(np.int32)
             active[0] = nb
         plan = qsa.topk_plan(nq, nb, bs, width, call)
+        assert plan["path"] == path, (j, plan["path"])
+        assert plan["workspace_bytes"] <= B.NOALLOC_SCRATCH_BYTES
         say(f"noalloc call {j}: nq={nq} nb={nb} bs={bs} w={width} {call} path={plan['path']}")
         sd = to_dev(s)
         act = None if active is None else to_dev(active)
