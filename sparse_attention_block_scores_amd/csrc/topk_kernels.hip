@@ -256,9 +256,11 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         }
     };
 
-    // The sample goes into registers first (SPT per thread), then the first
-    // slice of every wave is issued behind it: a wave stalls while the memory
-    // queue is full, and the bound needs every wave.
+    // The sample goes into registers first (SPT per thread) and is waited
+    // for before the first slice of every wave is issued: the bound needs
+    // every wave's sample, and a sample queued behind the whole chip's first
+    // slices arrives later (measured 0.2-0.6 us per call). The second slice
+    // follows the bound: a wave stalls while its memory queue is full.
     float smp[SPT];
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
@@ -271,6 +273,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
 #pragma unroll
     for (int u = 0; u < NBUF; ++u)
         cs[u] = u * NW + wid;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the sample is in registers
     load_slice(cs[0], buf[0]);
     if (threadIdx.x == 0) {
         s_next = NBUF * NW;
