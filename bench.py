@@ -297,6 +297,40 @@ def attention_figures(torch, qsa, synth, dev, time_us):
                           "rotated_hbm_frac": round(gathered / us_r / 1e3 / PEAK_HBM_GBS, 3)})
         att[wla.name] = entry
         del ks, vs, qa, ids_a, oa, la, wsa
+
+    # A6: the shared-block path (pairs of neighbouring queries over their
+    # merged lists) against the plain one on the same lists, both over three
+    # rotated key/value copies; "unique" bytes are the rows of each pair's
+    # distinct cells, the gather the shared path needs.
+    wl6 = synth.a6()
+    qh, kh, vh = wl6.tensors()
+    sel = wl6.selection()
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q6, ids6 = bf16(qh), torch.from_numpy(sel).to(dev)
+    ks = [bf16(kh) for _ in range(3)]
+    vs = [bf16(vh) for _ in range(3)]
+    o6 = torch.empty((wl6.nq, wl6.heads, 128), device=dev)
+    l6 = torch.empty((wl6.nq, wl6.heads), device=dev)
+    row_bytes = wl6.kv_heads * wl6.head_dim * 2 * 2
+    unique = 0
+    for p in range(0, wl6.nq, 2):
+        rows = sel[p:p + 2]
+        unique += np.unique(rows[(rows >= 0) & (rows < wl6.n_cells)]).size
+    entry = {"listed_MiB": round(wl6.gathered_bytes(sel) / 2 ** 20, 1),
+             "unique_MiB": round(unique * row_bytes / 2 ** 20, 1)}
+    for shared in (False, True):
+        need = qsa.attention_workspace_bytes(wl6.nq, wl6.heads, wl6.kv_heads, wl6.width, shared=shared)
+        ws6 = qsa.workspace(need, dev) if need else None
+        us = time_us(lambda i: qsa.selection_attention(q6, ks[i % 3], vs[i % 3], ids6, scale=wl6.scale(), out=o6,
+                                                       lse=l6, ws=ws6, stream=cur(), shared=shared), n=30)
+        entry["shared_rotated_us" if shared else "plain_rotated_us"] = round(us, 2)
+    entry["shared_unique_GBps"] = round(unique * row_bytes / entry["shared_rotated_us"] / 1e3, 1)
+    entry["shared_hbm_frac"] = round(entry["shared_unique_GBps"] / PEAK_HBM_GBS, 3)
+    att["A6"] = entry
+    del ks, vs, q6, ids6, o6, l6
     return att
 
 

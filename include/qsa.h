@@ -293,6 +293,37 @@ qsa_status qsa_selection_attention(const void *q, const void *k, const void *v,
                                    int32_t n_cells, int32_t width, float scale,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * qsa_selection_attention_shared - qsa_selection_attention for queries whose
+ * neighbours select many of the same cells (iree-org/wave issue #1257
+ * "NSA: LDS optimization for block-gather in selection attention", section
+ * Shared block deduplication). Queries 2i and 2i+1 form a pair (with an odd
+ * nq the last query is alone); a first launch merges the pair's two lists
+ * into one list of distinct cells, each marked with the queries that listed
+ * it, and the attention then gathers each distinct cell's key and value rows
+ * once for both queries.
+ *
+ *   Arguments, results and the bfloat16/FP32 arithmetic as
+ *   qsa_selection_attention; the sums may add the same terms in another
+ *   order. Limits (else QSA_EUNSUPPORTED): n_heads / kv_heads <= 8 (a pair's
+ *   heads fill one 16-column matrix-core tile), width <= 4096 (the merge's
+ *   hash lives in LDS), n_cells < 2^30 (a merged entry packs the cell id and
+ *   the two query marks into 32 bits). A query that lists a cell more than
+ *   once counts it that often: a pair with such a repeat is not merged (each
+ *   of its entries stays separate; the result is the same).
+ *   workspace: qsa_selection_attention_shared_workspace_bytes() bytes,
+ *   256-byte aligned, never 0 (the merged lists live there); written and read
+ *   within the call, no set-up. The size function returns 0 for sizes the
+ *   call rejects.
+ */
+size_t qsa_selection_attention_shared_workspace_bytes(int32_t nq, int32_t n_heads, int32_t kv_heads,
+                                                      int32_t width);
+qsa_status qsa_selection_attention_shared(const void *q, const void *k, const void *v,
+                                          const int32_t *ids, int64_t ld_ids, float *out, float *lse,
+                                          int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t head_dim,
+                                          int32_t n_cells, int32_t width, float scale,
+                                          void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *qsa_status_str(qsa_status status);
 

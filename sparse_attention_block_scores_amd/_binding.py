@@ -96,9 +96,12 @@ def lib() -> ctypes.CDLL:
         L.qsa_selection_attention_workspace_bytes.restype = sz
         L.qsa_selection_attention.argtypes = [P, P, P, P, i64, P, P, i32, i32, i32, i32, i32, i32,
                                               ctypes.c_float, P, sz, P]
+        L.qsa_selection_attention_shared_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.qsa_selection_attention_shared_workspace_bytes.restype = sz
+        L.qsa_selection_attention_shared.argtypes = L.qsa_selection_attention.argtypes
         for name in ("qsa_block_scores", "qsa_block_scores_bf16", "qsa_topk_plan_get", "qsa_workspace_init", "qsa_block_topk",
                      "qsa_select", "qsa_block_topk_cells", "qsa_select_cells", "qsa_selection_attention",
-                     "qsa_block_topk_noalloc"):
+                     "qsa_selection_attention_shared", "qsa_block_topk_noalloc"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -270,18 +273,23 @@ def block_scores_bf16(q, k, w, scores=None, stream=None):
     return scores
 
 
-def attention_workspace_bytes(nq: int, n_heads: int, kv_heads: int, width: int) -> int:
+def attention_workspace_bytes(nq: int, n_heads: int, kv_heads: int, width: int, shared: bool = False) -> int:
+    if shared:
+        return int(lib().qsa_selection_attention_shared_workspace_bytes(nq, n_heads, kv_heads, width))
     return int(lib().qsa_selection_attention_workspace_bytes(nq, n_heads, kv_heads, width))
 
 
-def selection_attention(q, k, v, ids, width=None, scale=None, out=None, lse=None, ws=None, stream=None):
+def selection_attention(q, k, v, ids, width=None, scale=None, out=None, lse=None, ws=None, stream=None,
+                        shared=False):
     """Attention of each query head over its query's listed cells.
 
     q [nq, n_heads, 128] and k, v [n_cells, kv_heads, 128] bfloat16; ids
     [nq, ld] int32 (the first ``width`` entries of a row are the list,
     default all of them; entries outside [0, n_cells) select nothing).
-    scale defaults to 1/sqrt(128). Returns (out [nq, n_heads, 128] float32,
-    lse [nq, n_heads] float32)."""
+    scale defaults to 1/sqrt(128). shared=True takes
+    qsa_selection_attention_shared (pairs of queries over their merged
+    lists). Returns (out [nq, n_heads, 128] float32, lse [nq, n_heads]
+    float32)."""
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, torch.bfloat16, name)
         if not t.is_contiguous() or t.dim() != 3:
@@ -302,14 +310,14 @@ def selection_attention(q, k, v, ids, width=None, scale=None, out=None, lse=None
     _dev(out, torch.float32, "out"), _dev(lse, torch.float32, "lse")
     if not out.is_contiguous() or not lse.is_contiguous():
         raise ValueError("out and lse must be contiguous")
-    need = attention_workspace_bytes(nq, n_heads, kv_heads, width)
+    need = attention_workspace_bytes(nq, n_heads, kv_heads, width, shared)
     if ws is None and need > 0:
         ws = workspace(need, q.device, stream)
-    _check(lib().qsa_selection_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(ids), ids.stride(0), _ptr(out),
-                                         _ptr(lse), nq, n_heads, kv_heads, head_dim, n_cells, width, scale,
-                                         _ptr(ws) if ws is not None else None,
-                                         _nbytes(ws) if ws is not None else 0,
-                                         _stream(stream)), "qsa_selection_attention")
+    fn, name = ((lib().qsa_selection_attention_shared, "qsa_selection_attention_shared") if shared
+                else (lib().qsa_selection_attention, "qsa_selection_attention"))
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(ids), ids.stride(0), _ptr(out), _ptr(lse), nq, n_heads, kv_heads,
+              head_dim, n_cells, width, scale, _ptr(ws) if ws is not None else None,
+              _nbytes(ws) if ws is not None else 0, _stream(stream)), name)
     return out, lse
 
 

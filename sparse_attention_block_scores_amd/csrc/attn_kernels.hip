@@ -23,6 +23,16 @@
 // Loads past the wave's range are issued too, masked to cell 0 (cache hits),
 // so that no load sits under a branch and the compiler's waits stay exact.
 //
+// Shared blocks (the same issue, section Shared block deduplication): with
+// key/value groups of up to 8 heads, queries 2i and 2i+1 form a pair whose
+// two lists attn_union_kernel first merges into one list of distinct cells,
+// each entry marked with the queries that listed it (an LDS hash per pair,
+// the order that of first occurrence). attn_kernel<true> then walks the
+// merged list: its 16 matrix-core columns are the pair's heads (query 2i in
+// columns 0-7, query 2i+1 in 8-15), each distinct cell's key and value rows
+// are gathered once for both, and a cell's logits in the columns of a query
+// that did not list it are -inf (weight 0).
+//
 // Matrix cores (v_mfma_f32_16x16x32_bf16, FP32 accumulation):
 //  * S^T[16 cells x 16 heads] = K[16 cells x 128] . Q^T[128 x 16 heads] in four
 //    32-deep steps. The contraction index is permuted: in step s lane group
@@ -44,6 +54,7 @@
 #include <math.h>
 
 #include "qsa_internal.h"
+#include "topk_device.h"  // wave scans
 
 namespace qsa {
 
@@ -93,6 +104,7 @@ struct StepIds {
 struct StepRows {
     uint4 ka[4], kb[4], v0[4], v1[4];
     uint64_t ma, mb;
+    uint64_t pa[2], pb[2];  // shared blocks: the cells each query of the pair listed
     bool va, vb;
 };
 
@@ -107,14 +119,31 @@ __device__ __forceinline__ StepIds load_ids(const int32_t *row, int c0, int widt
 }
 
 // Positions at or past `limit` and ids outside [0, n_cells) select nothing;
-// their rows are read from cell 0.
-__device__ __forceinline__ void load_rows(const StepIds &s, const AttnArgs &a, int limit, int64_t kv_row,
+// their rows are read from cell 0. SHARED: an entry is a merged one, cell id
+// in the low kPairIdBits bits and the listing queries of the pair above.
+template <bool SHARED>
+__device__ __forceinline__ void load_rows(const StepIds &s0, const AttnArgs &a, int limit, int64_t kv_row,
                                           int64_t head_off, int n, StepRows &r)
 {
+    StepIds s = s0;
+    uint32_t qa = 1u, qb = 1u;
+    if constexpr (SHARED) {
+        constexpr int kIdMask = (1 << kPairIdBits) - 1;
+        qa = (uint32_t)s0.a >> kPairIdBits;
+        qb = (uint32_t)s0.b >> kPairIdBits;
+        s.a = s0.a & kIdMask;
+        s.b = s0.b & kIdMask;
+    }
     const bool va = s.c0 + n < limit && (unsigned)s.a < (unsigned)a.n_cells;
     const bool vb = s.c0 + 16 + n < limit && (unsigned)s.b < (unsigned)a.n_cells;
     r.ma = __ballot(va);
     r.mb = __ballot(vb);
+    if constexpr (SHARED) {
+        r.pa[0] = __ballot(va && (qa & 1u));
+        r.pa[1] = __ballot(va && (qa & 2u));
+        r.pb[0] = __ballot(vb && (qb & 1u));
+        r.pb[1] = __ballot(vb && (qb & 2u));
+    }
     r.va = va;
     r.vb = vb;
     // Row offsets in elements: a non-negative 31-bit id times the row length.
@@ -136,9 +165,17 @@ __device__ __forceinline__ void load_rows(const StepIds &s, const AttnArgs &a, i
 }
 
 // One step: logits, the online softmax update, and the weighted value sum.
+// SHARED: a column takes the cells its query of the pair listed.
+template <bool SHARED>
 __device__ __forceinline__ void attend(const StepRows &r, const bf16x8 (&qb)[4], float scale_log2, int n, int lg,
                                        uint32_t *vt, float &m, float &l, f32x4 (&o)[8])
 {
+    uint64_t ma = r.ma, mb = r.mb;
+    if constexpr (SHARED) {
+        const bool second = n >= kPairHeads;
+        ma = second ? r.pa[1] : r.pa[0];
+        mb = second ? r.pb[1] : r.pb[0];
+    }
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -148,8 +185,8 @@ __device__ __forceinline__ void attend(const StepRows &r, const bf16x8 (&qb)[4],
     float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        x[i] = ((r.ma >> (4 * lg + i)) & 1) ? sa[i] * scale_log2 : -INFINITY;
-        x[4 + i] = ((r.mb >> (4 * lg + i)) & 1) ? sb[i] * scale_log2 : -INFINITY;
+        x[i] = ((ma >> (4 * lg + i)) & 1) ? sa[i] * scale_log2 : -INFINITY;
+        x[4 + i] = ((mb >> (4 * lg + i)) & 1) ? sb[i] * scale_log2 : -INFINITY;
     }
     float smax = x[0];
 #pragma unroll
@@ -231,6 +268,9 @@ __device__ __forceinline__ void finish(f32x4 acc, float sum, float ref, float *d
 }
 
 // Two waves per SIMD: at most 256 VGPRs, room for two steps of rows.
+// SHARED: a unit is a pair of queries (iq below is the pair) over its merged
+// list.
+template <bool SHARED>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a)
 {
     __shared__ AttnLds sm;
@@ -254,21 +294,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a)
 
     uint32_t *vt = sm.vt[wv];
     const int32_t *idrow = a.ids + (int64_t)iq * a.ld_ids;
+    // Listed positions of the unit's list: the merged list's length, read on
+    // the device (wave-uniform), or the callers' width.
+    const int wlen = SHARED ? __builtin_amdgcn_readfirstlane(a.union_len[iq]) : a.width;
     const int64_t kv_row = (int64_t)a.kv_heads * 128;
     const int64_t head_off = (int64_t)g * 128 + 32 * lg;
     const int first = (chunk * kAttnWaves + wv) * a.steps_per_wave * kAttnStepCells;
     // Steps of this wave that hold listed positions (wave-uniform).
-    const int steps = min(a.steps_per_wave, max(0, (a.width - first + kAttnStepCells - 1) / kAttnStepCells));
-    const int limit = min(a.width, first + steps * kAttnStepCells);
+    const int steps = min(a.steps_per_wave, max(0, (wlen - first + kAttnStepCells - 1) / kAttnStepCells));
+    const int limit = min(wlen, first + steps * kAttnStepCells);
     if (steps > 0) {
         // The id loads start the dependent chain; the query rows load beside them.
-        StepIds i0 = load_ids(idrow, first, a.width, n);
-        // This lane's matrix-core column: query head hb*16 + n of the group
-        // (a padding column reads head 0 of the group and is zeroed).
-        const bool head_ok = hb * kAttnHeadBlock + n < a.group;
-        const int head = g * a.group + (head_ok ? hb * kAttnHeadBlock + n : 0);
+        StepIds i0 = load_ids(idrow, first, wlen, n);
+        // This lane's matrix-core column: query head hb*16 + n of the group,
+        // or with SHARED head n % 8 of query 2 iq + n / 8 (a padding column
+        // reads head 0 of the group and is zeroed).
+        const int qcol = SHARED ? 2 * iq + (n >= kPairHeads ? 1 : 0) : iq;
+        const int hcol = SHARED ? (n & (kPairHeads - 1)) : hb * kAttnHeadBlock + n;
+        const bool head_ok = hcol < a.group && qcol < a.nq;
+        const int head = g * a.group + (head_ok ? hcol : 0);
         const uint32_t keep = head_ok ? 0xFFFFFFFFu : 0u;
-        const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + ((int64_t)iq * a.n_heads + head) * 128 + 32 * lg);
+        const uint4 *qp = reinterpret_cast<const uint4 *>(
+            a.q + ((int64_t)(head_ok ? qcol : iq * (SHARED ? 2 : 1)) * a.n_heads + head) * 128 + 32 * lg);
         bf16x8 qb[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -277,20 +324,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a)
         }
         StepRows r0, r1;
         if (steps == 1) {  // wave-uniform: nothing to overlap (decode calls), no prefetch
-            load_rows(i0, a, limit, kv_row, head_off, n, r0);
-            attend(r0, qb, a.scale_log2, n, lg, vt, m, l, o);
+            load_rows<SHARED>(i0, a, limit, kv_row, head_off, n, r0);
+            attend<SHARED>(r0, qb, a.scale_log2, n, lg, vt, m, l, o);
         } else {
-            StepIds i1 = load_ids(idrow, first + kAttnStepCells, a.width, n);
-            load_rows(i0, a, limit, kv_row, head_off, n, r0);
+            StepIds i1 = load_ids(idrow, first + kAttnStepCells, wlen, n);
+            load_rows<SHARED>(i0, a, limit, kv_row, head_off, n, r0);
             for (int j = 0; j < steps; j += 2) {
-                i0 = load_ids(idrow, first + (j + 2) * kAttnStepCells, a.width, n);
-                load_rows(i1, a, limit, kv_row, head_off, n, r1);
-                attend(r0, qb, a.scale_log2, n, lg, vt, m, l, o);
+                i0 = load_ids(idrow, first + (j + 2) * kAttnStepCells, wlen, n);
+                load_rows<SHARED>(i1, a, limit, kv_row, head_off, n, r1);
+                attend<SHARED>(r0, qb, a.scale_log2, n, lg, vt, m, l, o);
                 if (j + 1 >= steps)
                     break;
-                i1 = load_ids(idrow, first + (j + 3) * kAttnStepCells, a.width, n);
-                load_rows(i0, a, limit, kv_row, head_off, n, r0);
-                attend(r1, qb, a.scale_log2, n, lg, vt, m, l, o);
+                i1 = load_ids(idrow, first + (j + 3) * kAttnStepCells, wlen, n);
+                load_rows<SHARED>(i0, a, limit, kv_row, head_off, n, r0);
+                attend<SHARED>(r1, qb, a.scale_log2, n, lg, vt, m, l, o);
             }
         }
     }
@@ -324,10 +371,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a)
         sum += sm.merge.l[w][hn] * f;
         acc += *reinterpret_cast<const f32x4 *>(&sm.merge.o[w][hn][d0]) * f;
     }
-    const bool out_ok = hb * kAttnHeadBlock + hn < a.group;
-    const int head_out = g * a.group + hb * kAttnHeadBlock + hn;
-    float *dst = a.out + ((int64_t)iq * a.n_heads + head_out) * 128 + d0;
-    float *dst_lse = a.lse ? a.lse + (int64_t)iq * a.n_heads + head_out : nullptr;
+    const int q_out = SHARED ? 2 * iq + (hn >= kPairHeads ? 1 : 0) : iq;
+    const int h_out = SHARED ? (hn & (kPairHeads - 1)) : hb * kAttnHeadBlock + hn;
+    const bool out_ok = h_out < a.group && q_out < a.nq;
+    const int head_out = g * a.group + h_out;
+    float *dst = a.out + ((int64_t)q_out * a.n_heads + head_out) * 128 + d0;
+    float *dst_lse = a.lse ? a.lse + (int64_t)q_out * a.n_heads + head_out : nullptr;
     if (a.n_chunks == 1) {
         if (out_ok)
             finish(acc, sum, ref, dst, d0 == 0 ? dst_lse : nullptr);
@@ -340,8 +389,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a)
         a.part_ml[slot] = make_float2(big, sum);
 }
 
-// One workgroup per (unit, head of the block): merges the unit's chunks.
+// One workgroup per (unit, column of the block): merges the unit's chunks.
 // Every chunk's partial is loaded before any is used, so the loads overlap.
+template <bool SHARED>
 __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a)
 {
     const int hn = blockIdx.x % kAttnHeadBlock;
@@ -350,10 +400,12 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a)
     const int hb = u % a.hblocks;
     u /= a.hblocks;
     const int g = u % a.kv_heads;
-    const int iq = u / a.kv_heads;
-    if (hb * kAttnHeadBlock + hn >= a.group)
+    const int iu = u / a.kv_heads;
+    const int iq = SHARED ? 2 * iu + (hn >= kPairHeads ? 1 : 0) : iu;
+    const int hc = SHARED ? (hn & (kPairHeads - 1)) : hb * kAttnHeadBlock + hn;
+    if (hc >= a.group || iq >= a.nq)
         return;
-    const int head = g * a.group + hb * kAttnHeadBlock + hn;
+    const int head = g * a.group + hc;
     const int d = threadIdx.x;
     const int64_t slot0 = (int64_t)unit * a.n_chunks * kAttnHeadBlock + hn;
     float2 ml[kAttnMaxChunks];
@@ -381,18 +433,163 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a)
         a.lse[(int64_t)iq * a.n_heads + head] = sum > 0.f ? (ref + log2f(sum)) * 0.69314718055994531f : -INFINITY;
 }
 
+// ------------------------------------------------------------ pair merge
+// One workgroup per pair of queries (2p, 2p+1): the pair's listed cells into
+// one list of distinct cells (iree-org/wave issue #1257, section Shared block
+// deduplication; the dedup index is an LDS hash). Entries are taken in the
+// order query 2p's list, then query 2p+1's; each valid id (in [0, n_cells),
+// position < width) goes into an open-addressing hash slot, whose counter
+// counts the listings of each query. An entry is emitted if it is query 2p's
+// or its cell is not in query 2p's list, marked with every query that lists
+// the cell; its place in the merged list is the number of emitted entries
+// before it, so the list depends only on the input. A query that lists a cell
+// more than once must count it that often, so a pair with such a repeat is
+// not merged: every valid entry is emitted, marked with its own query only.
+constexpr int kUnionThreads = 1024;
+constexpr int kUnionSlots = 4 * kPairMaxWidth;                    // twice a pair's entries at the longest width
+constexpr int kUnionPer = 2 * kPairMaxWidth / kUnionThreads;      // entries per thread at most
+constexpr uint32_t kUnionEmpty = 0xFFFFFFFFu;
+
+__global__ __launch_bounds__(kUnionThreads) void attn_union_kernel(AttnArgs a)
+{
+    __shared__ uint32_t s_key[kUnionSlots];
+    __shared__ uint32_t s_cnt[kUnionSlots];  // listings: query 2p in the low half, query 2p+1 in the high half
+    __shared__ uint32_t s_wsum[kUnionThreads / 64];
+    __shared__ uint32_t s_dup;
+    const int p = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int W = a.src_width, E = 2 * W;
+    const int T = 1 << a.slot_bits;
+
+    // Thread tid takes entries [tid * per, tid * per + per) of the pair. All
+    // its ids are loaded before the first probe (a load behind a probing
+    // loop would wait for the loop).
+    const int per = (E + kUnionThreads - 1) / kUnionThreads;  // <= kUnionPer
+    uint32_t id[kUnionPer];
+    bool valid[kUnionPer];
+#pragma unroll
+    for (int j = 0; j < kUnionPer; ++j) {
+        const int e = tid * per + j;
+        const int qi = e >= W ? 1 : 0;
+        const int q = 2 * p + qi;
+        valid[j] = j < per && e < E && q < a.nq;
+        const int pos = min(e - qi * W, W - 1);
+        const int32_t x = a.src_ids[(int64_t)min(q, a.nq - 1) * a.src_ld + max(pos, 0)];
+        valid[j] = valid[j] && (unsigned)x < (unsigned)a.n_cells;
+        id[j] = (uint32_t)x;
+    }
+    for (int i = tid; i < T; i += kUnionThreads) {
+        s_key[i] = kUnionEmpty;
+        s_cnt[i] = 0u;
+    }
+    if (tid == 0)
+        s_dup = 0u;
+    __syncthreads();
+
+    int slot[kUnionPer];
+#pragma unroll
+    for (int j = 0; j < kUnionPer; ++j) {
+        slot[j] = 0;
+        if (!valid[j])
+            continue;
+        const int qi = tid * per + j >= W ? 1 : 0;
+        // Linear probing; the table holds at least twice the entries, so a
+        // free or matching slot is always found within T probes.
+        uint32_t h = (id[j] * 0x9E3779B1u) >> (32 - a.slot_bits);
+        for (int it = 0; it < T; ++it) {
+            uint32_t expect = kUnionEmpty;
+            __hip_atomic_compare_exchange_strong(&s_key[h], &expect, id[j], __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (expect == kUnionEmpty || expect == id[j])
+                break;
+            h = (h + 1u) & (uint32_t)(T - 1);
+        }
+        slot[j] = (int)h;
+        const uint32_t unit = qi ? 0x10000u : 1u;
+        const uint32_t old = __hip_atomic_fetch_add(&s_cnt[h], unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (((old >> (16 * qi)) & 0xFFFFu) != 0u)
+            __hip_atomic_store(&s_dup, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    const bool dup = s_dup != 0u;
+
+    uint32_t packed[kUnionPer];
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int j = 0; j < kUnionPer; ++j) {
+        packed[j] = kUnionEmpty;
+        if (!valid[j])
+            continue;
+        const int qi = tid * per + j >= W ? 1 : 0;
+        const uint32_t c = s_cnt[slot[j]];
+        uint32_t mask;
+        bool emit;
+        if (dup) {
+            emit = true;
+            mask = 1u << qi;
+        } else if (qi == 0) {
+            emit = true;
+            mask = 1u | ((c >> 16) != 0u ? 2u : 0u);
+        } else {
+            emit = (c & 0xFFFFu) == 0u;
+            mask = 2u;
+        }
+        if (emit) {
+            packed[j] = id[j] | (mask << kPairIdBits);
+            ++mine;
+        }
+    }
+    // Places: exclusive prefix of the emitted counts in entry order.
+    const uint32_t incl = wave_incl_sum(mine);
+    if (lane == 63)
+        s_wsum[wv] = incl;
+    __syncthreads();
+    uint32_t base = incl - mine;
+    uint32_t total = 0u;
+#pragma unroll
+    for (int w = 0; w < kUnionThreads / 64; ++w) {
+        const uint32_t c = s_wsum[w];
+        base += w < wv ? c : 0u;
+        total += c;
+    }
+    int32_t *dst = a.union_ids + (int64_t)p * a.width;
+#pragma unroll
+    for (int j = 0; j < kUnionPer; ++j) {
+        if (packed[j] != kUnionEmpty)
+            dst[base++] = (int32_t)packed[j];
+    }
+    if (tid == 0)
+        a.union_len[p] = (int32_t)total;
+}
 
 } // namespace
 
-bool make_attn_plan(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width, AttnPlan &p)
+bool make_attn_plan(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width, AttnPlan &p, bool shared)
 {
     p = AttnPlan{};
     if (nq < 0 || n_heads < 1 || kv_heads < 1 || n_heads % kv_heads != 0 || width < 1)
         return false;
     const int32_t group = n_heads / kv_heads;
-    p.hblocks = (group + kAttnHeadBlock - 1) / kAttnHeadBlock;
-    p.units = (int64_t)nq * kv_heads * p.hblocks;
-    const int32_t steps = (width + kAttnStepCells - 1) / kAttnStepCells;
+    int32_t list = width;  // length of the lists the units walk, at most
+    if (shared) {
+        // A pair's heads fill the 16 columns; its merged list is at most
+        // twice the width, hashed into at least twice that many slots.
+        if (group > kPairHeads || width > kPairMaxWidth)
+            return false;
+        p.shared = 1;
+        p.pairs = (nq + 1) / 2;
+        p.hblocks = 1;
+        p.units = (int64_t)p.pairs * kv_heads;
+        list = 2 * width;
+        int bits = 8;
+        while ((1 << bits) < 2 * list)
+            ++bits;
+        p.slot_bits = bits;
+    } else {
+        p.hblocks = (group + kAttnHeadBlock - 1) / kAttnHeadBlock;
+        p.units = (int64_t)nq * kv_heads * p.hblocks;
+    }
+    const int32_t steps = (list + kAttnStepCells - 1) / kAttnStepCells;
     const int32_t max_chunks = (steps + kAttnWaves - 1) / kAttnWaves;
     int64_t chunks = p.units > 0 ? (kAttnTargetGroups + p.units - 1) / p.units : 1;
     chunks = chunks < 1 ? 1 : (chunks > max_chunks ? max_chunks : chunks);
@@ -401,22 +598,42 @@ bool make_attn_plan(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width
     p.n_chunks = (steps + kAttnWaves * p.steps_per_wave - 1) / (kAttnWaves * p.steps_per_wave);
     if (p.units * p.n_chunks * kAttnHeadBlock > 0x7fffffffLL)
         return false;
+    size_t off = 0;
     if (p.n_chunks > 1) {
         const size_t parts = (size_t)p.units * p.n_chunks * kAttnHeadBlock;
         p.ml_offset = 0;
         p.o_offset = (parts * sizeof(float2) + 255) / 256 * 256;
-        p.bytes = p.o_offset + parts * 128 * sizeof(float);
+        off = p.o_offset + parts * 128 * sizeof(float);
     }
+    if (shared) {
+        const size_t q = (size_t)(p.pairs > 0 ? p.pairs : 1);
+        p.union_offset = (off + 255) / 256 * 256;
+        p.len_offset = (p.union_offset + q * (size_t)list * 4 + 255) / 256 * 256;
+        off = p.len_offset + q * 4;
+    }
+    p.bytes = off;
     return true;
 }
 
 hipError_t launch_attention(const AttnArgs &a, const AttnPlan &p, hipStream_t s)
 {
-    hipLaunchKernelGGL(attn_kernel, dim3((unsigned)(p.units * p.n_chunks)), dim3(kThreads), 0, s, a);
+    if (p.shared) {
+        hipLaunchKernelGGL(attn_union_kernel, dim3((unsigned)p.pairs), dim3(kUnionThreads), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(attn_kernel<true>, dim3((unsigned)(p.units * p.n_chunks)), dim3(kThreads), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess || p.n_chunks == 1)
+            return e;
+        hipLaunchKernelGGL(attn_merge_kernel<true>, dim3((unsigned)(p.units * kAttnHeadBlock)), dim3(128), 0, s, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(attn_kernel<false>, dim3((unsigned)(p.units * p.n_chunks)), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_chunks == 1)
         return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(p.units * kAttnHeadBlock)), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(attn_merge_kernel<false>, dim3((unsigned)(p.units * kAttnHeadBlock)), dim3(128), 0, s, a);
     return hipGetLastError();
 }
 

@@ -498,18 +498,33 @@ size_t qsa_selection_attention_workspace_bytes(int32_t nq, int32_t n_heads, int3
     return plan.bytes;
 }
 
-qsa_status qsa_selection_attention(const void *q, const void *k, const void *v, const int32_t *ids,
-                                   int64_t ld_ids, float *out, float *lse, int32_t nq, int32_t n_heads,
-                                   int32_t kv_heads, int32_t head_dim, int32_t n_cells, int32_t width,
-                                   float scale, void *workspace, size_t workspace_bytes, void *stream)
+size_t qsa_selection_attention_shared_workspace_bytes(int32_t nq, int32_t n_heads, int32_t kv_heads,
+                                                      int32_t width)
+{
+    AttnPlan plan;
+    if (!make_attn_plan(nq, n_heads, kv_heads, width, plan, true))
+        return 0;
+    return plan.bytes;
+}
+
+} // extern "C"
+
+namespace {
+
+qsa_status attention_call(bool shared, const void *q, const void *k, const void *v, const int32_t *ids,
+                          int64_t ld_ids, float *out, float *lse, int32_t nq, int32_t n_heads, int32_t kv_heads,
+                          int32_t head_dim, int32_t n_cells, int32_t width, float scale, void *workspace,
+                          size_t workspace_bytes, void *stream)
 {
     if (nq < 0 || n_heads < 1 || kv_heads < 1 || n_heads % kv_heads != 0 || n_cells < 1 || width < 1 ||
         ld_ids < width || !isfinite(scale))
         return QSA_EINVAL;
     if (head_dim != 128)
         return QSA_EUNSUPPORTED;
+    if (shared && (n_heads / kv_heads > kPairHeads || width > kPairMaxWidth || n_cells >= (1 << kPairIdBits)))
+        return QSA_EUNSUPPORTED;
     AttnPlan plan;
-    if (!make_attn_plan(nq, n_heads, kv_heads, width, plan))
+    if (!make_attn_plan(nq, n_heads, kv_heads, width, plan, shared))
         return QSA_EINVAL;
     if (nq == 0)
         return QSA_OK;
@@ -524,23 +539,58 @@ qsa_status qsa_selection_attention(const void *q, const void *k, const void *v, 
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint16_t *>(k);
     a.v = static_cast<const uint16_t *>(v);
-    a.ids = ids;
-    a.ld_ids = ld_ids;
     a.out = out;
     a.lse = lse;
-    a.part_ml = plan.bytes ? at<float2>(workspace, plan.ml_offset) : nullptr;
-    a.part_o = plan.bytes ? at<float>(workspace, plan.o_offset) : nullptr;
+    a.part_ml = plan.n_chunks > 1 ? at<float2>(workspace, plan.ml_offset) : nullptr;
+    a.part_o = plan.n_chunks > 1 ? at<float>(workspace, plan.o_offset) : nullptr;
     a.nq = nq;
     a.n_heads = n_heads;
     a.kv_heads = kv_heads;
     a.group = n_heads / kv_heads;
     a.hblocks = plan.hblocks;
     a.n_cells = n_cells;
-    a.width = width;
     a.steps_per_wave = plan.steps_per_wave;
     a.n_chunks = plan.n_chunks;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    if (shared) {
+        // The units walk the merged lists: twice the width, one row per pair.
+        a.union_ids = at<int32_t>(workspace, plan.union_offset);
+        a.union_len = at<int32_t>(workspace, plan.len_offset);
+        a.ids = a.union_ids;
+        a.ld_ids = 2 * (int64_t)width;
+        a.width = 2 * width;
+        a.src_ids = ids;
+        a.src_ld = ld_ids;
+        a.src_width = width;
+        a.slot_bits = plan.slot_bits;
+    } else {
+        a.ids = ids;
+        a.ld_ids = ld_ids;
+        a.width = width;
+    }
     return launch_attention(a, plan, (hipStream_t)stream) == hipSuccess ? QSA_OK : QSA_EHIP;
+}
+
+} // namespace
+
+extern "C" {
+
+qsa_status qsa_selection_attention(const void *q, const void *k, const void *v, const int32_t *ids,
+                                   int64_t ld_ids, float *out, float *lse, int32_t nq, int32_t n_heads,
+                                   int32_t kv_heads, int32_t head_dim, int32_t n_cells, int32_t width,
+                                   float scale, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return attention_call(false, q, k, v, ids, ld_ids, out, lse, nq, n_heads, kv_heads, head_dim, n_cells, width,
+                          scale, workspace, workspace_bytes, stream);
+}
+
+qsa_status qsa_selection_attention_shared(const void *q, const void *k, const void *v, const int32_t *ids,
+                                          int64_t ld_ids, float *out, float *lse, int32_t nq, int32_t n_heads,
+                                          int32_t kv_heads, int32_t head_dim, int32_t n_cells, int32_t width,
+                                          float scale, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return attention_call(true, q, k, v, ids, ld_ids, out, lse, nq, n_heads, kv_heads, head_dim, n_cells, width,
+                          scale, workspace, workspace_bytes, stream);
 }
 
 } // extern "C"

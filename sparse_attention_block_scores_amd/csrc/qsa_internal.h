@@ -128,8 +128,17 @@ constexpr int kAttnStepCells = 32;        // cells per wave step
 constexpr int kAttnHeadBlock = 16;        // query heads per workgroup (one matrix-core column each)
 constexpr int kAttnTargetGroups = 256;    // workgroups the chunking aims for (one per CU)
 constexpr int kAttnMaxChunks = 16;        // chunks of one unit's list at most
+// Shared-block attention: pairs of queries, each pair's lists merged first.
+constexpr int kPairHeads = 8;             // heads of one query in a pair's 16 matrix-core columns
+constexpr int kPairMaxWidth = 4096;       // longest list the merge's LDS hash takes
+constexpr int kPairIdBits = 30;           // merged entry: cell id (low 30 bits) | which queries listed it
 
 struct AttnPlan {
+    int32_t shared;          // 1: pairs of queries over their merged lists
+    int32_t pairs;           // shared: ceil(nq / 2)
+    int32_t slot_bits;       // shared: log2 of the merge's hash slots
+    size_t union_offset;     // shared: workspace: merged lists, [pairs][2 * width] int32
+    size_t len_offset;       // shared: workspace: merged list lengths, [pairs] int32
     int32_t hblocks;         // blocks of up to 16 heads per key/value head
     int32_t steps_per_wave;  // 32-cell steps each wave takes
     int32_t n_chunks;        // chunks of the id list per (query, kv head, head block)
@@ -151,9 +160,18 @@ struct AttnArgs {
     float *part_o;
     int32_t nq, n_heads, kv_heads, group, hblocks, n_cells, width, steps_per_wave, n_chunks;
     float scale_log2;        // softmax scale times log2(e)
+    // Shared-block attention: ids are the merged lists (ld_ids = width = twice
+    // the callers' width), src_ids the callers' lists.
+    const int32_t *src_ids;  // [nq][src_ld]
+    int64_t src_ld;
+    int32_t src_width;
+    int32_t slot_bits;
+    int32_t *union_ids;      // [pairs][width]
+    int32_t *union_len;      // [pairs]
 };
 
-bool make_attn_plan(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width, AttnPlan &plan);
+bool make_attn_plan(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width, AttnPlan &plan,
+                    bool shared = false);
 hipError_t launch_attention(const AttnArgs &a, const AttnPlan &plan, hipStream_t s);
 
 } // namespace qsa

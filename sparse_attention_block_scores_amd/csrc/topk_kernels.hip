@@ -450,7 +450,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
             }
 #pragma unroll
             for (int u = 0; u < CPR; ++u)
-                shift[u] = s_ssrc[blk[u] / STEP];
+                shift[u] = s_ssrc[(uint32_t)blk[u] / STEP];  // blocks are non-negative
 #pragma unroll
             for (int u = 0; u < CPR; ++u) {
                 if (i0 + u * kWave < wtot) {

@@ -228,6 +228,7 @@ class AttnWorkload:
     width: int
     block_size: int = 4
     head_dim: int = 128
+    pair_keep: float = 0.0  # > 0: queries 2i and 2i+1 share this fraction of their blocks
 
     def tensors(self):
         """bfloat16 bit patterns (uint16) of q, k and v."""
@@ -237,6 +238,9 @@ class AttnWorkload:
         return q, k, v
 
     def selection(self):
+        if self.pair_keep > 0:
+            return paired_selection(f"{self.name}/ids", self.nq, self.n_cells // self.block_size,
+                                    self.block_size, self.width, self.pair_keep)
         return random_selection(f"{self.name}/ids", self.nq, self.n_cells // self.block_size,
                                 self.block_size, self.width)
 
@@ -265,6 +269,31 @@ def random_selection(tag: str, nq: int, n_blocks: int, block_size: int, width: i
     return ids
 
 
+def paired_selection(tag: str, nq: int, n_blocks: int, block_size: int, width: int, keep: float) -> np.ndarray:
+    """ids [nq, width] int32 in the form of random_selection, where query
+    2i+1 keeps round(keep * nsel) of query 2i's blocks (those of the smallest
+    values of a seeded stream over them) and draws the rest uniformly from
+    the blocks query 2i did not select (neighbouring prompt positions select
+    overlapping blocks; the pages give no overlap figure, keep sets it)."""
+    nsel = min(width // block_size, n_blocks)
+    ids = random_selection(tag, nq, n_blocks, block_size, width)
+    cells = np.arange(block_size, dtype=np.int64)
+    nkeep = min(nsel, int(round(keep * nsel)))
+    for iq in range(1, nq, 2):
+        base = ids[iq - 1, : nsel * block_size : block_size].astype(np.int64) // block_size
+        kept = base[np.argpartition(splitmix64(stream_seed(f"{tag}/keep/{iq}"), nsel), nkeep - 1)[:nkeep]] \
+            if 0 < nkeep < nsel else (base if nkeep == nsel else base[:0])
+        others = np.setdiff1d(np.arange(n_blocks, dtype=np.int64), base, assume_unique=True)
+        nnew = min(nsel - nkeep, others.size)
+        new = others[np.argpartition(splitmix64(stream_seed(f"{tag}/new/{iq}"), others.size), nnew - 1)[:nnew]] \
+            if 0 < nnew < others.size else (others if nnew == others.size else others[:0])
+        blocks = np.sort(np.concatenate([kept, new]))
+        row = (blocks[:, None] * block_size + cells[None, :]).reshape(-1)
+        ids[iq, :] = -1
+        ids[iq, : row.size] = row
+    return ids
+
+
 def a1() -> AttnWorkload:
     """Tiny decode: 3 queries, 2 key/value heads of 8 query heads, 4,096 cells."""
     return AttnWorkload("A1", nq=3, heads=16, kv_heads=2, n_cells=4096, width=256)
@@ -278,3 +307,10 @@ def a3() -> AttnWorkload:
 def a5() -> AttnWorkload:
     """Prompt chunk: 256 queries, one group of 16 heads, 524,288 cells, 2,048 selected."""
     return AttnWorkload("A5", nq=256, heads=16, kv_heads=1, n_cells=524288, width=2048)
+
+
+def a6() -> AttnWorkload:
+    """Prompt chunk for the shared-block path: 256 queries, 16 heads in two
+    key/value groups of 8, 524,288 cells, 2,048 selected, neighbouring
+    queries sharing 3/4 of their blocks."""
+    return AttnWorkload("A6", nq=256, heads=16, kv_heads=2, n_cells=524288, width=2048, pair_keep=0.75)

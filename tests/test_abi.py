@@ -195,13 +195,13 @@ def test_plan_struct_size_matches_header():
     assert ctypes.sizeof(B.Options) == 8 * 4
 
 
-def _attn(L, **over):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, ids=FAKE, ld=2048, out=FAKE, lse=FAKE, nq=16, h=16, kvh=1, d=128,
-             cells=262144, width=2048, scale=0.0883883, ws=FAKE, wsb=1 << 30)
+def _attn(L, shared=False, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ids=FAKE, ld=2048, out=FAKE, lse=FAKE, nq=16, h=16, kvh=2 if shared else 1,
+             d=128, cells=262144, width=2048, scale=0.0883883, ws=FAKE, wsb=1 << 30)
     a.update(over)
-    return L.qsa_selection_attention(a["q"], a["k"], a["v"], a["ids"], a["ld"], a["out"], a["lse"], a["nq"],
-                                     a["h"], a["kvh"], a["d"], a["cells"], a["width"], a["scale"], a["ws"],
-                                     a["wsb"], None)
+    fn = L.qsa_selection_attention_shared if shared else L.qsa_selection_attention
+    return fn(a["q"], a["k"], a["v"], a["ids"], a["ld"], a["out"], a["lse"], a["nq"], a["h"], a["kvh"], a["d"],
+              a["cells"], a["width"], a["scale"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -239,6 +239,34 @@ def test_attention_workspace_sizes():
     parts = 16 * 8 * 16
     assert qsa.attention_workspace_bytes(16, 16, 1, 2048) == (parts * 8 + 255) // 256 * 256 + parts * 512
     assert qsa.attention_workspace_bytes(16, 16, 3, 2048) == 0  # invalid grouping
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(h=16, kvh=1), B.QSA_EUNSUPPORTED),   # a pair's heads must fit 16 columns: groups of at most 8
+    (dict(width=4097, ld=4097), B.QSA_EUNSUPPORTED),
+    (dict(cells=1 << 30), B.QSA_EUNSUPPORTED),
+    (dict(d=64), B.QSA_EUNSUPPORTED),
+    (dict(h=16, kvh=3), B.QSA_EINVAL),
+    (dict(ld=2047), B.QSA_EINVAL),
+    (dict(width=0), B.QSA_EINVAL),
+    (dict(k=FAKE + 8), B.QSA_EINVAL),
+    (dict(ws=None), B.QSA_EWORKSPACE),
+    (dict(wsb=1024), B.QSA_EWORKSPACE),
+])
+def test_shared_attention_argument_errors(over, status):
+    assert _attn(qsa.lib(), shared=True, **over) == status
+
+
+def test_shared_attention_workspace_sizes():
+    # 256 queries in 128 pairs x 2 key/value heads: 256 units, one chunk each;
+    # the merged lists (twice the width per pair) and their lengths.
+    lists = 128 * 4096 * 4
+    assert qsa.attention_workspace_bytes(256, 16, 2, 2048, shared=True) == (lists + 255) // 256 * 256 + 128 * 4
+    # one query: a pair of its own
+    assert qsa.attention_workspace_bytes(1, 8, 1, 64, shared=True) > 0
+    assert qsa.attention_workspace_bytes(16, 16, 1, 2048, shared=True) == 0  # groups of 16 heads
+    assert qsa.attention_workspace_bytes(16, 16, 2, 4097, shared=True) == 0  # past the merge's width
+    assert _attn(qsa.lib(), shared=True, nq=0) == B.QSA_OK
 
 
 def _noalloc(L, **over):

@@ -27,21 +27,21 @@ def bf16_dev(bits):
     return to_dev(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
 
 
-def gpu_attention(qb, kb, vb, ids, scale, width=None):
+def gpu_attention(qb, kb, vb, ids, scale, width=None, shared=False):
     out, lse = qsa.selection_attention(bf16_dev(qb), bf16_dev(kb), bf16_dev(vb), to_dev(ids),
-                                       width=width, scale=scale)
+                                       width=width, scale=scale, shared=shared)
     torch.cuda.synchronize()
     return out.cpu().numpy(), lse.cpu().numpy()
 
 
-def check(qb, kb, vb, ids, scale, label, width=None):
+def check(qb, kb, vb, ids, scale, label, width=None, shared=False):
     width = ids.shape[1] if width is None else width
     q, k, v = synth.bf16_values(qb), synth.bf16_values(kb), synth.bf16_values(vb)
     listed = np.ascontiguousarray(ids[:, :width])
     ref, ref_lse = oracle.selection_attention(q, k, v, listed, scale)
     scale_t, _ = oracle.selection_attention(q, k, np.abs(v), listed, scale)
     say(f"attention {label}")
-    out, lse = gpu_attention(qb, kb, vb, ids, scale, width)
+    out, lse = gpu_attention(qb, kb, vb, ids, scale, width, shared)
     err = np.abs(out.astype(np.float64) - ref)
     tol = RTOL * scale_t
     if not (err <= tol).all():
@@ -320,3 +320,100 @@ def test_graph_replays_with_changing_lists():
         fin = np.isfinite(ref_lse)
         assert (np.isneginf(got_lse) == ~fin).all(), j
         assert (np.abs(got_lse[fin] - ref_lse[fin]) <= RTOL * np.maximum(1.0, np.abs(ref_lse[fin]))).all(), j
+
+
+# ------------------------------------------------------------ shared blocks
+# qsa_selection_attention_shared (iree-org/wave issue #1257, section Shared
+# block deduplication): pairs of queries over their merged lists, the same
+# oracle and tolerance. Lists of neighbouring queries that overlap, coincide,
+# are disjoint, unsorted, ragged, hold foreign ids or repeats (a pair with a
+# repeat is not merged), odd query counts (the last query alone), groups of
+# 1-8 heads, widths up to the 4,096 the merge takes.
+
+
+def pair_ids(tag, nq, n_cells, width, ld, keep, order="sorted"):
+    ids = np.full((nq, ld), 1, np.int32)
+    ids[:, :width] = synth.paired_selection(tag, nq, max(1, n_cells // 4), 4, width, keep)
+    if order == "shuffled":
+        for iq in range(nq):
+            perm = np.argsort(synth.splitmix64(synth.stream_seed(f"{tag}/perm/{iq}"), width), kind="stable")
+            ids[iq, :width] = ids[iq, :width][perm]
+    return ids
+
+
+SHARED_CASES = [
+    # tag, nq, heads, kv_heads, n_cells, width, ld, keep (None: make_ids variant below), variant
+    ("overlap", 8, 16, 2, 20000, 2048, 2048, 0.75, "sorted"),
+    ("same", 4, 16, 2, 9000, 512, 512, 1.0, "sorted"),
+    ("disjoint", 4, 8, 2, 5000, 300, 301, 0.0, "sorted"),
+    ("shuffled", 6, 8, 1, 7000, 1000, 1000, 0.5, "shuffled"),
+    ("odd", 5, 16, 2, 3000, 777, 780, 0.6, "sorted"),
+    ("g1", 3, 2, 2, 400, 64, 64, 0.9, "sorted"),
+    ("w4096", 3, 16, 2, 50000, 4096, 4096, 0.8, "sorted"),
+    ("one", 1, 1, 1, 64, 1, 1, None, "random"),
+    ("ragged", 6, 8, 1, 1000, 100, 103, None, "ragged"),
+    ("foreign", 4, 2, 2, 50, 31, 31, None, "foreign"),
+    ("dups", 4, 8, 1, 50, 33, 40, None, "dups"),
+]
+
+
+@pytest.mark.parametrize("tag,nq,heads,kvh,n_cells,width,ld,keep,variant", SHARED_CASES,
+                         ids=[c[0] for c in SHARED_CASES])
+def test_shared_shapes(tag, nq, heads, kvh, n_cells, width, ld, keep, variant):
+    t = f"gpu/attn_shared/{tag}"
+    qb = synth.bf16_bits(synth.normal(t + "/q", (nq, heads, 128)))
+    kb = synth.bf16_bits(synth.normal(t + "/k", (n_cells, kvh, 128)))
+    vb = synth.bf16_bits(synth.normal(t + "/v", (n_cells, kvh, 128)))
+    ids = pair_ids(t, nq, n_cells, width, ld, keep, variant) if keep is not None else \
+        make_ids(t, variant, nq, n_cells, width, ld)
+    check(qb, kb, vb, ids, 1.0 / np.sqrt(128.0),
+          f"shared {tag} nq={nq} h={heads}/{kvh} cells={n_cells} w={width}", width=width, shared=True)
+
+
+def test_shared_matches_unshared():
+    """Both entry points on the same overlapping lists: each within the
+    oracle's tolerance, and of each other by twice it."""
+    nq, heads, kvh, n_cells, width = 10, 16, 2, 30000, 2048
+    t = "gpu/attn_shared/both"
+    qb = synth.bf16_bits(synth.normal(t + "/q", (nq, heads, 128)))
+    kb = synth.bf16_bits(synth.normal(t + "/k", (n_cells, kvh, 128)))
+    vb = synth.bf16_bits(synth.normal(t + "/v", (n_cells, kvh, 128)))
+    ids = pair_ids(t, nq, n_cells, width, width, 0.75)
+    say("attention shared against unshared")
+    a_out, a_lse = gpu_attention(qb, kb, vb, ids, 0.1)
+    b_out, b_lse = gpu_attention(qb, kb, vb, ids, 0.1, shared=True)
+    qf, kf, vf = synth.bf16_values(qb), synth.bf16_values(kb), synth.bf16_values(vb)
+    scale_t, _ = oracle.selection_attention(qf, kf, np.abs(vf), ids, 0.1)
+    assert (np.abs(a_out.astype(np.float64) - b_out) <= 2 * RTOL * scale_t).all()
+    assert (np.abs(a_lse.astype(np.float64) - b_lse) <= 2 * RTOL * np.maximum(1.0, np.abs(a_lse))).all()
+
+
+def test_shared_workload_full():
+    """The shared-block prompt workload in full (256 queries, groups of 8
+    heads, neighbours sharing 3/4 of their blocks), as the benchmark times it."""
+    wl = synth.a6()
+    qb, kb, vb = wl.tensors()
+    check(qb, kb, vb, wl.selection(), wl.scale(), wl.name, shared=True)
+
+
+def test_shared_repeat_calls_on_one_workspace():
+    """Merged lists and partials of one call never leak into the next: three
+    calls on one workspace, the lists changing between them."""
+    nq, heads, kvh, n_cells, width = 6, 8, 1, 40000, 2048
+    t = "gpu/attn_shared/ws"
+    qb = synth.bf16_bits(synth.normal(t + "/q", (nq, heads, 128)))
+    kb = synth.bf16_bits(synth.normal(t + "/k", (n_cells, kvh, 128)))
+    vb = synth.bf16_bits(synth.normal(t + "/v", (n_cells, kvh, 128)))
+    lists = [pair_ids(t + "/x", nq, n_cells, width, width, 0.9), pair_ids(t + "/y", nq, n_cells, width, width, 0.2),
+             make_ids(t + "/z", "ragged", nq, n_cells, width, width)]
+    ws = qsa.workspace(qsa.attention_workspace_bytes(nq, heads, kvh, width, shared=True))
+    ws.fill_(0xFF)
+    q, k, v = bf16_dev(qb), bf16_dev(kb), bf16_dev(vb)
+    qf, kf, vf = synth.bf16_values(qb), synth.bf16_values(kb), synth.bf16_values(vb)
+    for j, ids in enumerate(lists):
+        say(f"attention shared call {j} on one workspace")
+        out, _ = qsa.selection_attention(q, k, v, to_dev(ids), scale=0.09, ws=ws, shared=True)
+        torch.cuda.synchronize()
+        ref, _ = oracle.selection_attention(qf, kf, vf, ids, 0.09)
+        scale_t, _ = oracle.selection_attention(qf, kf, np.abs(vf), ids, 0.09)
+        assert (np.abs(out.cpu().numpy() - ref) <= RTOL * scale_t).all(), j
