@@ -447,9 +447,9 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a)
 // not merged: every valid entry is emitted, marked with its own query only.
 constexpr int kUnionThreads = 1024;
 constexpr int kUnionSlots = 4 * kPairMaxWidth;                    // twice a pair's entries at the longest width
-constexpr int kUnionPer = 2 * kPairMaxWidth / kUnionThreads;      // entries per thread at most
 constexpr uint32_t kUnionEmpty = 0xFFFFFFFFu;
 
+template <int PER>  // entries per thread: 2 * width <= PER * kUnionThreads
 __global__ __launch_bounds__(kUnionThreads) void attn_union_kernel(AttnArgs a)
 {
     __shared__ uint32_t s_key[kUnionSlots];
@@ -460,22 +460,21 @@ __global__ __launch_bounds__(kUnionThreads) void attn_union_kernel(AttnArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int W = a.src_width, E = 2 * W;
     const int T = 1 << a.slot_bits;
+    const int32_t *row0 = a.src_ids + (int64_t)(2 * p) * a.src_ld;
+    const bool has1 = 2 * p + 1 < a.nq;
 
-    // Thread tid takes entries [tid * per, tid * per + per) of the pair. All
-    // its ids are loaded before the first probe (a load behind a probing
-    // loop would wait for the loop).
-    const int per = (E + kUnionThreads - 1) / kUnionThreads;  // <= kUnionPer
-    uint32_t id[kUnionPer];
-    bool valid[kUnionPer];
+    // Thread tid takes entries [tid * PER, tid * PER + PER) of the pair: query
+    // 2p's positions, then 2p+1's. All its ids are loaded before the first
+    // probe (a load behind a probing loop would wait for the loop).
+    uint32_t id[PER];
+    bool valid[PER];
 #pragma unroll
-    for (int j = 0; j < kUnionPer; ++j) {
-        const int e = tid * per + j;
-        const int qi = e >= W ? 1 : 0;
-        const int q = 2 * p + qi;
-        valid[j] = j < per && e < E && q < a.nq;
-        const int pos = min(e - qi * W, W - 1);
-        const int32_t x = a.src_ids[(int64_t)min(q, a.nq - 1) * a.src_ld + max(pos, 0)];
-        valid[j] = valid[j] && (unsigned)x < (unsigned)a.n_cells;
+    for (int j = 0; j < PER; ++j) {
+        const int e = tid * PER + j;
+        const bool second = e >= W;
+        const int pos = min(second ? e - W : e, W - 1);
+        const int32_t x = (second && has1 ? row0 + a.src_ld : row0)[pos];
+        valid[j] = e < E && (!second || has1) && (unsigned)x < (unsigned)a.n_cells;
         id[j] = (uint32_t)x;
     }
     for (int i = tid; i < T; i += kUnionThreads) {
@@ -486,13 +485,13 @@ __global__ __launch_bounds__(kUnionThreads) void attn_union_kernel(AttnArgs a)
         s_dup = 0u;
     __syncthreads();
 
-    int slot[kUnionPer];
+    uint32_t slot[PER];
 #pragma unroll
-    for (int j = 0; j < kUnionPer; ++j) {
-        slot[j] = 0;
+    for (int j = 0; j < PER; ++j) {
+        slot[j] = 0u;
         if (!valid[j])
             continue;
-        const int qi = tid * per + j >= W ? 1 : 0;
+        const uint32_t qi = tid * PER + j >= W ? 1u : 0u;
         // Linear probing; the table holds at least twice the entries, so a
         // free or matching slot is always found within T probes.
         uint32_t h = (id[j] * 0x9E3779B1u) >> (32 - a.slot_bits);
@@ -504,40 +503,25 @@ __global__ __launch_bounds__(kUnionThreads) void attn_union_kernel(AttnArgs a)
                 break;
             h = (h + 1u) & (uint32_t)(T - 1);
         }
-        slot[j] = (int)h;
-        const uint32_t unit = qi ? 0x10000u : 1u;
-        const uint32_t old = __hip_atomic_fetch_add(&s_cnt[h], unit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        slot[j] = h;
+        const uint32_t old =
+            __hip_atomic_fetch_add(&s_cnt[h], qi ? 0x10000u : 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (((old >> (16 * qi)) & 0xFFFFu) != 0u)
             __hip_atomic_store(&s_dup, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     __syncthreads();
     const bool dup = s_dup != 0u;
 
-    uint32_t packed[kUnionPer];
+    uint32_t packed[PER];
     uint32_t mine = 0u;
 #pragma unroll
-    for (int j = 0; j < kUnionPer; ++j) {
-        packed[j] = kUnionEmpty;
-        if (!valid[j])
-            continue;
-        const int qi = tid * per + j >= W ? 1 : 0;
-        const uint32_t c = s_cnt[slot[j]];
-        uint32_t mask;
-        bool emit;
-        if (dup) {
-            emit = true;
-            mask = 1u << qi;
-        } else if (qi == 0) {
-            emit = true;
-            mask = 1u | ((c >> 16) != 0u ? 2u : 0u);
-        } else {
-            emit = (c & 0xFFFFu) == 0u;
-            mask = 2u;
-        }
-        if (emit) {
-            packed[j] = id[j] | (mask << kPairIdBits);
-            ++mine;
-        }
+    for (int j = 0; j < PER; ++j) {
+        const bool second = tid * PER + j >= W;
+        const uint32_t c = valid[j] ? s_cnt[slot[j]] : 0u;
+        const bool emit = valid[j] && (dup || !second || (c & 0xFFFFu) == 0u);
+        const uint32_t mask = dup ? (second ? 2u : 1u) : (second ? 2u : (1u | ((c >> 16) != 0u ? 2u : 0u)));
+        packed[j] = emit ? (id[j] | (mask << kPairIdBits)) : kUnionEmpty;
+        mine += emit ? 1u : 0u;
     }
     // Places: exclusive prefix of the emitted counts in entry order.
     const uint32_t incl = wave_incl_sum(mine);
@@ -554,7 +538,7 @@ __global__ __launch_bounds__(kUnionThreads) void attn_union_kernel(AttnArgs a)
     }
     int32_t *dst = a.union_ids + (int64_t)p * a.width;
 #pragma unroll
-    for (int j = 0; j < kUnionPer; ++j) {
+    for (int j = 0; j < PER; ++j) {
         if (packed[j] != kUnionEmpty)
             dst[base++] = (int32_t)packed[j];
     }
@@ -618,7 +602,15 @@ bool make_attn_plan(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width
 hipError_t launch_attention(const AttnArgs &a, const AttnPlan &p, hipStream_t s)
 {
     if (p.shared) {
-        hipLaunchKernelGGL(attn_union_kernel, dim3((unsigned)p.pairs), dim3(kUnionThreads), 0, s, a);
+        const int entries = 2 * a.src_width;  // <= 2 * kPairMaxWidth = 8 * kUnionThreads
+        if (entries <= kUnionThreads)
+            hipLaunchKernelGGL(attn_union_kernel<1>, dim3((unsigned)p.pairs), dim3(kUnionThreads), 0, s, a);
+        else if (entries <= 2 * kUnionThreads)
+            hipLaunchKernelGGL(attn_union_kernel<2>, dim3((unsigned)p.pairs), dim3(kUnionThreads), 0, s, a);
+        else if (entries <= 4 * kUnionThreads)
+            hipLaunchKernelGGL(attn_union_kernel<4>, dim3((unsigned)p.pairs), dim3(kUnionThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(attn_union_kernel<8>, dim3((unsigned)p.pairs), dim3(kUnionThreads), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
