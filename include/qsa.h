@@ -33,9 +33,12 @@
  * is caller-owned DEVICE memory; the library never allocates or frees device
  * memory, and the only device memory of its own is the fixed workspace array
  * of qsa_block_topk_noalloc (one per GPU, for callers that cannot allocate).
- * All work is enqueued
- * on `stream` (a hipStream_t; NULL = the default stream) and the calls return
- * without synchronising. Nothing is printed.
+ * All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ * stream) and the calls return without synchronising. Nothing is printed.
+ * Host-side state: the first call that takes the exact chunked split raises
+ * one kernel's dynamic-LDS limit (a kernel attribute, set once per process;
+ * concurrent first calls are safe), and the first allocation-free call on a
+ * device looks up that device's array. Nothing else persists between calls.
  *
  * Errors. Arguments are checked on the host before anything is launched; a
  * call that returns anything but QSA_OK has enqueued nothing. QSA_EHIP means
