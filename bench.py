@@ -187,8 +187,53 @@ def secondary(torch, qsa, synth, dev, reps=50):
         bf[wlb.name] = {"us": round(us, 2), "TFLOPs": round(tf, 1), "bf16_peak_frac": round(tf / PEAK_BF16_MFMA_TFLOPS, 4)}
         del qb, kb, wb, sb
     out["bf16_scorer"] = bf
+    out["vendor_gemm"] = vendor_gemm(torch, synth, dev)
 
     out["selection_attention"] = attention_figures(torch, qsa, synth, dev, time_us)
+    return out
+
+
+def vendor_gemm(torch, synth, dev, reps=10):
+    """The vendor GEMM (torch.matmul, hipBLASLt) on this GPU, as a yardstick
+    for the scorer's fraction of the matrix peaks: 8192^3 in FP32 and BF16,
+    and the scorer's own contraction on the prompt-call shape (32 heads x 256
+    queries = 8,192 rows of K = 128 against 131,072 keys, FP32) as a plain
+    GEMM that writes every head's dot products (4 GiB) and applies no relu,
+    weights or head sum. Event-timed means over `reps` calls after 3 warm-up
+    calls."""
+    def mean_us(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / reps
+
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    n = 8192
+    for name, dt, peak in (("fp32", torch.float32, PEAK_FP32_MFMA_TFLOPS), ("bf16", torch.bfloat16, PEAK_BF16_MFMA_TFLOPS)):
+        a = torch.randn((n, n), device=dev, generator=g).to(dt)
+        b = torch.randn((n, n), device=dev, generator=g).to(dt)
+        us = mean_us(lambda: torch.matmul(a, b))
+        tf = 2.0 * n ** 3 / (us * 1e-6) / 1e12
+        out[f"{name}_8192cube"] = {"us": round(us, 1), "TFLOPs": round(tf, 1), "peak_frac": round(tf / peak, 4)}
+        del a, b
+    wl = synth.c5()
+    qh, kh, _ = wl.tensors()
+    q2 = torch.from_numpy(qh).to(dev).reshape(wl.nq * wl.heads, wl.head_dim)
+    kt = torch.from_numpy(kh).to(dev)
+    c = torch.empty((wl.nq * wl.heads, wl.n_blocks), device=dev)
+    us = mean_us(lambda: torch.matmul(q2, kt.t(), out=c))
+    tf = wl.flops() / (us * 1e-6) / 1e12
+    out["fp32_scorer_contraction_unfused"] = {"us": round(us, 1), "TFLOPs": round(tf, 1),
+                                              "peak_frac": round(tf / PEAK_FP32_MFMA_TFLOPS, 4)}
+    del q2, kt, c
     return out
 
 
@@ -196,7 +241,8 @@ def topk_figures(torch, qsa, synth, dev, time_us, c3_scores=None):
     """Top-k-only figures: decode contexts (3 queries) as dispatched, with the
     chunked split and with the filtered split forced; the 16-query decode
     top-k on the scorer's C3 scores; prompt calls (256 queries) at each
-    context and key variant over rotated score buffers."""
+    context and key variant over rotated score buffers, and with every query
+    flagged (the exact pass that follows a failed sampled bound)."""
     cur = torch.cuda.current_stream
     out = {}
     dec, dec_split, dec_filter = {}, {}, {}
@@ -245,9 +291,16 @@ def topk_figures(torch, qsa, synth, dev, time_us, c3_scores=None):
             if variant == "continuous":
                 warm = time_us(lambda i: qsa.block_topk(bufs[0], nb, 4, t.width, "prompt", ids=idp, counts=cp,
                                                         ws=wsp, stream=cur()), n=40)
+                # Every query flagged (as if its sampled bound had failed): the
+                # exact rule with one more read of the row.
+                flag = qsa.make_options(topk_path=qsa.PATH_ONEREAD, force_fallback=1)
+                flagged = time_us(lambda i: qsa.block_topk(bufs[i % nbuf], nb, 4, t.width, "prompt", ids=idp,
+                                                           counts=cp, ws=wsp, options=flag, stream=cur()),
+                                  n=max(40, 2 * nbuf))
                 entry.update({"us": round(us, 2), "scores_GBps": round(gbs, 1),
                               "hbm_frac": round(gbs / PEAK_HBM_GBS, 3), "rotated_buffers": nbuf,
-                              "rotated_MiB": round(nbuf * touched / 2 ** 20), "warm_us": round(warm, 2)})
+                              "rotated_MiB": round(nbuf * touched / 2 ** 20), "warm_us": round(warm, 2),
+                              "flagged_us": round(flagged, 2)})
             else:  # 64-level keys; all-equal keys (detected during the stream)
                 entry[variant + "_us"] = round(us, 2)
             del bufs

@@ -132,6 +132,10 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
     }
     if (path == QSA_PATH_ONEREAD && n_blocks > kOneReadMaxBatches * kOneReadBatch)
         path = QSA_PATH_SPLIT;  // per-batch counts of longer rows do not fit the LDS table
+    // A query whose sampled bound fails is finished in LDS chunks, keeping up
+    // to r + 1 blocks of each beside a list of as many (select_row_chunked).
+    if (path == QSA_PATH_ONEREAD && 2 * ((int64_t)p.r_blocks + 1) > kOneReadCap)
+        path = QSA_PATH_SPLIT;
     if (path == QSA_PATH_FILTER && p.filter_chunks > kFilterMaxChunks)
         path = QSA_PATH_SPLIT;  // stage B scans at most kFilterMaxChunks chunk headers
     p.path = path;

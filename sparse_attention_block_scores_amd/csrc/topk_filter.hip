@@ -331,7 +331,9 @@ __global__ __launch_bounds__(kOneReadThreads) void gather_kernel(FilterArgs a)
         write_first_cells<NT>(g, q, qs.wq);  // every visible key equal: ties go to the lowest cells
         return;
     }
-    // The exact rule over the whole row, with its key range from the headers.
+    // The exact rule over the whole row, with its key range from the headers
+    // (a few queries: the row was just read by the first launch, and its
+    // passes here mostly hit the caches).
     if (qs.tail != 0)
         widen_for_tail(qs, g.bs, count_at_least<NT>(RowKeys{row, VEC}, n, kp, sh));
     select_cells_in<NT>(RowKeys{row, VEC}, n, mn, mx, qs, [&](int i) { return i; }, g, q, sh);

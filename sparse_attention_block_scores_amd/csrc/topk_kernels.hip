@@ -24,9 +24,10 @@
 //    LDS, in block order. If they hold at least the selection's cells, the
 //    threshold is >= LB and the rule over the candidates gives the exact
 //    selection. Otherwise (too few cells, or more candidates than the cap) the
-//    query takes the exact path over its whole row in the same workgroup
-//    (equal keys need no histogram there: their range is empty). Workgroups
-//    never talk to each other, so no device-scope fences are needed.
+//    query takes the exact rule over its whole row in the same workgroup, as
+//    the chunked split in one more read of the row (select_row_chunked).
+//    Workgroups never talk to each other, so no device-scope fences are
+//    needed.
 #include <type_traits>
 
 #include "qsa_internal.h"
@@ -474,11 +475,11 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
         select_from_candidates<NT>(s_ckey, s_cblk, (int)total, kbase, kmax, qs, g, q, sh);
         return;
     }
-    // Flagged: the exact rule over the whole row, read from global memory (the
-    // histograms are zero: no histogram pass ran).
-    if (qs.tail != 0)
-        widen_for_tail(qs, g.bs, count_at_least<NT>(RowKeys{row, VEC}, n, kp, sh));
-    select_cells<NT>(RowKeys{row, VEC}, n, qs, [&](int i) { return i; }, g, q, sh);
+    // Flagged: the exact rule over the whole row with one more read of it, in
+    // chunks through the LDS of the per-wave lists (the histograms are zero:
+    // no histogram pass ran; the plan keeps 2 * (r + 1) within the cap).
+    select_row_chunked<NT, 2 * kOneReadCap, VEC>(row, n, qs, kp, reinterpret_cast<uint32_t *>(s_wlist), s_ckey, s_cblk,
+                                                 kOneReadCap, g, q, sh);
 }
 
 // ------------------------------------------------------------------- utility

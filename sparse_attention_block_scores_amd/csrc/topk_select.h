@@ -414,4 +414,138 @@ __device__ __forceinline__ void select_cells_in(const Src &src, int n, uint32_t 
     emit_selection<NT>(src, n, qs, block_at, g, q, sh, T, above);
 }
 
+// The exact rule over a whole row of n blocks with one read of it, for a
+// query whose sampled bound failed: the chunked split's two stages inside one
+// workgroup (Strata pull #3987, section Approach). The row passes through LDS
+// in chunks of CH blocks (s_chunk, CH words). With r_a = r, or r + 1 when the
+// last visible block is partial (widen_for_tail), each chunk appends to the
+// candidate list, in block order, its own first r_a blocks in (key desc,
+// block asc) order among those at or above the bound lo. A block of the
+// selection has fewer than r_a blocks ahead of it in the whole row, hence in
+// any part of it, so it is kept. When the list reaches 2*r_a entries, or the
+// next chunk could overflow it, the list keeps its own first r_a (the same
+// argument) and lo becomes one above the r_a-th key among them: a later block
+// with a key at or below that key has those r_a blocks ahead of it. The first
+// chunk that keeps r_a blocks into an empty list sets lo the same way. The
+// selection is then made over the list, which holds every selected block and
+// every block whose key is at or above a partial last block's key kp when
+// that block is taken (fewer than r_a blocks are ahead of each of them), so
+// its count of such keys decides the widening as the whole row would (if the
+// block is not taken, the list holds r_a keys at or above kp either way).
+// Needs 2 * r_a <= min(cap, CH); s_ckey and s_cblk hold cap entries; the
+// histograms must be zero on entry. VEC: the row may be read in 16-byte
+// groups up to n rounded up to a multiple of 4.
+template <int NT, int CH, bool VEC>
+__device__ __forceinline__ void select_row_chunked(const float *row, int n, QuerySel qs, uint32_t kp,
+                                                   uint32_t *s_chunk, uint32_t *s_ckey, int32_t *s_cblk,
+                                                   int cap, const TopkGeom &g, int q, SelectShared &sh)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int G = CH / (4 * NT);  // 4-key groups per thread and chunk
+    static_assert(G >= 1 && G * 4 * NT == CH, "a chunk is whole 4-key groups per thread");
+    const uint32_t r_a = (uint32_t)(qs.r + (qs.tail != 0 ? 1 : 0));
+    // Loads at or past the resource's end read zero without a memory access.
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(row), (short)0, (VEC ? ((n + 3) & ~3) : n) * 4, kRowBufferWord3);
+    uint32_t ncand = 0;  // uniform
+    uint32_t lo = 0u;    // keys below lo cannot be selected
+#pragma unroll 1
+    for (int b0 = 0; b0 < n; b0 += CH) {
+        const int nc = min(CH, n - b0);
+        // The chunk's keys into LDS, every load issued before any is used,
+        // counting the keys at or above lo on the way.
+        uint32_t k[G][4];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int i = 4 * ((int)threadIdx.x + NT * j);
+            if constexpr (VEC) {
+                const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, 4 * (b0 + i), 0, 0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    k[j][e] = v[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    k[j][e] = __builtin_amdgcn_raw_buffer_load_b32(rr, 4 * (b0 + i + e), 0, 0);
+            }
+        }
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int i = 4 * ((int)threadIdx.x + NT * j);
+            uint32_t kk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kk[e] = key_of(__uint_as_float(k[j][e]));
+                cnt += (i + e < nc && kk[e] >= lo) ? 1u : 0u;
+            }
+            if (i + 3 < nc) {
+                *reinterpret_cast<uint4 *>(s_chunk + i) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (i + e < nc)
+                        s_chunk[i + e] = kk[e];
+            }
+        }
+        const uint32_t c_ge = wg_sum<NT>(cnt, sh);  // its barriers order the stores before the reads
+        const LdsKeys chunk{s_chunk};
+        // Every key at or above lo (the first nc ties at lo are all of them),
+        // or the chunk's own first r_a when more pass.
+        uint32_t T = lo, budget = (uint32_t)nc, taken = c_ge;
+        if (c_ge > r_a) {
+            uint32_t above;
+            radix_select<NT>(chunk, nc, r_a, sh, T, above);
+            budget = r_a - above;
+            taken = r_a;
+        }
+        if (taken != 0) {
+            uint32_t *ck = s_ckey + ncand;
+            int32_t *cb = s_cblk + ncand;
+            ordered_take<NT>(chunk, nc, T, budget, 1u, 1u, sh, [&](int i, uint32_t pos, uint32_t) {
+                ck[pos] = s_chunk[i];
+                cb[pos] = b0 + i;
+            });
+        }
+        // A list that was empty now holds the first r_a blocks of the row so
+        // far: its r_a-th key bounds the rest as a cut-back list's does.
+        if (ncand == 0 && c_ge > r_a)
+            lo = T != 0xFFFFFFFFu ? T + 1u : T;
+        ncand += taken;
+        lds_barrier();  // the list is written; the chunk buffer is free
+        if (b0 + CH < n && (ncand >= 2 * r_a || ncand + r_a > (uint32_t)cap)) {
+            const LdsKeys list{s_ckey};
+            uint32_t above;
+            radix_select<NT>(list, (int)ncand, r_a, sh, T, above);
+            ordered_take<NT>(list, (int)ncand, T, r_a - above, 1u, 1u, sh, [&](int i, uint32_t pos, uint32_t) {
+                s_chunk[pos] = s_ckey[i];
+                s_chunk[CH / 2 + pos] = (uint32_t)s_cblk[i];
+            });
+            lds_barrier();
+            for (int i = threadIdx.x; i < (int)r_a; i += NT) {
+                s_ckey[i] = s_chunk[i];
+                s_cblk[i] = (int32_t)s_chunk[CH / 2 + i];
+            }
+            ncand = r_a;
+            lo = T != 0xFFFFFFFFu ? T + 1u : T;
+            lds_barrier();
+        }
+    }
+    const LdsKeys list{s_ckey};
+    if (qs.tail != 0)
+        widen_for_tail(qs, g.bs, count_at_least<NT>(list, (int)ncand, kp, sh));
+    uint32_t T, above;
+    radix_select<NT>(list, (int)ncand, (uint32_t)qs.r, sh, T, above);
+    // The emit of select_cells, with the rolled walk (this runs rarely, and
+    // its code shares the instruction cache with the common path's).
+    int32_t *out = g.ids + (int64_t)q * g.width;
+    const uint32_t limit = (uint32_t)qs.wq;
+    ordered_take<NT>(list, (int)ncand, T, (uint32_t)qs.r - above, (uint32_t)g.bs, (uint32_t)qs.last_unit, sh,
+                     [&](int i, uint32_t first, uint32_t cnt) { write_cells(out, first, cnt, s_cblk[i] * g.bs, limit); });
+    for (int p = qs.wq + (int)threadIdx.x; p < g.width; p += NT)
+        out[p] = -1;
+    if (g.counts && threadIdx.x == 0)
+        g.counts[q] = qs.wq;
+}
+
 } // namespace qsa

@@ -101,6 +101,15 @@ def test_forced_paths_and_workspace_growth():
         qsa.topk_workspace_bytes(8, 10000, 4, 2048, "prompt")
     p = qsa.topk_plan(2, 5000, 3, 100, "decode", qsa.make_options(topk_path=qsa.PATH_ONEREAD))
     assert p["path"] == qsa.PATH_ONEREAD and p["r_blocks"] == 34
+    # A flagged one-read query keeps up to r + 1 blocks per LDS chunk beside a
+    # list of as many within the 8,192-block cap: larger selections take the
+    # split, forced or not.
+    one = qsa.make_options(topk_path=qsa.PATH_ONEREAD)
+    assert qsa.topk_plan(2, 200000, 4, 4095 * 4, "prompt", one)["path"] == qsa.PATH_ONEREAD
+    assert qsa.topk_plan(2, 200000, 4, 4095 * 4 + 1, "prompt", one)["path"] == qsa.PATH_SPLIT
+    assert qsa.topk_plan(2, 200000, 1, 4096, "prompt", one)["path"] == qsa.PATH_SPLIT
+    assert qsa.topk_plan(256, 1000000, 4, 4095 * 4 + 1, "prompt")["path"] == qsa.PATH_SPLIT
+    assert qsa.topk_plan(256, 1000000, 4, 4095 * 4, "prompt")["path"] == qsa.PATH_ONEREAD
 
 
 @pytest.mark.parametrize("nb", [1, 4104, 4105, 10240, 16384, 32768, 64512, 100000])

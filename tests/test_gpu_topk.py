@@ -70,6 +70,8 @@ def _keys(tag, variant, nq, n_blocks, ld):
         s[:, :n_blocks] = vals[synth.integers(tag, nq * n_blocks, 0, 4).reshape(nq, n_blocks)]
     elif variant == "sorted":
         s[:, :n_blocks] = np.arange(n_blocks, dtype=np.float32)[None, :] * 0.25
+    elif variant == "descending":
+        s[:, :n_blocks] = np.arange(n_blocks, 0, -1, dtype=np.float32)[None, :] * 0.25
     elif variant == "narrow":  # positive, within one binade, 64 levels: heavy ties
         s[:, :n_blocks] = 1.0 + synth.integers(tag, nq * n_blocks, 0, 63).reshape(nq, n_blocks) / 64.0
     return s
@@ -169,6 +171,29 @@ def test_prompt_contexts_full_size(n_blocks, variant):
         got = gpu_topk(s, n_blocks, wl.block_size, wl.width, "prompt", active=active, options=_opts(path))
         assert_ids_equal(got, exp, f"C4 nb={n_blocks} {variant} {path}")
         assert (got[1] == wl.width).all()
+
+
+@pytest.mark.parametrize("path", ["fallback", "filter_fallback"])
+@pytest.mark.parametrize("variant", ["normal", "q64", "sorted", "descending", "few", "equal"])
+def test_flagged_exact_pass_over_chunks(path, variant):
+    """Flagged queries on rows of several LDS chunks: the one-read path's
+    exact pass in chunks of 16,384 blocks with a ragged last one, selections
+    from 512 blocks up to 4,095 (the list is cut back and the bound rises
+    between chunks; one more, 4,096, takes the split), ascending and
+    descending keys (later chunks add every block or none), ties, and partial
+    last blocks (one block more per chunk); the filtered split's flagged
+    queries on the same rows."""
+    nq, n = 3, 3 * 16384 + 1001
+    s = _keys(f"gpu/flagged/{variant}", variant, nq, n, n)
+    for bs, width in ((4, 2048), (4, 16380), (4, 16384), (1, 4095), (3, 12285)):
+        active = np.array([n, n - 7, 16384 + 3], np.int32)
+        say(f"flagged chunks {variant} {path} bs={bs} w={width}")
+        got = gpu_topk(s, n, bs, width, "prompt", active=active, options=_opts(path))
+        assert_ids_equal(got, oracle.topk_sort(s, n, bs, width, active), f"flagged {variant} {path} w={width}")
+        cells = np.array([n * bs - 1, n * bs - bs - 1, (16384 + 3) * bs - 2], np.int32)
+        got = gpu_topk_cells(s, n, bs, width, "prompt", cells, options=_opts(path))
+        assert_ids_equal(got, oracle.topk_sort_cells(s, n, bs, width, cells),
+                         f"flagged cells {variant} {path} w={width}")
 
 
 def test_workspace_reused_across_calls_of_different_sizes():
