@@ -74,11 +74,16 @@ typedef enum qsa_call {
 } qsa_call;
 
 /* Top-k path choice. AUTO is what production callers use; the others force a
- * path for tests and measurements. Every path returns the same ids. */
+ * path for tests and measurements. Every path returns the same ids. A forced
+ * ONEREAD with rows of more than 64 * 16,384 blocks, or a selection of more
+ * than 4,095 blocks (2 * (r + 1) over the 8,192-block cap of its flagged
+ * pass), and a forced FILTER with more than 1,024 chunks per row, take SPLIT
+ * (qsa_topk_plan_get shows the path taken). */
 enum {
     QSA_PATH_AUTO = 0,
     QSA_PATH_SPLIT = 1,    /* exact chunked split: per-chunk stage A, per-query stage B */
-    QSA_PATH_ONEREAD = 2,  /* sampled bound, one read by one workgroup per query, exact fallback */
+    QSA_PATH_ONEREAD = 2,  /* sampled bound, one read by one workgroup per query; a flagged query
+                              takes the exact rule in one more read of its row */
     QSA_PATH_FILTER = 3    /* sampled bound and one read spread over chunk workgroups (first launch),
                               per-query selection over their candidates (second launch) */
 };
@@ -96,7 +101,7 @@ typedef struct qsa_options {
     int32_t topk_path;      /* QSA_PATH_* */
     int32_t chunk_blocks;   /* SPLIT chunk size in blocks: 0 = auto, else 64..15360, multiple of 4 */
     int32_t sample;         /* QSA_SAMPLE_* */
-    int32_t force_fallback; /* ONEREAD, FILTER: every query takes the exact path over its whole row */
+    int32_t force_fallback; /* ONEREAD, FILTER: every query is flagged (the exact rule over its whole row) */
     int32_t filter_blocks;  /* FILTER chunk size in blocks: 0 = auto, else 1024, 2048, 4096 or 8192 */
     int32_t reserved[3];    /* must be zero */
 } qsa_options;
