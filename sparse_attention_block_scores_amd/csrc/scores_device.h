@@ -15,9 +15,10 @@
 //    of its own q row and of its key row; the sum is the same dot product in
 //    another order.
 //  * Columns: key tiles of 32 blocks x 128 floats (16 KB) are staged in LDS,
-//    double-buffered; the next tile's global loads are in flight while the
-//    current tile's 64*MR MFMAs run. LDS rows are padded to 132 floats so the
-//    128-bit LDS reads of 32 different key rows hit distinct banks.
+//    double-buffered (in pairs of tiles for 16-wave workgroups); the next
+//    tiles' global loads are in flight while the current tile's 64*MR MFMAs
+//    run. LDS rows are padded to 132 floats so the 128-bit LDS reads of 32
+//    different key rows hit distinct banks.
 //  * Epilogue: the 32x32 accumulator puts rows 8*(v/4) + 4*(lane/32) + v%4
 //    of column lane%32 in register v, so a query's head sum is a few in-lane
 //    adds plus (for HP >= 8) one exchange with lane^32. Only scores leave
@@ -34,11 +35,15 @@ constexpr int kHeadDim = 128;
 constexpr int kTileBlocks = 32;
 constexpr int kLdsRow = 132;  // floats per staged key row (128 + 4 pad)
 
-// LDS of one scoring workgroup: two staged key tiles and the weights of its
+// Key tiles a workgroup of NW waves stages at once: two pairs for 16 waves
+// (a barrier per pair), else two single tiles.
+constexpr int score_tile_buffers(int nw) { return nw == 16 ? 4 : 2; }
+
+// LDS of one scoring workgroup: NK staged key tiles and the weights of its
 // ROWS padded rows.
-template <int ROWS>
+template <int ROWS, int NK>
 struct ScoreLds {
-    __attribute__((aligned(16))) float k[2][kTileBlocks * kLdsRow];
+    __attribute__((aligned(16))) float k[NK][kTileBlocks * kLdsRow];
     float w[ROWS];
 };
 
@@ -131,9 +136,18 @@ __device__ __forceinline__ void score_epilogue(const f32x16 (&acc)[MR], const Sc
 // MFMAs and the epilogue; store(qi, blk, score) receives each score. All
 // threads call; the LDS is free again on return.
 template <int HP, int MR, int NW, class Store>
-__device__ __forceinline__ void score_tiles(const ScoreArgs &a, int row0, int t0, int t1, ScoreLds<NW * MR * 32> &sm,
-                                            Store store)
+__device__ __forceinline__ void score_tiles(const ScoreArgs &a, int row0, int t0, int t1,
+                                            ScoreLds<NW * MR * 32, score_tile_buffers(NW)> &sm, Store store)
 {
+    // 16 waves stage key tiles in pairs with one barrier per pair: between
+    // the two tiles of a pair the waves drift apart, so one wave's epilogue
+    // runs beside other waves' MFMAs instead of all epilogues at once (C5:
+    // 1,941 -> 1,902 us). Their tile loads are clamped to the last block, so
+    // no load sits under a branch (which makes the compiler wait for every
+    // memory access in flight, score stores included, before the next use).
+    // Eight-wave workgroups take a few tiles each, and the pairs' longer
+    // prologue did not pay there (C3: 41.5 -> 48.4 us).
+    constexpr bool PAIRS = score_tile_buffers(NW) == 4;
     constexpr int NT = NW * 64;
     constexpr int ROWS = NW * MR * 32;
     static_assert(HP <= 32 || (HP == 64 && MR == 2), "64 heads need both row tiles of a wave");
@@ -173,10 +187,16 @@ __device__ __forceinline__ void score_tiles(const ScoreArgs &a, int row0, int t0
 #pragma unroll
         for (int i = 0; i < GPT; ++i) {
             const int gidx = tid + NT * i;
-            const int blk = t * kTileBlocks + (gidx >> 5);
-            pre[i] = blk < a.n_blocks
-                         ? reinterpret_cast<const float4 *>(a.k + (int64_t)blk * kHeadDim)[gidx & 31]
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+            if constexpr (PAIRS) {
+                // Past the last block: the last block again (never scored).
+                const int blk = min(t * kTileBlocks + (gidx >> 5), a.n_blocks - 1);
+                pre[i] = reinterpret_cast<const float4 *>(a.k + (int64_t)blk * kHeadDim)[gidx & 31];
+            } else {
+                const int blk = t * kTileBlocks + (gidx >> 5);
+                pre[i] = blk < a.n_blocks
+                             ? reinterpret_cast<const float4 *>(a.k + (int64_t)blk * kHeadDim)[gidx & 31]
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
     };
     auto store_tile = [&](float *dst) {
@@ -187,44 +207,81 @@ __device__ __forceinline__ void score_tiles(const ScoreArgs &a, int row0, int t0
         }
     };
 
-    load_tile(t0);
-    store_tile(sm.k[0]);
-    __syncthreads();
-
-    for (int t = t0; t < t1; ++t) {
-        const int cur = (t - t0) & 1;
-        if (t + 1 < t1)
-            load_tile(t + 1);
-
-        // A wave whose rows are all padding skips the MFMAs and the epilogue
-        // (it still stages key tiles and meets every barrier).
-        if (live) {
-            f32x16 acc[MR];
+    // One key tile (staged at kt) through the MFMAs and the epilogue. A wave
+    // whose rows are all padding skips both (it still stages key tiles and
+    // meets every barrier).
+    auto score_tile = [&](int t, const float *kt) {
+        if (!live)
+            return;
+        f32x16 acc[MR];
 #pragma unroll
-            for (int m = 0; m < MR; ++m)
+        for (int m = 0; m < MR; ++m)
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    acc[m][v] = 0.f;
-            const float *kb = &sm.k[cur][li * kLdsRow + 64 * half];
+            for (int v = 0; v < 16; ++v)
+                acc[m][v] = 0.f;
+        const float *kb = kt + li * kLdsRow + 64 * half;
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const float4 b = *reinterpret_cast<const float4 *>(kb + 4 * u);
-                const float bv[4] = {b.x, b.y, b.z, b.w};
+        for (int u = 0; u < 16; ++u) {
+            const float4 b = *reinterpret_cast<const float4 *>(kb + 4 * u);
+            const float bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
+            for (int e = 0; e < 4; ++e)
 #pragma unroll
-                    for (int m = 0; m < MR; ++m)
-                        acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[m][4 * u + e], bv[e], acc[m], 0, 0, 0);
-            }
-
-            score_epilogue<HP, MR>(
-                acc, a, row0, wv, half, t * kTileBlocks + li,
-                [&](int m, int v) { return sm.w[(wv * MR + m) * 32 + 8 * (v >> 2) + 4 * half + (v & 3)]; }, store);
+                for (int m = 0; m < MR; ++m)
+                    acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[m][4 * u + e], bv[e], acc[m], 0, 0, 0);
         }
+        score_epilogue<HP, MR>(
+            acc, a, row0, wv, half, t * kTileBlocks + li,
+            [&](int m, int v) { return sm.w[(wv * MR + m) * 32 + 8 * (v >> 2) + 4 * half + (v & 3)]; }, store);
+    };
 
-        if (t + 1 < t1)
-            store_tile(sm.k[cur ^ 1]);
+    if constexpr (PAIRS) {
+        // Pair p of the range sits in LDS half p % 2; the next pair waits in
+        // a two-tile register ring, and the pair after it is being loaded.
+        float4 ring[2][GPT];
+        auto load_into = [&](int t, float4 (&dst)[GPT]) {
+            load_tile(t);
+#pragma unroll
+            for (int i = 0; i < GPT; ++i)
+                dst[i] = pre[i];
+        };
+        auto store_from = [&](const float4 (&src)[GPT], float *dst) {
+#pragma unroll
+            for (int i = 0; i < GPT; ++i)
+                pre[i] = src[i];
+            store_tile(dst);
+        };
+        load_into(t0, ring[0]);
+        load_into(t0 + 1, ring[1]);
+        store_from(ring[0], sm.k[0]);
+        store_from(ring[1], sm.k[1]);
+        load_into(t0 + 2, ring[0]);
+        load_into(t0 + 3, ring[1]);
         __syncthreads();
+        for (int tb = t0; tb < t1; tb += 2) {
+            const int h = ((tb - t0) >> 1) & 1;
+            score_tile(tb, sm.k[2 * h]);
+            if (tb + 1 < t1)
+                score_tile(tb + 1, sm.k[2 * h + 1]);
+            store_from(ring[0], sm.k[2 * (h ^ 1)]);
+            store_from(ring[1], sm.k[2 * (h ^ 1) + 1]);
+            load_into(tb + 4, ring[0]);
+            load_into(tb + 5, ring[1]);
+            __syncthreads();
+        }
+    } else {
+        load_tile(t0);
+        store_tile(sm.k[0]);
+        __syncthreads();
+        for (int t = t0; t < t1; ++t) {
+            const int cur = (t - t0) & 1;
+            if (t + 1 < t1)
+                load_tile(t + 1);
+            score_tile(t, sm.k[cur]);
+            if (t + 1 < t1)
+                store_tile(sm.k[cur ^ 1]);
+            __syncthreads();
+        }
     }
 }
 

@@ -32,7 +32,7 @@ template <int HP, int MR, int NW, bool BF16>
 __global__ __launch_bounds__(NW * 64, NW >= 8 && HP >= 4 ? 4 : 2) void scores_kernel(ScoreArgs a, ScoreGrid grid)
 {
     constexpr int ROWS = NW * MR * 32;
-    using Lds = typename std::conditional<BF16, ScoreLdsH<ROWS>, ScoreLds<ROWS>>::type;
+    using Lds = typename std::conditional<BF16, ScoreLdsH<ROWS>, ScoreLds<ROWS, score_tile_buffers(NW)>>::type;
     __shared__ Lds sm;
 
     int slab, grp;
