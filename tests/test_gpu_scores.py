@@ -172,3 +172,33 @@ def test_bf16_prompt_select_shape_sampled():
     err = np.abs(s[qi, bi].astype(np.float64) - ref)
     assert (err <= tol).all(), f"worst {np.max(err / tol):.3f} x tolerance"
     assert_scores_close(s[:2], rows, "bf16 C5 rows 0-1")
+
+
+def test_score_rows_past_4gib():
+    """Score rows 2.4 GB apart (a 7.2 GB score buffer; the third row starts
+    past 2^32 bytes): the FP32 scorer writes every row at its 64-bit offset
+    and nothing past n_blocks. The BF16 scorer, whose buffer stores address
+    the rows of 32 queries with 31-bit offsets, rejects a row stride of 2^24
+    floats or more before any launch."""
+    nq, heads, n, ld = 3, 8, 3000, 600_000_000
+    tag = "gpu/scores/far"
+    q = synth.normal(tag + "/q", (nq, heads, 128))
+    k = synth.normal(tag + "/k", (n, 128))
+    w = synth.uniform01(tag + "/w", (nq, heads))
+    big = torch.empty((nq, ld), dtype=torch.float32, device="cuda")
+    big[:, n:n + 64] = 7.0
+    say("scores rows past 4 GiB")
+    qsa.block_scores(to_dev(q), to_dev(k), to_dev(w), scores=big)
+    torch.cuda.synchronize()
+    got = big[:, :n].cpu().numpy()
+    ref = oracle.block_scores(q, k, w)
+    terms = oracle.block_scores(np.abs(q), np.abs(k), np.abs(w))
+    assert_scores_close(got, ref, "rows past 4 GiB", terms)
+    assert (big[:, n:n + 64] == 7.0).all(), "columns past n_blocks were written"
+    qb = to_dev(q).to(torch.bfloat16)
+    kb = to_dev(k).to(torch.bfloat16)
+    with pytest.raises(qsa.QSAError, match="unsupported"):
+        qsa.block_scores_bf16(qb, kb, to_dev(w), scores=big)
+    assert (big[:, n:n + 64] == 7.0).all()
+    del big
+    torch.cuda.empty_cache()

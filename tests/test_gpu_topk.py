@@ -196,6 +196,45 @@ def test_flagged_exact_pass_over_chunks(path, variant):
                          f"flagged cells {variant} {path} w={width}")
 
 
+def test_oneread_longest_row():
+    """The one-read path's longest row (64 batches of 16,384 blocks: 4 MiB of
+    scores per query), sampled and with every query flagged, and one block
+    more, which takes the split."""
+    nq, n = 3, 64 * 16384
+    s = _keys("gpu/topk/longest", "normal", nq, n + 1, n + 1)
+    for nb in (n, n + 1):
+        active = np.array([nb, nb - 5, nb // 2 + 3], np.int32)
+        exp = oracle.topk_sort(s, nb, 4, 2048, active)
+        for path in ("oneread_lines", "fallback", "filter"):
+            plan = qsa.topk_plan(nq, nb, 4, 2048, "prompt", _opts(path))["path"]
+            if path != "filter":
+                assert plan == (qsa.PATH_ONEREAD if nb == n else qsa.PATH_SPLIT), (nb, path)
+            say(f"longest row nb={nb} {path}")
+            got = gpu_topk(s, nb, 4, 2048, "prompt", active=active, options=_opts(path))
+            assert_ids_equal(got, exp, f"longest row nb={nb} {path}")
+
+
+def test_rows_past_4gib():
+    """Score rows 2.4 GB apart in a 7.2 GB buffer: every path reads rows at
+    64-bit offsets (the third row starts past 2^32 bytes). Only the visible
+    blocks are written."""
+    dev = device()
+    nq, n, ld = 3, 50000, 600_000_000
+    host = _keys("gpu/topk/far", "normal", nq, n, n)
+    big = torch.empty((nq, ld), dtype=torch.float32, device=dev)
+    big[:, :n] = torch.from_numpy(host).to(dev)
+    view = big[:, :n]
+    assert view.stride(0) == ld and 2 * ld * 4 > 2 ** 32
+    active = np.array([n, n - 3, 12345], np.int32)
+    exp = oracle.topk_sort(host, n, 4, 2048, active)
+    for path in ("auto", "split", "oneread_lines", "fallback", "filter", "filter_fallback"):
+        say(f"rows past 4 GiB {path}")
+        got = gpu_topk(None, n, 4, 2048, "prompt", active=active, options=_opts(path), scores_dev=view)
+        assert_ids_equal(got, exp, f"rows past 4 GiB {path}")
+    del big, view
+    torch.cuda.empty_cache()
+
+
 def test_workspace_reused_across_calls_of_different_sizes():
     dev = device()
     need = max(qsa.topk_workspace_bytes(8, 20000, 4, 2048, "prompt"),
