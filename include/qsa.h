@@ -68,6 +68,9 @@ typedef enum qsa_status {
     QSA_EHIP = 4           /* a HIP launch or runtime call failed */
 } qsa_status;
 
+/* The kind of call. Entry points take it as an int32_t `call` (as
+ * qsa_status_str takes its code), so that any value a caller passes is a
+ * valid argument and anything else is rejected with QSA_EINVAL. */
 typedef enum qsa_call {
     QSA_DECODE = 0,  /* no active-block count: every block is visible */
     QSA_PROMPT = 1   /* optional per-query active-block count */
@@ -167,11 +170,11 @@ qsa_status qsa_block_scores_bf16(const void *q, const void *k, const float *w,
 /* Bytes of workspace qsa_block_topk / qsa_select need for these sizes and
  * options (0 if the arguments are invalid). */
 size_t qsa_topk_workspace_bytes(int32_t nq, int32_t n_blocks, int32_t block_size,
-                                int32_t width, qsa_call call, const qsa_options *opt);
+                                int32_t width, int32_t call, const qsa_options *opt);
 
 /* Fill the plan for these arguments (host only; no GPU needed). */
 qsa_status qsa_topk_plan_get(int32_t nq, int32_t n_blocks, int32_t block_size,
-                             int32_t width, qsa_call call, const qsa_options *opt,
+                             int32_t width, int32_t call, const qsa_options *opt,
                              qsa_topk_plan *out);
 
 /* Zero-fill `bytes` of workspace on `stream` (a kernel, not a memset). */
@@ -192,7 +195,7 @@ qsa_status qsa_workspace_init(void *workspace, size_t bytes, void *stream);
  */
 qsa_status qsa_block_topk(const float *scores, int64_t ld_scores, int32_t nq,
                           int32_t n_blocks, int32_t block_size, int32_t width,
-                          qsa_call call, const int32_t *active_blocks,
+                          int32_t call, const int32_t *active_blocks,
                           int32_t *cell_ids, int32_t *counts,
                           void *workspace, size_t workspace_bytes, void *stream,
                           const qsa_options *opt);
@@ -214,7 +217,7 @@ qsa_status qsa_block_topk(const float *scores, int64_t ld_scores, int32_t nq,
  */
 qsa_status qsa_block_topk_cells(const float *scores, int64_t ld_scores, int32_t nq,
                                 int32_t n_blocks, int32_t block_size, int32_t width,
-                                qsa_call call, const int32_t *visible_cells,
+                                int32_t call, const int32_t *visible_cells,
                                 int32_t *cell_ids, int32_t *counts,
                                 void *workspace, size_t workspace_bytes, void *stream,
                                 const qsa_options *opt);
@@ -240,7 +243,7 @@ qsa_status qsa_block_topk_cells(const float *scores, int64_t ld_scores, int32_t 
 #define QSA_NOALLOC_SCRATCH_BYTES (16u << 20)
 qsa_status qsa_block_topk_noalloc(const float *scores, int64_t ld_scores, int32_t nq,
                                   int32_t n_blocks, int32_t block_size, int32_t width,
-                                  qsa_call call, const int32_t *active_blocks,
+                                  int32_t call, const int32_t *active_blocks,
                                   int32_t *cell_ids, int32_t *counts, void *stream);
 
 /*
@@ -251,7 +254,7 @@ qsa_status qsa_block_topk_noalloc(const float *scores, int64_t ld_scores, int32_
 qsa_status qsa_select(const float *q, const float *k, const float *w,
                       int32_t n_heads, int32_t head_dim,
                       float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks,
-                      int32_t block_size, int32_t width, qsa_call call,
+                      int32_t block_size, int32_t width, int32_t call,
                       const int32_t *active_blocks, int32_t *cell_ids, int32_t *counts,
                       void *workspace, size_t workspace_bytes, void *stream,
                       const qsa_options *opt);
@@ -260,7 +263,7 @@ qsa_status qsa_select(const float *q, const float *k, const float *w,
 qsa_status qsa_select_cells(const float *q, const float *k, const float *w,
                             int32_t n_heads, int32_t head_dim,
                             float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks,
-                            int32_t block_size, int32_t width, qsa_call call,
+                            int32_t block_size, int32_t width, int32_t call,
                             const int32_t *visible_cells, int32_t *cell_ids, int32_t *counts,
                             void *workspace, size_t workspace_bytes, void *stream,
                             const qsa_options *opt);
@@ -332,8 +335,8 @@ qsa_status qsa_selection_attention_shared(const void *q, const void *k, const vo
                                           int32_t n_cells, int32_t width, float scale,
                                           void *workspace, size_t workspace_bytes, void *stream);
 
-/* Static text for a status code. */
-const char *qsa_status_str(qsa_status status);
+/* Static text for a status code (a qsa_status; other values get a text too). */
+const char *qsa_status_str(int32_t status);
 
 #ifdef __cplusplus
 }

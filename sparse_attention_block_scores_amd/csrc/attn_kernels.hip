@@ -561,7 +561,7 @@ bool make_attn_plan(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width
         if (group > kPairHeads || width > kPairMaxWidth)
             return false;
         p.shared = 1;
-        p.pairs = (nq + 1) / 2;
+        p.pairs = nq / 2 + (nq & 1);
         p.hblocks = 1;
         p.units = (int64_t)p.pairs * kv_heads;
         list = 2 * width;
@@ -573,13 +573,15 @@ bool make_attn_plan(int32_t nq, int32_t n_heads, int32_t kv_heads, int32_t width
         p.hblocks = (group + kAttnHeadBlock - 1) / kAttnHeadBlock;
         p.units = (int64_t)nq * kv_heads * p.hblocks;
     }
-    const int32_t steps = (list + kAttnStepCells - 1) / kAttnStepCells;
-    const int32_t max_chunks = (steps + kAttnWaves - 1) / kAttnWaves;
+    // (64-bit: width may be as large as 2^31 - 1.)
+    const int64_t steps = ((int64_t)list + kAttnStepCells - 1) / kAttnStepCells;
+    const int64_t max_chunks = (steps + kAttnWaves - 1) / kAttnWaves;
     int64_t chunks = p.units > 0 ? (kAttnTargetGroups + p.units - 1) / p.units : 1;
     chunks = chunks < 1 ? 1 : (chunks > max_chunks ? max_chunks : chunks);
     chunks = chunks > kAttnMaxChunks ? kAttnMaxChunks : chunks;  // the merge loads every partial at once
     p.steps_per_wave = (int32_t)((steps + kAttnWaves * chunks - 1) / (kAttnWaves * chunks));
-    p.n_chunks = (steps + kAttnWaves * p.steps_per_wave - 1) / (kAttnWaves * p.steps_per_wave);
+    p.n_chunks = (int32_t)((steps + (int64_t)kAttnWaves * p.steps_per_wave - 1) /
+                           ((int64_t)kAttnWaves * p.steps_per_wave));
     if (p.units * p.n_chunks * kAttnHeadBlock > 0x7fffffffLL)
         return false;
     size_t off = 0;

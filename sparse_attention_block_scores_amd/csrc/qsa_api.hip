@@ -43,7 +43,7 @@ qsa_status check_options(const qsa_options *opt)
 } // namespace
 
 qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int32_t width,
-                          qsa_call call, const qsa_options *opt, TopkPlan &plan)
+                          int32_t call, const qsa_options *opt, TopkPlan &plan)
 {
     memset(&plan, 0, sizeof plan);
     if (nq < 0 || n_blocks < 0 || block_size < 1 || width < 1)
@@ -65,18 +65,19 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
 
     // Split geometry: the fewest chunks of at most kChunkBound blocks, equal
     // sizes rounded up to a multiple of 4 (or the forced size).
+    // (64-bit sums: n_blocks may be as large as 2^31 - 1 with one-cell blocks.)
     if (opt && opt->chunk_blocks) {
         p.chunk_blocks = opt->chunk_blocks;
     } else {
-        const int32_t nb = n_blocks > 0 ? n_blocks : 1;
-        const int32_t k = (nb + kChunkBound - 1) / kChunkBound;
-        p.chunk_blocks = ((nb + k - 1) / k + 3) / 4 * 4;
+        const int64_t nb = n_blocks > 0 ? n_blocks : 1;
+        const int64_t k = (nb + kChunkBound - 1) / kChunkBound;
+        p.chunk_blocks = (int32_t)(((nb + k - 1) / k + 3) / 4 * 4);
     }
-    p.n_chunks = n_blocks > 0 ? (n_blocks + p.chunk_blocks - 1) / p.chunk_blocks : 1;
+    p.n_chunks = n_blocks > 0 ? (int32_t)(((int64_t)n_blocks + p.chunk_blocks - 1) / p.chunk_blocks) : 1;
     p.split_threads = kSplitThreads;
     // Room for one block more per chunk: a query whose last visible block is
     // partial keeps r + 1 candidates per chunk (qsa_block_topk_cells).
-    const int64_t cap_c = p.r_blocks + 1 < p.chunk_blocks ? p.r_blocks + 1 : p.chunk_blocks;
+    const int64_t cap_c = (int64_t)p.r_blocks + 1 < p.chunk_blocks ? (int64_t)p.r_blocks + 1 : p.chunk_blocks;
     plan.cand_stride = ((int64_t)p.n_chunks * (cap_c > 0 ? cap_c : 1) + 3) / 4 * 4;
     p.stage_b_lds = plan.cand_stride <= kStageBLdsWords ? 1 : 0;
 
@@ -86,7 +87,7 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
     p.cap = kOneReadCap;
     p.sample_stride = kSampleStride;
     p.sample_mode = (opt && opt->sample) ? opt->sample : QSA_SAMPLE_LINES;
-    p.ks = 2 * p.r_blocks / kSampleStride + 16;
+    p.ks = (int32_t)(2 * (int64_t)p.r_blocks / kSampleStride + 16);
 
     // Filtered split geometry: chunks of 1,024-8,192 blocks, the largest size
     // that still gives about kFilterTargetGroups first-launch workgroups (or
@@ -162,7 +163,7 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
 namespace {
 
 qsa_status check_topk_args(const float *scores, int64_t ld, int32_t nq, int32_t n_blocks,
-                           qsa_call call, const int32_t *active, const int32_t *cells,
+                           int32_t call, const int32_t *active, const int32_t *cells,
                            const int32_t *ids, const int32_t *counts)
 {
     if (nq > 0 && (!scores || !ids))
@@ -263,7 +264,7 @@ using namespace qsa;
 namespace {
 
 qsa_status topk_call(const float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks, int32_t block_size,
-                     int32_t width, qsa_call call, const int32_t *active, const int32_t *cells,
+                     int32_t width, int32_t call, const int32_t *active, const int32_t *cells,
                      int32_t *cell_ids, int32_t *counts, void *workspace, size_t workspace_bytes,
                      void *stream, const qsa_options *opt)
 {
@@ -285,7 +286,7 @@ qsa_status topk_call(const float *scores, int64_t ld_scores, int32_t nq, int32_t
 
 qsa_status select_call(const float *q, const float *k, const float *w, int32_t n_heads, int32_t head_dim,
                        float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks, int32_t block_size,
-                       int32_t width, qsa_call call, const int32_t *active, const int32_t *cells,
+                       int32_t width, int32_t call, const int32_t *active, const int32_t *cells,
                        int32_t *cell_ids, int32_t *counts, void *workspace, size_t workspace_bytes,
                        void *stream, const qsa_options *opt)
 {
@@ -358,7 +359,7 @@ qsa_status device_scratch(hipStream_t s, void **out)
 extern "C" {
 
 qsa_status qsa_block_topk_noalloc(const float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks,
-                                  int32_t block_size, int32_t width, qsa_call call, const int32_t *active_blocks,
+                                  int32_t block_size, int32_t width, int32_t call, const int32_t *active_blocks,
                                   int32_t *cell_ids, int32_t *counts, void *stream)
 {
     TopkPlan plan;
@@ -381,7 +382,7 @@ qsa_status qsa_block_topk_noalloc(const float *scores, int64_t ld_scores, int32_
     return run_topk(g, plan, ws, (hipStream_t)stream, nullptr);
 }
 
-const char *qsa_status_str(qsa_status status)
+const char *qsa_status_str(int32_t status)
 {
     switch (status) {
     case QSA_OK: return "ok";
@@ -394,7 +395,7 @@ const char *qsa_status_str(qsa_status status)
 }
 
 qsa_status qsa_topk_plan_get(int32_t nq, int32_t n_blocks, int32_t block_size, int32_t width,
-                             qsa_call call, const qsa_options *opt, qsa_topk_plan *out)
+                             int32_t call, const qsa_options *opt, qsa_topk_plan *out)
 {
     if (!out)
         return QSA_EINVAL;
@@ -406,7 +407,7 @@ qsa_status qsa_topk_plan_get(int32_t nq, int32_t n_blocks, int32_t block_size, i
 }
 
 size_t qsa_topk_workspace_bytes(int32_t nq, int32_t n_blocks, int32_t block_size, int32_t width,
-                                qsa_call call, const qsa_options *opt)
+                                int32_t call, const qsa_options *opt)
 {
     TopkPlan plan;
     if (make_topk_plan(nq, n_blocks, block_size, width, call, opt, plan) != QSA_OK)
@@ -453,7 +454,7 @@ qsa_status qsa_block_scores_bf16(const void *q, const void *k, const float *w, f
 }
 
 qsa_status qsa_block_topk(const float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks,
-                          int32_t block_size, int32_t width, qsa_call call,
+                          int32_t block_size, int32_t width, int32_t call,
                           const int32_t *active_blocks, int32_t *cell_ids, int32_t *counts,
                           void *workspace, size_t workspace_bytes, void *stream,
                           const qsa_options *opt)
@@ -463,7 +464,7 @@ qsa_status qsa_block_topk(const float *scores, int64_t ld_scores, int32_t nq, in
 }
 
 qsa_status qsa_block_topk_cells(const float *scores, int64_t ld_scores, int32_t nq, int32_t n_blocks,
-                                int32_t block_size, int32_t width, qsa_call call,
+                                int32_t block_size, int32_t width, int32_t call,
                                 const int32_t *visible_cells, int32_t *cell_ids, int32_t *counts,
                                 void *workspace, size_t workspace_bytes, void *stream,
                                 const qsa_options *opt)
@@ -474,7 +475,7 @@ qsa_status qsa_block_topk_cells(const float *scores, int64_t ld_scores, int32_t 
 
 qsa_status qsa_select(const float *q, const float *k, const float *w, int32_t n_heads,
                       int32_t head_dim, float *scores, int64_t ld_scores, int32_t nq,
-                      int32_t n_blocks, int32_t block_size, int32_t width, qsa_call call,
+                      int32_t n_blocks, int32_t block_size, int32_t width, int32_t call,
                       const int32_t *active_blocks, int32_t *cell_ids, int32_t *counts,
                       void *workspace, size_t workspace_bytes, void *stream,
                       const qsa_options *opt)
@@ -485,7 +486,7 @@ qsa_status qsa_select(const float *q, const float *k, const float *w, int32_t n_
 
 qsa_status qsa_select_cells(const float *q, const float *k, const float *w, int32_t n_heads,
                             int32_t head_dim, float *scores, int64_t ld_scores, int32_t nq,
-                            int32_t n_blocks, int32_t block_size, int32_t width, qsa_call call,
+                            int32_t n_blocks, int32_t block_size, int32_t width, int32_t call,
                             const int32_t *visible_cells, int32_t *cell_ids, int32_t *counts,
                             void *workspace, size_t workspace_bytes, void *stream,
                             const qsa_options *opt)

@@ -56,7 +56,7 @@ struct TopkPlan {
 
 // Fills `plan`; returns QSA_OK or the argument error.
 qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int32_t width,
-                          qsa_call call, const qsa_options *opt, TopkPlan &plan);
+                          int32_t call, const qsa_options *opt, TopkPlan &plan);
 
 struct TopkGeom {
     const float *scores;
