@@ -15,10 +15,11 @@
 //    of its own q row and of its key row; the sum is the same dot product in
 //    another order.
 //  * Columns: key tiles of 32 blocks x 128 floats (16 KB) are staged in LDS,
-//    double-buffered (in pairs of tiles for 16-wave workgroups); the next
-//    tiles' global loads are in flight while the current tile's 64*MR MFMAs
-//    run. LDS rows are padded to 132 floats so the 128-bit LDS reads of 32
-//    different key rows hit distinct banks.
+//    double-buffered; the next tiles' global loads are in flight while the
+//    current tile's 64*MR MFMAs run (16-wave workgroups stage pairs of tiles
+//    with loads straight into LDS: score_tiles_dma). LDS rows are padded to
+//    132 floats so the 128-bit LDS reads of 32 different key rows hit
+//    distinct banks.
 //  * Epilogue: the 32x32 accumulator puts rows 8*(v/4) + 4*(lane/32) + v%4
 //    of column lane%32 in register v, so a query's head sum is a few in-lane
 //    adds plus (for HP >= 8) one exchange with lane^32. Only scores leave
@@ -34,16 +35,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kHeadDim = 128;
 constexpr int kTileBlocks = 32;
 constexpr int kLdsRow = 132;  // floats per staged key row (128 + 4 pad)
+// Fourth word of a raw buffer resource on gfx9-family GPUs (32-bit data
+// format, no swizzle); with stride 0 an access at or past num_records bytes
+// is dropped (stores) or reads zero (loads).
+constexpr int kScoreBufferWord3 = 0x00020000;
 
-// Key tiles a workgroup of NW waves stages at once: two pairs for 16 waves
-// (a barrier per pair), else two single tiles.
-constexpr int score_tile_buffers(int nw) { return nw == 16 ? 4 : 2; }
-
-// LDS of one scoring workgroup: NK staged key tiles and the weights of its
+// LDS of one scoring workgroup: two staged key tiles and the weights of its
 // ROWS padded rows.
-template <int ROWS, int NK>
+template <int ROWS>
 struct ScoreLds {
-    __attribute__((aligned(16))) float k[NK][kTileBlocks * kLdsRow];
+    __attribute__((aligned(16))) float k[2][kTileBlocks * kLdsRow];
     float w[ROWS];
 };
 
@@ -136,18 +137,9 @@ __device__ __forceinline__ void score_epilogue(const f32x16 (&acc)[MR], const Sc
 // MFMAs and the epilogue; store(qi, blk, score) receives each score. All
 // threads call; the LDS is free again on return.
 template <int HP, int MR, int NW, class Store>
-__device__ __forceinline__ void score_tiles(const ScoreArgs &a, int row0, int t0, int t1,
-                                            ScoreLds<NW * MR * 32, score_tile_buffers(NW)> &sm, Store store)
+__device__ __forceinline__ void score_tiles(const ScoreArgs &a, int row0, int t0, int t1, ScoreLds<NW * MR * 32> &sm,
+                                            Store store)
 {
-    // 16 waves stage key tiles in pairs with one barrier per pair: between
-    // the two tiles of a pair the waves drift apart, so one wave's epilogue
-    // runs beside other waves' MFMAs instead of all epilogues at once (C5:
-    // 1,941 -> 1,902 us). Their tile loads are clamped to the last block, so
-    // no load sits under a branch (which makes the compiler wait for every
-    // memory access in flight, score stores included, before the next use).
-    // Eight-wave workgroups take a few tiles each, and the pairs' longer
-    // prologue did not pay there (C3: 41.5 -> 48.4 us).
-    constexpr bool PAIRS = score_tile_buffers(NW) == 4;
     constexpr int NT = NW * 64;
     constexpr int ROWS = NW * MR * 32;
     static_assert(HP <= 32 || (HP == 64 && MR == 2), "64 heads need both row tiles of a wave");
@@ -187,16 +179,10 @@ __device__ __forceinline__ void score_tiles(const ScoreArgs &a, int row0, int t0
 #pragma unroll
         for (int i = 0; i < GPT; ++i) {
             const int gidx = tid + NT * i;
-            if constexpr (PAIRS) {
-                // Past the last block: the last block again (never scored).
-                const int blk = min(t * kTileBlocks + (gidx >> 5), a.n_blocks - 1);
-                pre[i] = reinterpret_cast<const float4 *>(a.k + (int64_t)blk * kHeadDim)[gidx & 31];
-            } else {
-                const int blk = t * kTileBlocks + (gidx >> 5);
-                pre[i] = blk < a.n_blocks
-                             ? reinterpret_cast<const float4 *>(a.k + (int64_t)blk * kHeadDim)[gidx & 31]
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+            const int blk = t * kTileBlocks + (gidx >> 5);
+            pre[i] = blk < a.n_blocks
+                         ? reinterpret_cast<const float4 *>(a.k + (int64_t)blk * kHeadDim)[gidx & 31]
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
     auto store_tile = [&](float *dst) {
@@ -235,53 +221,127 @@ __device__ __forceinline__ void score_tiles(const ScoreArgs &a, int row0, int t0
             [&](int m, int v) { return sm.w[(wv * MR + m) * 32 + 8 * (v >> 2) + 4 * half + (v & 3)]; }, store);
     };
 
-    if constexpr (PAIRS) {
-        // Pair p of the range sits in LDS half p % 2; the next pair waits in
-        // a two-tile register ring, and the pair after it is being loaded.
-        float4 ring[2][GPT];
-        auto load_into = [&](int t, float4 (&dst)[GPT]) {
-            load_tile(t);
-#pragma unroll
-            for (int i = 0; i < GPT; ++i)
-                dst[i] = pre[i];
-        };
-        auto store_from = [&](const float4 (&src)[GPT], float *dst) {
-#pragma unroll
-            for (int i = 0; i < GPT; ++i)
-                pre[i] = src[i];
-            store_tile(dst);
-        };
-        load_into(t0, ring[0]);
-        load_into(t0 + 1, ring[1]);
-        store_from(ring[0], sm.k[0]);
-        store_from(ring[1], sm.k[1]);
-        load_into(t0 + 2, ring[0]);
-        load_into(t0 + 3, ring[1]);
+    load_tile(t0);
+    store_tile(sm.k[0]);
+    __syncthreads();
+    for (int t = t0; t < t1; ++t) {
+        const int cur = (t - t0) & 1;
+        if (t + 1 < t1)
+            load_tile(t + 1);
+        score_tile(t, sm.k[cur]);
+        if (t + 1 < t1)
+            store_tile(sm.k[cur ^ 1]);
         __syncthreads();
-        for (int tb = t0; tb < t1; tb += 2) {
-            const int h = ((tb - t0) >> 1) & 1;
-            score_tile(tb, sm.k[2 * h]);
-            if (tb + 1 < t1)
-                score_tile(tb + 1, sm.k[2 * h + 1]);
-            store_from(ring[0], sm.k[2 * (h ^ 1)]);
-            store_from(ring[1], sm.k[2 * (h ^ 1) + 1]);
-            load_into(tb + 4, ring[0]);
-            load_into(tb + 5, ring[1]);
-            __syncthreads();
+    }
+}
+
+
+// The FP32 path of 16-wave workgroups with one row tile per wave (the
+// prompt-call shapes): key tiles go from memory straight into LDS
+// (buffer_load ... lds), so staging holds no registers and issues no LDS
+// writes. Two pairs of tile buffers, kA and kB, are separate LDS arrays: the
+// reads of one pair then need not wait for the loads into the other, and the
+// barrier after a pair waits for them. One load instruction fills half a key
+// row (64 lanes x 4 bytes, in lane order at the instruction's LDS base), so
+// rows keep the 132-float padding of the register-staged path.
+constexpr int kDmaTile = kTileBlocks * kLdsRow;  // floats per staged key tile
+
+template <int HP, class Store>
+__device__ __forceinline__ void score_tiles_dma(const ScoreArgs &a, int row0, int t0, int t1,
+                                                float (&kA)[2][kDmaTile], float (&kB)[2][kDmaTile],
+                                                float *w_lds, Store store)
+{
+    constexpr int NW = 16, MR = 1, NT = NW * 64, ROWS = NW * 32;
+    static_assert(HP <= 32, "one row tile per wave");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, half = lane >> 5;
+    const bool live = __builtin_amdgcn_readfirstlane(row0 + wv * 32) < a.nq * HP;  // wave-uniform
+
+    // q rows of this wave -> VGPRs (A operand).
+    float qa[64];
+    {
+        const int R = row0 + wv * 32 + li;
+        const int qi = R / HP, h = R % HP;
+        const bool ok = qi < a.nq && h < a.heads;
+        const float4 *src = reinterpret_cast<const float4 *>(
+            a.q + ((int64_t)(ok ? qi : 0) * a.heads + (ok ? h : 0)) * kHeadDim + 64 * half);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const float4 v = ok ? src[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+            qa[4 * u + 0] = v.x;
+            qa[4 * u + 1] = v.y;
+            qa[4 * u + 2] = v.z;
+            qa[4 * u + 3] = v.w;
         }
-    } else {
-        load_tile(t0);
-        store_tile(sm.k[0]);
+    }
+    for (int r = tid; r < ROWS; r += NT) {
+        const int R = row0 + r;
+        const int qi = R / HP, h = R % HP;
+        w_lds[r] = (qi < a.nq && h < a.heads) ? a.w[(int64_t)qi * a.heads + h] : 0.f;
+    }
+
+    // Tiles tp and tp + 1 into dst: wave w loads key rows 2w and 2w + 1 of
+    // each, half a row per instruction. The resource spans the pair's
+    // visible blocks (none past the last: those read zero without a memory
+    // access), so every offset stays below 32 KiB whatever n_blocks is.
+    auto issue_pair = [&](int tp, float (&dst)[2][kDmaTile]) {
+        const int64_t first = (int64_t)tp * kTileBlocks;
+        const int64_t left = (int64_t)a.n_blocks - first;
+        const int recs = left <= 0 ? 0 : (int)(left < 2 * kTileBlocks ? left : 2 * kTileBlocks) * kHeadDim * 4;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(a.k + (left > 0 ? first : 0) * kHeadDim), (short)0, recs, kScoreBufferWord3);
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int row = 2 * wv + (x >> 1), part = x & 1;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    r, (__attribute__((address_space(3))) void *)(&dst[d][row * kLdsRow + part * 64]), 4,
+                    ((d * kTileBlocks + row) * kHeadDim + part * 64 + lane) * 4, 0, 0, 0);
+            }
+    };
+
+    // One staged tile through the MFMAs and the epilogue. (Deferring each
+    // epilogue past the next tile's matrix steps, with a second accumulator
+    // set, measured slower here: C5 1,885 -> 1,917 us.)
+    auto score_tile = [&](int t, const float *kt) {
+        if (!live)
+            return;
+        f32x16 acc[MR];
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            acc[0][v] = 0.f;
+        const float *kb = kt + li * kLdsRow + 64 * half;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const float4 b = *reinterpret_cast<const float4 *>(kb + 4 * u);
+            const float bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[4 * u + e], bv[e], acc[0], 0, 0, 0);
+        }
+        score_epilogue<HP, MR>(
+            acc, a, row0, wv, half, t * kTileBlocks + li,
+            [&](int m, int v) { return w_lds[wv * 32 + 8 * (v >> 2) + 4 * half + (v & 3)]; }, store);
+    };
+
+    issue_pair(t0, kA);
+    __syncthreads();  // the first pair and the weights are in LDS
+    for (int tb = t0; tb < t1; tb += 4) {
+        issue_pair(tb + 2, kB);
+        score_tile(tb, kA[0]);
+        if (tb + 1 < t1)
+            score_tile(tb + 1, kA[1]);
+        __syncthreads();  // kB loaded; kA read by every wave
+        if (tb + 2 >= t1)
+            break;
+        issue_pair(tb + 4, kA);
+        score_tile(tb + 2, kB[0]);
+        if (tb + 3 < t1)
+            score_tile(tb + 3, kB[1]);
         __syncthreads();
-        for (int t = t0; t < t1; ++t) {
-            const int cur = (t - t0) & 1;
-            if (t + 1 < t1)
-                load_tile(t + 1);
-            score_tile(t, sm.k[cur]);
-            if (t + 1 < t1)
-                store_tile(sm.k[cur ^ 1]);
-            __syncthreads();
-        }
     }
 }
 
@@ -296,10 +356,6 @@ __device__ __forceinline__ void score_tiles(const ScoreArgs &a, int row0, int t0
 // path's. In ScoreArgs, q and k then point at BF16 data.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kLdsRowH = 136;  // BF16 values per staged key row (128 + 8 pad: 272-byte rows)
-// Fourth word of a raw buffer resource on gfx9-family GPUs (32-bit data
-// format, no swizzle); with stride 0 an access at or past num_records bytes
-// is dropped (stores) or reads zero (loads).
-constexpr int kScoreBufferWord3 = 0x00020000;
 
 template <int ROWS>
 struct ScoreLdsH {

@@ -32,8 +32,7 @@ template <int HP, int MR, int NW, bool BF16>
 __global__ __launch_bounds__(NW * 64, NW >= 8 && HP >= 4 ? 4 : 2) void scores_kernel(ScoreArgs a, ScoreGrid grid)
 {
     constexpr int ROWS = NW * MR * 32;
-    using Lds = typename std::conditional<BF16, ScoreLdsH<ROWS>, ScoreLds<ROWS, score_tile_buffers(NW)>>::type;
-    __shared__ Lds sm;
+    using Lds = typename std::conditional<BF16, ScoreLdsH<ROWS>, ScoreLds<ROWS>>::type;
 
     int slab, grp;
     {
@@ -68,8 +67,17 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 && HP >= 4 ? 4 : 2) void scores_ke
             const int off = ok ? ((qi - qb) * (int)a.ld + blk) * 4 : (int)0x80000000;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), r, off, 0, 0);
         };
+        __shared__ Lds sm;
         score_tiles_bf16<HP, MR, NW>(a, slab * ROWS, t0, t1, sm, store);
+    } else if constexpr (NW == 16 && MR == 1) {
+        // Key tiles straight into LDS (score_tiles_dma): two separate arrays.
+        __shared__ __attribute__((aligned(16))) float kA[2][kDmaTile];
+        __shared__ __attribute__((aligned(16))) float kB[2][kDmaTile];
+        __shared__ float w_lds[ROWS];
+        score_tiles_dma<HP>(a, slab * ROWS, t0, t1, kA, kB, w_lds,
+                            [&](int qi, int blk, float s) { a.scores[(int64_t)qi * a.ld + blk] = s; });
     } else {
+        __shared__ Lds sm;
         score_tiles<HP, MR, NW>(a, slab * ROWS, t0, t1, sm,
                                 [&](int qi, int blk, float s) { a.scores[(int64_t)qi * a.ld + blk] = s; });
     }
