@@ -519,4 +519,105 @@ __device__ __forceinline__ void score_tiles_bf16(const ScoreArgs &a, int row0, i
     }
 }
 
+// The BF16 path of 16-wave workgroups with one row tile per wave: key-tile
+// pairs straight into LDS as in score_tiles_dma (a padded BF16 key row is
+// one load instruction: 64 lanes x 4 bytes), kA and kB separate LDS arrays.
+constexpr int kDmaTileH = kTileBlocks * kLdsRowH;  // BF16 values per staged key tile
+
+template <int HP, class Store>
+__device__ __forceinline__ void score_tiles_bf16_dma(const ScoreArgs &a, int row0, int t0, int t1,
+                                                     uint16_t (&kA)[2][kDmaTileH], uint16_t (&kB)[2][kDmaTileH],
+                                                     float *w_lds, Store store)
+{
+    constexpr int NW = 16, MR = 1, NT = NW * 64, ROWS = NW * 32;
+    static_assert(HP <= 32, "one row tile per wave");
+    const uint16_t *qh = reinterpret_cast<const uint16_t *>(a.q);
+    const uint16_t *kh = reinterpret_cast<const uint16_t *>(a.k);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, half = lane >> 5;
+
+    // q rows of this wave -> VGPRs (A operand): 64 BF16 values per lane.
+    bf16x8 qa[8];
+    {
+        const int R = row0 + wv * 32 + li;
+        const int qi = R / HP, h = R % HP;
+        const bool ok = qi < a.nq && h < a.heads;
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            qh + ((int64_t)(ok ? qi : 0) * a.heads + (ok ? h : 0)) * kHeadDim + 64 * half);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint4 v = ok ? src[u] : make_uint4(0u, 0u, 0u, 0u);
+            qa[u] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    for (int r = tid; r < ROWS; r += NT) {
+        const int R = row0 + r;
+        const int qi = R / HP, h = R % HP;
+        w_lds[r] = (qi < a.nq && h < a.heads) ? a.w[(int64_t)qi * a.heads + h] : 0.f;
+    }
+
+    // Tiles tp and tp + 1 into dst: wave w loads key rows 2w and 2w + 1 of
+    // each, a whole row per instruction; the resource spans the pair's
+    // visible blocks (the rest reads zero without a memory access).
+    auto issue_pair = [&](int tp, uint16_t (&dst)[2][kDmaTileH]) {
+        const int64_t first = (int64_t)tp * kTileBlocks;
+        const int64_t left = (int64_t)a.n_blocks - first;
+        const int recs = left <= 0 ? 0 : (int)(left < 2 * kTileBlocks ? left : 2 * kTileBlocks) * kHeadDim * 2;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(kh + (left > 0 ? first : 0) * kHeadDim), (short)0, recs, kScoreBufferWord3);
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int row = 2 * wv + x;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    r, (__attribute__((address_space(3))) void *)(&dst[d][row * kLdsRowH]), 4,
+                    ((d * kTileBlocks + row) * kHeadDim) * 2 + 4 * lane, 0, 0, 0);
+            }
+    };
+
+    issue_pair(t0, kA);
+    __syncthreads();  // the first pair and the weights are in LDS
+    // This wave's weights, once, in registers.
+    float wr[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+        wr[v] = w_lds[wv * 32 + 8 * (v >> 2) + 4 * half + (v & 3)];
+
+    // One staged tile through the matrix cores and the epilogue (every lane
+    // stores; the store drops what is not a score: MASKED). Waves whose rows
+    // are all padding compute zero rows, whose stores are all dropped.
+    auto score_tile = [&](int t, const uint16_t *kt) {
+        f32x16 acc[MR];
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            acc[0][v] = 0.f;
+        const uint16_t *kb = kt + li * kLdsRowH + 64 * half;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(kb + 8 * u));
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[u], b, acc[0], 0, 0, 0);
+        }
+        score_epilogue<HP, MR, true>(acc, a, row0, wv, half, t * kTileBlocks + li,
+                                     [&](int m, int v) { return wr[v]; }, store);
+    };
+
+    for (int tb = t0; tb < t1; tb += 4) {
+        issue_pair(tb + 2, kB);
+        score_tile(tb, kA[0]);
+        if (tb + 1 < t1)
+            score_tile(tb + 1, kA[1]);
+        __syncthreads();  // kB loaded; kA read by every wave
+        if (tb + 2 >= t1)
+            break;
+        issue_pair(tb + 4, kA);
+        score_tile(tb + 2, kB[0]);
+        if (tb + 3 < t1)
+            score_tile(tb + 3, kB[1]);
+        __syncthreads();
+    }
+}
+
 } // namespace qsa

@@ -67,8 +67,15 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 && HP >= 4 ? 4 : 2) void scores_ke
             const int off = ok ? ((qi - qb) * (int)a.ld + blk) * 4 : (int)0x80000000;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), r, off, 0, 0);
         };
-        __shared__ Lds sm;
-        score_tiles_bf16<HP, MR, NW>(a, slab * ROWS, t0, t1, sm, store);
+        if constexpr (NW == 16 && MR == 1) {
+            __shared__ __attribute__((aligned(16))) uint16_t kA[2][kDmaTileH];
+            __shared__ __attribute__((aligned(16))) uint16_t kB[2][kDmaTileH];
+            __shared__ float w_lds[ROWS];
+            score_tiles_bf16_dma<HP>(a, slab * ROWS, t0, t1, kA, kB, w_lds, store);
+        } else {
+            __shared__ Lds sm;
+            score_tiles_bf16<HP, MR, NW>(a, slab * ROWS, t0, t1, sm, store);
+        }
     } else if constexpr (NW == 16 && MR == 1) {
         // Key tiles straight into LDS (score_tiles_dma): two separate arrays.
         __shared__ __attribute__((aligned(16))) float kA[2][kDmaTile];
