@@ -58,13 +58,15 @@ def test_shapes(heads, nq, n_blocks):
     assert (s[:, n_blocks:] == 7.0).all(), "columns past n_blocks were written"
 
 
-@pytest.mark.parametrize("heads,nq", [(3, 2731), (8, 1030), (13, 515), (31, 257)])
-def test_many_rows(heads, nq):
+@pytest.mark.parametrize("heads,nq,n_blocks", [(3, 2731, 1000), (8, 1030, 1000), (13, 515, 1000), (31, 257, 1000),
+                                               (32, 257, 1500)])
+def test_many_rows(heads, nq, n_blocks):
     """8,192 or more padded (query, head) rows take the 16-wave workgroups
     (one per CU); row counts here are not multiples of their 512-row slabs and
-    1,000 blocks end in a partial key tile."""
-    n_blocks = 1000
-    tag = f"gpu/scores/many/{heads}/{nq}"
+    1,000 blocks end in a partial key tile. 1,500 blocks give 47 key tiles in
+    column groups of three (the last of two, ending in a partial tile): a
+    group's last tile pair is then half used."""
+    tag = f"gpu/scores/many/{heads}/{nq}" + ("" if n_blocks == 1000 else f"/{n_blocks}")
     q = synth.normal(tag + "/q", (nq, heads, 128))
     k = synth.normal(tag + "/k", (n_blocks, 128))
     w = synth.uniform01(tag + "/w", (nq, heads))
@@ -132,10 +134,11 @@ def test_bf16_shapes(heads, nq, n_blocks):
     assert (s[:, n_blocks:] == 7.0).all(), "columns past n_blocks were written"
 
 
-@pytest.mark.parametrize("heads,nq", [(8, 1030), (31, 257)])
-def test_bf16_many_rows(heads, nq):
-    n_blocks = 1000
-    tag = f"gpu/scores_bf16/many/{heads}/{nq}"
+@pytest.mark.parametrize("heads,nq,n_blocks", [(8, 1030, 1000), (31, 257, 1000), (32, 257, 1500)])
+def test_bf16_many_rows(heads, nq, n_blocks):
+    """The 16-wave BF16 workgroups (key-tile pairs loaded straight into LDS),
+    as test_many_rows."""
+    tag = f"gpu/scores_bf16/many/{heads}/{nq}" + ("" if n_blocks == 1000 else f"/{n_blocks}")
     qb = synth.bf16_bits(synth.normal(tag + "/q", (nq, heads, 128)))
     kb = synth.bf16_bits(synth.normal(tag + "/k", (n_blocks, 128)))
     w = synth.uniform01(tag + "/w", (nq, heads))
