@@ -391,7 +391,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build measures the single-GPU hot path "
+        print("bench.py runs on one GPU only: it measures the single-GPU hot path "
               "(use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 

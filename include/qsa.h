@@ -63,7 +63,7 @@ extern "C" {
 typedef enum qsa_status {
     QSA_OK = 0,
     QSA_EINVAL = 1,        /* argument out of range, inconsistent or misaligned */
-    QSA_EUNSUPPORTED = 2,  /* valid request this build does not implement */
+    QSA_EUNSUPPORTED = 2,  /* valid request the library does not implement */
     QSA_EWORKSPACE = 3,    /* workspace NULL, misaligned or too small */
     QSA_EHIP = 4           /* a HIP launch or runtime call failed */
 } qsa_status;
