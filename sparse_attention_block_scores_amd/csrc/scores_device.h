@@ -148,6 +148,30 @@ __device__ __forceinline__ void score_tiles(const ScoreArgs &a, int row0, int t0
     const int li = lane & 31, half = lane >> 5;
     const bool live = __builtin_amdgcn_readfirstlane(row0 + wv * MR * 32) < a.nq * HP;  // wave-uniform
 
+    // Key tile t -> registers: 1024 float4 granules, 1024/NT per thread.
+    constexpr int GPT = (kTileBlocks * kHeadDim / 4) / NT;
+    float4 pre[GPT];
+    auto load_tile = [&](int t) {
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) {
+            const int gidx = tid + NT * i;
+            const int blk = t * kTileBlocks + (gidx >> 5);
+            pre[i] = blk < a.n_blocks
+                         ? reinterpret_cast<const float4 *>(a.k + (int64_t)blk * kHeadDim)[gidx & 31]
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto store_tile = [&](float *dst) {
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) {
+            const int gidx = tid + NT * i;
+            *reinterpret_cast<float4 *>(dst + (gidx >> 5) * kLdsRow + (gidx & 31) * 4) = pre[i];
+        }
+    };
+    // The first tile's loads go out before q's and w's, so that their round
+    // trips overlap (storing w waits for every load issued before it).
+    load_tile(t0);
+
     // q rows of this wave -> VGPRs (A operand).
     float qa[MR][64];
 #pragma unroll
@@ -171,27 +195,6 @@ __device__ __forceinline__ void score_tiles(const ScoreArgs &a, int row0, int t0
         const int qi = R / HP, h = R % HP;
         sm.w[r] = (qi < a.nq && h < a.heads) ? a.w[(int64_t)qi * a.heads + h] : 0.f;
     }
-
-    // Key tile t -> registers: 1024 float4 granules, 1024/NT per thread.
-    constexpr int GPT = (kTileBlocks * kHeadDim / 4) / NT;
-    float4 pre[GPT];
-    auto load_tile = [&](int t) {
-#pragma unroll
-        for (int i = 0; i < GPT; ++i) {
-            const int gidx = tid + NT * i;
-            const int blk = t * kTileBlocks + (gidx >> 5);
-            pre[i] = blk < a.n_blocks
-                         ? reinterpret_cast<const float4 *>(a.k + (int64_t)blk * kHeadDim)[gidx & 31]
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    };
-    auto store_tile = [&](float *dst) {
-#pragma unroll
-        for (int i = 0; i < GPT; ++i) {
-            const int gidx = tid + NT * i;
-            *reinterpret_cast<float4 *>(dst + (gidx >> 5) * kLdsRow + (gidx & 31) * 4) = pre[i];
-        }
-    };
 
     // One key tile (staged at kt) through the MFMAs and the epilogue. A wave
     // whose rows are all padding skips both (it still stages key tiles and
@@ -221,7 +224,6 @@ __device__ __forceinline__ void score_tiles(const ScoreArgs &a, int row0, int t0
             [&](int m, int v) { return sm.w[(wv * MR + m) * 32 + 8 * (v >> 2) + 4 * half + (v & 3)]; }, store);
     };
 
-    load_tile(t0);
     store_tile(sm.k[0]);
     __syncthreads();
     for (int t = t0; t < t1; ++t) {
@@ -380,27 +382,6 @@ __device__ __forceinline__ void score_tiles_bf16(const ScoreArgs &a, int row0, i
     const int li = lane & 31, half = lane >> 5;
     const bool live = __builtin_amdgcn_readfirstlane(row0 + wv * MR * 32) < a.nq * HP;  // wave-uniform
 
-    // q rows of this wave -> VGPRs (A operand): 64 BF16 values per lane.
-    bf16x8 qa[MR][8];
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-        const int R = row0 + (wv * MR + m) * 32 + li;
-        const int qi = R / HP, h = R % HP;
-        const bool ok = qi < a.nq && h < a.heads;
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            qh + ((int64_t)(ok ? qi : 0) * a.heads + (ok ? h : 0)) * kHeadDim + 64 * half);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const uint4 v = ok ? src[u] : make_uint4(0u, 0u, 0u, 0u);
-            qa[m][u] = __builtin_bit_cast(bf16x8, v);
-        }
-    }
-    for (int r = tid; r < ROWS; r += NT) {
-        const int R = row0 + r;
-        const int qi = R / HP, h = R % HP;
-        sm.w[r] = (qi < a.nq && h < a.heads) ? a.w[(int64_t)qi * a.heads + h] : 0.f;
-    }
-
     // Key tile t -> registers: 8 KB per tile, CH bytes per thread. The loads
     // are unconditional (a block past the end re-reads the last block, and
     // its scores are never stored): a load under a branch would make the
@@ -460,8 +441,32 @@ __device__ __forceinline__ void score_tiles_bf16(const ScoreArgs &a, int row0, i
             pre[i] = src[i];
         store_tile(dst);
     };
+    // The first pair's loads go out before q's and w's, so that their round
+    // trips overlap (storing w waits for every load issued before it).
     load_into(t0, ring[0]);
     load_into(t0 + 1, ring[1]);
+
+    // q rows of this wave -> VGPRs (A operand): 64 BF16 values per lane.
+    bf16x8 qa[MR][8];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        const int R = row0 + (wv * MR + m) * 32 + li;
+        const int qi = R / HP, h = R % HP;
+        const bool ok = qi < a.nq && h < a.heads;
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            qh + ((int64_t)(ok ? qi : 0) * a.heads + (ok ? h : 0)) * kHeadDim + 64 * half);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint4 v = ok ? src[u] : make_uint4(0u, 0u, 0u, 0u);
+            qa[m][u] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    for (int r = tid; r < ROWS; r += NT) {
+        const int R = row0 + r;
+        const int qi = R / HP, h = R % HP;
+        sm.w[r] = (qi < a.nq && h < a.heads) ? a.w[(int64_t)qi * a.heads + h] : 0.f;
+    }
+
     store_from(ring[0], sm.k[0]);
     store_from(ring[1], sm.k[1]);
     load_into(t0 + 2, ring[0]);
