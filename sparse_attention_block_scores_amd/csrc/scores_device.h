@@ -261,6 +261,31 @@ __device__ __forceinline__ void score_tiles_dma(const ScoreArgs &a, int row0, in
     const int li = lane & 31, half = lane >> 5;
     const bool live = __builtin_amdgcn_readfirstlane(row0 + wv * 32) < a.nq * HP;  // wave-uniform
 
+    // Tiles tp and tp + 1 into dst: wave w loads key rows 2w and 2w + 1 of
+    // each, half a row per instruction. The resource spans the pair's
+    // visible blocks (none past the last: those read zero without a memory
+    // access), so every offset stays below 32 KiB whatever n_blocks is.
+    auto issue_pair = [&](int tp, float (&dst)[2][kDmaTile]) {
+        const int64_t first = (int64_t)tp * kTileBlocks;
+        const int64_t left = (int64_t)a.n_blocks - first;
+        const int recs = left <= 0 ? 0 : (int)(left < 2 * kTileBlocks ? left : 2 * kTileBlocks) * kHeadDim * 4;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(a.k + (left > 0 ? first : 0) * kHeadDim), (short)0, recs, kScoreBufferWord3);
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int row = 2 * wv + (x >> 1), part = x & 1;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    r, (__attribute__((address_space(3))) void *)(&dst[d][row * kLdsRow + part * 64]), 4,
+                    ((d * kTileBlocks + row) * kHeadDim + part * 64 + lane) * 4, 0, 0, 0);
+            }
+    };
+
+    // The first pair's loads go out before q's and w's, so that their round
+    // trips overlap (storing w waits for every load issued before it).
+    issue_pair(t0, kA);
+
     // q rows of this wave -> VGPRs (A operand).
     float qa[64];
     {
@@ -283,27 +308,6 @@ __device__ __forceinline__ void score_tiles_dma(const ScoreArgs &a, int row0, in
         const int qi = R / HP, h = R % HP;
         w_lds[r] = (qi < a.nq && h < a.heads) ? a.w[(int64_t)qi * a.heads + h] : 0.f;
     }
-
-    // Tiles tp and tp + 1 into dst: wave w loads key rows 2w and 2w + 1 of
-    // each, half a row per instruction. The resource spans the pair's
-    // visible blocks (none past the last: those read zero without a memory
-    // access), so every offset stays below 32 KiB whatever n_blocks is.
-    auto issue_pair = [&](int tp, float (&dst)[2][kDmaTile]) {
-        const int64_t first = (int64_t)tp * kTileBlocks;
-        const int64_t left = (int64_t)a.n_blocks - first;
-        const int recs = left <= 0 ? 0 : (int)(left < 2 * kTileBlocks ? left : 2 * kTileBlocks) * kHeadDim * 4;
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float *>(a.k + (left > 0 ? first : 0) * kHeadDim), (short)0, recs, kScoreBufferWord3);
-#pragma unroll
-        for (int d = 0; d < 2; ++d)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int row = 2 * wv + (x >> 1), part = x & 1;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    r, (__attribute__((address_space(3))) void *)(&dst[d][row * kLdsRow + part * 64]), 4,
-                    ((d * kTileBlocks + row) * kHeadDim + part * 64 + lane) * 4, 0, 0, 0);
-            }
-    };
 
     // One staged tile through the MFMAs and the epilogue. (Deferring each
     // epilogue past the next tile's matrix steps, with a second accumulator
@@ -329,7 +333,6 @@ __device__ __forceinline__ void score_tiles_dma(const ScoreArgs &a, int row0, in
             [&](int m, int v) { return w_lds[wv * 32 + 8 * (v >> 2) + 4 * half + (v & 3)]; }, store);
     };
 
-    issue_pair(t0, kA);
     __syncthreads();  // the first pair and the weights are in LDS
     for (int tb = t0; tb < t1; tb += 4) {
         issue_pair(tb + 2, kB);
@@ -543,26 +546,6 @@ __device__ __forceinline__ void score_tiles_bf16_dma(const ScoreArgs &a, int row
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 31, half = lane >> 5;
 
-    // q rows of this wave -> VGPRs (A operand): 64 BF16 values per lane.
-    bf16x8 qa[8];
-    {
-        const int R = row0 + wv * 32 + li;
-        const int qi = R / HP, h = R % HP;
-        const bool ok = qi < a.nq && h < a.heads;
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            qh + ((int64_t)(ok ? qi : 0) * a.heads + (ok ? h : 0)) * kHeadDim + 64 * half);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const uint4 v = ok ? src[u] : make_uint4(0u, 0u, 0u, 0u);
-            qa[u] = __builtin_bit_cast(bf16x8, v);
-        }
-    }
-    for (int r = tid; r < ROWS; r += NT) {
-        const int R = row0 + r;
-        const int qi = R / HP, h = R % HP;
-        w_lds[r] = (qi < a.nq && h < a.heads) ? a.w[(int64_t)qi * a.heads + h] : 0.f;
-    }
-
     // Tiles tp and tp + 1 into dst: wave w loads key rows 2w and 2w + 1 of
     // each, a whole row per instruction; the resource spans the pair's
     // visible blocks (the rest reads zero without a memory access).
@@ -583,7 +566,30 @@ __device__ __forceinline__ void score_tiles_bf16_dma(const ScoreArgs &a, int row
             }
     };
 
+    // The first pair's loads go out before q's and w's, so that their round
+    // trips overlap (storing w waits for every load issued before it).
     issue_pair(t0, kA);
+
+    // q rows of this wave -> VGPRs (A operand): 64 BF16 values per lane.
+    bf16x8 qa[8];
+    {
+        const int R = row0 + wv * 32 + li;
+        const int qi = R / HP, h = R % HP;
+        const bool ok = qi < a.nq && h < a.heads;
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            qh + ((int64_t)(ok ? qi : 0) * a.heads + (ok ? h : 0)) * kHeadDim + 64 * half);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint4 v = ok ? src[u] : make_uint4(0u, 0u, 0u, 0u);
+            qa[u] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    for (int r = tid; r < ROWS; r += NT) {
+        const int R = row0 + r;
+        const int qi = R / HP, h = R % HP;
+        w_lds[r] = (qi < a.nq && h < a.heads) ? a.w[(int64_t)qi * a.heads + h] : 0.f;
+    }
+
     __syncthreads();  // the first pair and the weights are in LDS
     // This wave's weights, once, in registers.
     float wr[16];
