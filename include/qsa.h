@@ -118,7 +118,7 @@ typedef struct qsa_topk_plan {
     int32_t n_chunks;        /* SPLIT chunks per query */
     int32_t split_threads;   /* SPLIT workgroup size */
     int32_t stage_b_lds;     /* 1 if stage B keeps its candidates in LDS */
-    int32_t oneread_blocks;  /* ONEREAD blocks streamed per batch */
+    int32_t oneread_blocks;  /* ONEREAD blocks streamed per batch (halved for short rows) */
     int32_t cap;             /* ONEREAD, FILTER candidate cap per query (blocks) */
     int32_t sample_stride;   /* 32 */
     int32_t sample_mode;     /* QSA_SAMPLE_STRIDE or QSA_SAMPLE_LINES */

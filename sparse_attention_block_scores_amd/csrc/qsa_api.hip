@@ -83,7 +83,7 @@ qsa_status make_topk_plan(int32_t nq, int32_t n_blocks, int32_t block_size, int3
 
     // One-read geometry: one workgroup streams each query's row in batches of
     // blocks (one slice per wave).
-    p.oneread_blocks = kOneReadBatch;
+    p.oneread_blocks = oneread_short_slices(nq, n_blocks) ? kOneReadShortBatch : kOneReadBatch;
     p.cap = kOneReadCap;
     p.sample_stride = kSampleStride;
     p.sample_mode = (opt && opt->sample) ? opt->sample : QSA_SAMPLE_LINES;

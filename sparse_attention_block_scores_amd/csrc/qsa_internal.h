@@ -18,6 +18,22 @@ constexpr int kOneReadF4 = 4;             // float4 loads per lane and slice
 constexpr int kOneReadBuffers = 2;        // slices in flight per lane
 constexpr int kOneReadBatch = kOneReadThreads * kOneReadF4 * 4;  // blocks streamed per batch
 constexpr int kOneReadMaxBatches = 64;    // the one-read path takes rows of up to 64 batches
+// Short streams use slices half as long (kOneReadShortF4 float4 loads per
+// lane): more slices per wave balance the waves' ends better. Measured on
+// MI355X: 256 queries x 32,768 blocks 14.4 -> 13.5 us, 65,536 blocks equal
+// or better, longer rows no gain; with 3 queries (a lone workgroup streams
+// each row) 10,240 / 16,384 blocks 8.8 -> 8.3 / 9.4 -> 9.2 us but 32,768 /
+// 64,512 blocks 0.2 / 0.4 us slower.
+constexpr int kOneReadShortF4 = 2;
+constexpr int kOneReadShortRow = 65536;     // many queries: rows up to this many blocks
+constexpr int kOneReadShortFewRow = 16384;  // few queries: rows up to this many blocks
+constexpr int kOneReadShortQueries = 64;    // "many"
+constexpr int kOneReadShortBatch = kOneReadThreads * kOneReadShortF4 * 4;
+
+inline bool oneread_short_slices(int32_t nq, int32_t n_blocks)
+{
+    return n_blocks <= kOneReadShortFewRow || (nq >= kOneReadShortQueries && n_blocks <= kOneReadShortRow);
+}
 constexpr int kChunkBound = 4104;         // split chunks: the fewest of at most this many blocks
 constexpr int kMinChunk = 64;
 constexpr int kMaxChunk = 15360;          // keeps a chunk's keys under 60 KB of LDS

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(NT) void oneread_kernel(OneReadArgs a)
     constexpr int MAXS = kOneReadMaxBatches * NW;         // slices of the longest row taken here
     constexpr int WCAP = kOneReadCap / NW;                // candidates a wave may keep
     constexpr int SPT = kOneReadSample / NT;              // sample keys per thread
-    static_assert(kOneReadBatch == NW * STEP, "a batch is one slice per wave");
+    static_assert(kOneReadBatch == NW * STEP || kOneReadShortBatch == NW * STEP, "a batch is one slice per wave");
     __shared__ __attribute__((aligned(16))) uint2 s_wlist[kOneReadCap];    // per-wave candidates: (FP32 bits, block)
     __shared__ __attribute__((aligned(16))) uint32_t s_ckey[kOneReadCap];  // candidates in block order
     __shared__ __attribute__((aligned(16))) int32_t s_cblk[kOneReadCap];
@@ -524,12 +524,28 @@ hipError_t launch_split(const SplitArgs &a, hipStream_t s)
 
 hipError_t launch_oneread(const OneReadArgs &a, hipStream_t s)
 {
+    // A row's slices must fit the kernel's per-slice records (MAXS): the
+    // half-size slices serve rows of at most kOneReadShortRow blocks.
+    static_assert(kOneReadShortFewRow <= kOneReadShortRow, "the few-query limit is the smaller");
+    static_assert((int64_t)kOneReadShortRow <= (int64_t)kOneReadMaxBatches * kOneReadShortBatch,
+                  "short rows fit the slice records");
     const dim3 grid((unsigned)a.g.nq);
-    if (a.g.vec4)
-        hipLaunchKernelGGL((oneread_kernel<kOneReadThreads, kOneReadF4, true>), grid, dim3(kOneReadThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((oneread_kernel<kOneReadThreads, kOneReadF4, false>), grid, dim3(kOneReadThreads), 0, s,
-                           a);
+    const bool shortrow = oneread_short_slices(a.g.nq, a.g.n_blocks);
+    if (a.g.vec4) {
+        if (shortrow)
+            hipLaunchKernelGGL((oneread_kernel<kOneReadThreads, kOneReadShortF4, true>), grid, dim3(kOneReadThreads), 0,
+                               s, a);
+        else
+            hipLaunchKernelGGL((oneread_kernel<kOneReadThreads, kOneReadF4, true>), grid, dim3(kOneReadThreads), 0, s,
+                               a);
+    } else {
+        if (shortrow)
+            hipLaunchKernelGGL((oneread_kernel<kOneReadThreads, kOneReadShortF4, false>), grid, dim3(kOneReadThreads),
+                               0, s, a);
+        else
+            hipLaunchKernelGGL((oneread_kernel<kOneReadThreads, kOneReadF4, false>), grid, dim3(kOneReadThreads), 0, s,
+                               a);
+    }
     return hipGetLastError();
 }
 
