@@ -61,6 +61,11 @@ def test_dispatch_rule():
     # chunk sizes for about 512 first-launch workgroups
     assert qsa.topk_plan(3, 130048, 4, 2048, "decode")["filter_blocks"] == 1024
     assert qsa.topk_plan(16, 130048, 4, 2048, "decode")["filter_blocks"] == 4096
+    # One-read stream slices: half size (a batch of 8,192 blocks) for rows of
+    # up to 16,384 blocks, or 65,536 with 64 or more queries.
+    for nq, nb, batch in ((3, 16384, 8192), (3, 16385, 16384), (63, 65536, 16384), (64, 65536, 8192),
+                          (64, 65537, 16384), (256, 32768, 8192), (256, 130048, 16384), (16, 65536, 16384)):
+        assert qsa.topk_plan(nq, nb, 4, 2048, "prompt")["oneread_blocks"] == batch, (nq, nb)
 
 
 def test_filter_geometry():

@@ -214,6 +214,25 @@ def test_oneread_longest_row():
             assert_ids_equal(got, exp, f"longest row nb={nb} {path}")
 
 
+@pytest.mark.parametrize("nq,n_blocks,short", [(3, 16384, True), (3, 16385, False), (64, 65536, True),
+                                               (64, 65537, False), (63, 65536, False)])
+def test_oneread_slice_sizes_at_their_bounds(nq, n_blocks, short):
+    """The one-read kernel streams short rows in 2 KiB slices (up to 16,384
+    blocks, or 65,536 with 64 or more queries) and longer ones in 4 KiB
+    slices: rows on either side of each bound, with ragged visible lengths
+    (partial last slices), sampled and with every query flagged."""
+    tag = f"gpu/topk/slices/{nq}/{n_blocks}"
+    s = _keys(tag, "normal", nq, n_blocks, n_blocks)
+    active = (n_blocks - (np.arange(nq) * 37) % 700).astype(np.int32)
+    exp = oracle.topk_rule(s, n_blocks, 4, 2048, active)
+    plan = qsa.topk_plan(nq, n_blocks, 4, 2048, "prompt")
+    assert plan["oneread_blocks"] == (8192 if short else 16384), plan
+    for path in ("auto", "oneread_lines", "fallback"):
+        say(f"slices nq={nq} nb={n_blocks} {path}")
+        got = gpu_topk(s, n_blocks, 4, 2048, "prompt", active=active, options=_opts(path))
+        assert_ids_equal(got, exp, f"slices nq={nq} nb={n_blocks} {path}")
+
+
 def test_rows_past_4gib():
     """Score rows 2.4 GB apart in a 7.2 GB buffer: every path reads rows at
     64-bit offsets (the third row starts past 2^32 bytes). Only the visible
