@@ -527,18 +527,21 @@ __device__ __forceinline__ void score_tiles_bf16(const ScoreArgs &a, int row0, i
     }
 }
 
-// The BF16 path of 16-wave workgroups with one row tile per wave: key-tile
-// pairs straight into LDS as in score_tiles_dma (a padded BF16 key row is
-// one load instruction: 64 lanes x 4 bytes), kA and kB separate LDS arrays.
+// The BF16 path of 512-row workgroups (16 waves of one row tile, or 8 waves
+// of two: each key operand read from LDS then feeds two matrix steps): key-
+// tile pairs straight into LDS as in score_tiles_dma (a padded BF16 key row
+// is one load instruction: 64 lanes x 4 bytes), kA and kB separate LDS arrays.
 constexpr int kDmaTileH = kTileBlocks * kLdsRowH;  // BF16 values per staged key tile
 
-template <int HP, class Store>
+template <int HP, int NW, int MR, class Store>
 __device__ __forceinline__ void score_tiles_bf16_dma(const ScoreArgs &a, int row0, int t0, int t1,
                                                      uint16_t (&kA)[2][kDmaTileH], uint16_t (&kB)[2][kDmaTileH],
                                                      float *w_lds, Store store)
 {
-    constexpr int NW = 16, MR = 1, NT = NW * 64, ROWS = NW * 32;
-    static_assert(HP <= 32, "one row tile per wave");
+    constexpr int NT = NW * 64, ROWS = NW * MR * 32;
+    constexpr int RPW = kTileBlocks / NW;  // key rows each wave loads per tile
+    static_assert(HP <= 32, "whole queries inside a row tile");
+    static_assert(RPW * NW == kTileBlocks, "waves split a tile's rows evenly");
     const uint16_t *qh = reinterpret_cast<const uint16_t *>(a.q);
     const uint16_t *kh = reinterpret_cast<const uint16_t *>(a.k);
     const int tid = threadIdx.x;
@@ -558,8 +561,8 @@ __device__ __forceinline__ void score_tiles_bf16_dma(const ScoreArgs &a, int row
 #pragma unroll
         for (int d = 0; d < 2; ++d)
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int row = 2 * wv + x;
+            for (int x = 0; x < RPW; ++x) {
+                const int row = RPW * wv + x;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     r, (__attribute__((address_space(3))) void *)(&dst[d][row * kLdsRowH]), 4,
                     ((d * kTileBlocks + row) * kHeadDim) * 2 + 4 * lane, 0, 0, 0);
@@ -571,9 +574,10 @@ __device__ __forceinline__ void score_tiles_bf16_dma(const ScoreArgs &a, int row
     issue_pair(t0, kA);
 
     // q rows of this wave -> VGPRs (A operand): 64 BF16 values per lane.
-    bf16x8 qa[8];
-    {
-        const int R = row0 + wv * 32 + li;
+    bf16x8 qa[MR][8];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        const int R = row0 + (wv * MR + m) * 32 + li;
         const int qi = R / HP, h = R % HP;
         const bool ok = qi < a.nq && h < a.heads;
         const uint4 *src = reinterpret_cast<const uint4 *>(
@@ -581,7 +585,7 @@ __device__ __forceinline__ void score_tiles_bf16_dma(const ScoreArgs &a, int row
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const uint4 v = ok ? src[u] : make_uint4(0u, 0u, 0u, 0u);
-            qa[u] = __builtin_bit_cast(bf16x8, v);
+            qa[m][u] = __builtin_bit_cast(bf16x8, v);
         }
     }
     for (int r = tid; r < ROWS; r += NT) {
@@ -592,10 +596,12 @@ __device__ __forceinline__ void score_tiles_bf16_dma(const ScoreArgs &a, int row
 
     __syncthreads();  // the first pair and the weights are in LDS
     // This wave's weights, once, in registers.
-    float wr[16];
+    float wr[MR][16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-        wr[v] = w_lds[wv * 32 + 8 * (v >> 2) + 4 * half + (v & 3)];
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            wr[m][v] = w_lds[(wv * MR + m) * 32 + 8 * (v >> 2) + 4 * half + (v & 3)];
 
     // One staged tile through the matrix cores and the epilogue (every lane
     // stores; the store drops what is not a score: MASKED). Waves whose rows
@@ -603,16 +609,20 @@ __device__ __forceinline__ void score_tiles_bf16_dma(const ScoreArgs &a, int row
     auto score_tile = [&](int t, const uint16_t *kt) {
         f32x16 acc[MR];
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            acc[0][v] = 0.f;
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[m][v] = 0.f;
         const uint16_t *kb = kt + li * kLdsRowH + 64 * half;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(kb + 8 * u));
-            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[u], b, acc[0], 0, 0, 0);
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[m][u], b, acc[m], 0, 0, 0);
         }
         score_epilogue<HP, MR, true>(acc, a, row0, wv, half, t * kTileBlocks + li,
-                                     [&](int m, int v) { return wr[v]; }, store);
+                                     [&](int m, int v) { return wr[m][v]; }, store);
     };
 
     for (int tb = t0; tb < t1; tb += 4) {

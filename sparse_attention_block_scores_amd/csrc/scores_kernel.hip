@@ -26,10 +26,12 @@ struct ScoreGrid {
 
 // The second bound is the waves per SIMD the register budget must allow:
 // two 4-wave or two 8-wave workgroups per CU, or one 16-wave workgroup. With
-// 1 or 2 heads the epilogue keeps a partial sum per row and gets the larger
+// 1 or 2 heads the epilogue keeps a partial sum per row, and with two row
+// tiles per wave (MR = 2) q takes twice the VGPRs: those get the larger
 // budget of one 8-wave workgroup per CU instead of spilling.
 template <int HP, int MR, int NW, bool BF16>
-__global__ __launch_bounds__(NW * 64, NW >= 8 && HP >= 4 ? 4 : 2) void scores_kernel(ScoreArgs a, ScoreGrid grid)
+__global__ __launch_bounds__(NW * 64, NW >= 8 && HP >= 4 && MR == 1 ? 4 : 2) void scores_kernel(ScoreArgs a,
+                                                                                              ScoreGrid grid)
 {
     constexpr int ROWS = NW * MR * 32;
     using Lds = typename std::conditional<BF16, ScoreLdsH<ROWS>, ScoreLds<ROWS>>::type;
@@ -67,11 +69,11 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 && HP >= 4 ? 4 : 2) void scores_ke
             const int off = ok ? ((qi - qb) * (int)a.ld + blk) * 4 : (int)0x80000000;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), r, off, 0, 0);
         };
-        if constexpr (NW == 16 && MR == 1) {
+        if constexpr ((NW == 16 && MR == 1) || (NW == 8 && MR == 2)) {
             __shared__ __attribute__((aligned(16))) uint16_t kA[2][kDmaTileH];
             __shared__ __attribute__((aligned(16))) uint16_t kB[2][kDmaTileH];
             __shared__ float w_lds[ROWS];
-            score_tiles_bf16_dma<HP>(a, slab * ROWS, t0, t1, kA, kB, w_lds, store);
+            score_tiles_bf16_dma<HP, NW, MR>(a, slab * ROWS, t0, t1, kA, kB, w_lds, store);
         } else {
             __shared__ Lds sm;
             score_tiles_bf16<HP, MR, NW>(a, slab * ROWS, t0, t1, sm, store);
@@ -123,8 +125,10 @@ hipError_t launch_cfg(const ScoreArgs &a, hipStream_t s)
 // 64 heads: a wave holds a whole query (two 32-row tiles). Otherwise each
 // wave holds one 32-row tile (a quarter of the VGPRs, four waves per SIMD);
 // many rows take 16-wave workgroups, one per CU, which halves the key tiles
-// each CU stages and the key traffic from L2; few rows take 8-wave
-// workgroups (as do 1 or 2 heads), whose 256 rows match the decode shapes.
+// each CU stages and the key traffic from L2 (BF16 with 8 or more heads:
+// 8-wave workgroups of two row tiles per wave, the same 512-row slabs); few
+// rows take 8-wave workgroups (as do 1 or 2 heads), whose 256 rows match the
+// decode shapes.
 template <int HP, bool BF16>
 hipError_t launch_hp(const ScoreArgs &a, hipStream_t s)
 {
@@ -133,8 +137,17 @@ hipError_t launch_hp(const ScoreArgs &a, hipStream_t s)
     } else {
         const int64_t rows = (int64_t)a.nq * HP;
         if constexpr (HP >= 4) {  // 1 or 2 heads: the epilogue's partial sums need more VGPRs
-            if (rows >= 16 * 512)
-                return launch_cfg<HP, 1, 16, BF16>(a, s);
+            if (rows >= 16 * 512) {
+                // BF16 with 8 or more heads: eight-wave workgroups of two row
+                // tiles per wave (the same 512-row slabs), so each key-tile
+                // operand read from LDS feeds two matrix steps (C5 239 -> 226
+                // us); FP32 keeps one row tile per wave (its operand reads are
+                // a quarter as frequent per cycle, and q takes 64 VGPRs a tile).
+                if constexpr (BF16 && HP >= 8)
+                    return launch_cfg<HP, 2, 8, BF16>(a, s);
+                else
+                    return launch_cfg<HP, 1, 16, BF16>(a, s);
+            }
         }
         return launch_cfg<HP, 1, 8, BF16>(a, s);
     }

@@ -134,10 +134,10 @@ def test_bf16_shapes(heads, nq, n_blocks):
     assert (s[:, n_blocks:] == 7.0).all(), "columns past n_blocks were written"
 
 
-@pytest.mark.parametrize("heads,nq,n_blocks", [(8, 1030, 1000), (31, 257, 1000), (32, 257, 1500)])
+@pytest.mark.parametrize("heads,nq,n_blocks", [(8, 1030, 1000), (13, 515, 1000), (31, 257, 1000), (32, 257, 1500)])
 def test_bf16_many_rows(heads, nq, n_blocks):
-    """The 16-wave BF16 workgroups (key-tile pairs loaded straight into LDS),
-    as test_many_rows."""
+    """The BF16 workgroups of 512-row slabs (eight waves of two row tiles,
+    key-tile pairs loaded straight into LDS), as test_many_rows."""
     tag = f"gpu/scores_bf16/many/{heads}/{nq}" + ("" if n_blocks == 1000 else f"/{n_blocks}")
     qb = synth.bf16_bits(synth.normal(tag + "/q", (nq, heads, 128)))
     kb = synth.bf16_bits(synth.normal(tag + "/k", (n_blocks, 128)))
