@@ -243,6 +243,30 @@ def length_shape(shape, contiguous, nq, name):
         raise ValueError(f"{name} must be a contiguous [nq] = [{nq}] int32 tensor, got {tuple(shape)}")
 
 
+def attention_shapes(q_shape, k_shape, v_shape, ids_shape, ids_strides, width, out_shape=None, lse_shape=None):
+    """Shape checks of selection_attention: q [nq, n_heads, D], k and v
+    [n_cells, kv_heads, D], ids [nq, ld] with unit column stride and
+    ld >= width, out [nq, n_heads, D] and lse [nq, n_heads] when given.
+    Returns (nq, n_heads, kv_heads, D, n_cells)."""
+    if len(q_shape) != 3 or len(k_shape) != 3 or len(v_shape) != 3:
+        raise ValueError(f"q, k and v must be 3-d; got q{tuple(q_shape)} k{tuple(k_shape)} v{tuple(v_shape)}")
+    nq, n_heads, head_dim = (int(x) for x in q_shape)
+    n_cells, kv_heads = int(k_shape[0]), int(k_shape[1])
+    if tuple(v_shape) != tuple(k_shape) or int(k_shape[2]) != head_dim:
+        raise ValueError(f"k and v must both be [n_cells, kv_heads, {head_dim}]; got k{tuple(k_shape)} v{tuple(v_shape)}")
+    if len(ids_shape) != 2 or int(ids_strides[1]) != 1:
+        raise ValueError("ids must be [nq, ld] with unit column stride")
+    if int(ids_shape[0]) != nq:
+        raise ValueError(f"ids has {int(ids_shape[0])} rows, expected nq = {nq}")
+    if width > int(ids_shape[1]):
+        raise ValueError(f"width {width} is larger than the {int(ids_shape[1])} columns of ids")
+    if out_shape is not None and tuple(out_shape) != (nq, n_heads, head_dim):
+        raise ValueError(f"out must be [nq, n_heads, head_dim] = [{nq}, {n_heads}, {head_dim}], got {tuple(out_shape)}")
+    if lse_shape is not None and tuple(lse_shape) != (nq, n_heads):
+        raise ValueError(f"lse must be [nq, n_heads] = [{nq}, {n_heads}], got {tuple(lse_shape)}")
+    return nq, n_heads, kv_heads, head_dim, n_cells
+
+
 def block_scores(q, k, w, scores=None, stream=None):
     """score[q,b] = sum_h w[q,h] relu(q[q,h,:] . k[b,:]) -> float32 [nq, ld]."""
     _dev(q, torch.float32, "q"), _dev(k, torch.float32, "k"), _dev(w, torch.float32, "w")
@@ -295,13 +319,12 @@ def selection_attention(q, k, v, ids, width=None, scale=None, out=None, lse=None
         if not t.is_contiguous() or t.dim() != 3:
             raise ValueError(f"{name} must be a contiguous 3-d tensor")
     _dev(ids, torch.int32, "ids")
-    if ids.dim() != 2 or ids.stride(1) != 1:
+    if ids.dim() != 2:
         raise ValueError("ids must be [nq, ld] with unit column stride")
-    nq, n_heads, head_dim = q.shape
-    n_cells, kv_heads = k.shape[0], k.shape[1]
-    if tuple(v.shape) != tuple(k.shape) or k.shape[2] != head_dim or ids.shape[0] != nq:
-        raise ValueError("shape mismatch between q, k, v and ids")
     width = ids.shape[1] if width is None else int(width)
+    nq, n_heads, kv_heads, head_dim, n_cells = attention_shapes(
+        q.shape, k.shape, v.shape, ids.shape, ids.stride(), width,
+        None if out is None else out.shape, None if lse is None else lse.shape)
     scale = 1.0 / head_dim ** 0.5 if scale is None else float(scale)
     if out is None:
         out = torch.empty((nq, n_heads, head_dim), dtype=torch.float32, device=q.device)

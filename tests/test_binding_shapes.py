@@ -61,3 +61,26 @@ def test_length_shape():
         B.length_shape((4,), True, 5, "cells")
     with pytest.raises(ValueError, match="active"):
         B.length_shape((5,), False, 5, "active")
+
+
+def test_attention_shapes_ok():
+    assert B.attention_shapes((3, 8, 128), (4096, 2, 128), (4096, 2, 128), (3, 256), (256, 1), 256,
+                              (3, 8, 128), (3, 8)) == (3, 8, 2, 128, 4096)
+    assert B.attention_shapes((3, 8, 128), (4096, 2, 128), (4096, 2, 128), (3, 300), (304, 1), 256) \
+        == (3, 8, 2, 128, 4096)
+
+
+@pytest.mark.parametrize("q,k,v,ids,strides,width,out,lse,msg", [
+    ((3, 8, 128), (4096, 2, 128), (4096, 2, 64), (3, 256), (256, 1), 256, None, None, "k and v"),
+    ((3, 8, 128), (4096, 2, 64), (4096, 2, 64), (3, 256), (256, 1), 256, None, None, "k and v"),
+    ((24, 128), (4096, 2, 128), (4096, 2, 128), (3, 256), (256, 1), 256, None, None, "3-d"),
+    ((3, 8, 128), (4096, 2, 128), (4096, 2, 128), (2, 256), (256, 1), 256, None, None, "rows"),
+    ((3, 8, 128), (4096, 2, 128), (4096, 2, 128), (3, 256), (1, 3), 256, None, None, "unit column stride"),
+    ((3, 8, 128), (4096, 2, 128), (4096, 2, 128), (3, 256), (256, 1), 257, None, None, "width"),
+    ((3, 8, 128), (4096, 2, 128), (4096, 2, 128), (3, 256), (256, 1), 256, (3, 4, 128), None, "out must be"),
+    ((3, 8, 128), (4096, 2, 128), (4096, 2, 128), (3, 256), (256, 1), 256, (2, 8, 128), None, "out must be"),
+    ((3, 8, 128), (4096, 2, 128), (4096, 2, 128), (3, 256), (256, 1), 256, None, (3, 4), "lse must be"),
+])
+def test_attention_shape_mismatch(q, k, v, ids, strides, width, out, lse, msg):
+    with pytest.raises(ValueError, match=msg):
+        B.attention_shapes(q, k, v, ids, strides, width, out, lse)

@@ -82,3 +82,33 @@ def test_block_scores_rejects_narrow_scores():
         qsa.block_scores(q, k, w, scores=s)
     torch.cuda.synchronize()
     assert (s == 5.0).all()
+
+
+@pytest.mark.parametrize("case", ["out_heads", "out_rows", "lse_heads", "ids_rows", "width_past_ids"])
+def test_selection_attention_rejects(case):
+    dev = device()
+    nq, heads, kv, cells = 3, 8, 2, 4096
+    q = torch.randn((nq, heads, 128), device=dev).to(torch.bfloat16)
+    k = torch.randn((cells, kv, 128), device=dev).to(torch.bfloat16)
+    v = torch.randn((cells, kv, 128), device=dev).to(torch.bfloat16)
+    ids = torch.arange(nq * 256, dtype=torch.int32, device=dev).reshape(nq, 256)
+    out = torch.full((nq, heads, 128), -7.0, device=dev)
+    lse = torch.full((nq, heads), -7.0, device=dev)
+    kw = dict(out=out, lse=lse)
+    if case == "out_heads":
+        kw["out"] = torch.full((nq, heads // 2, 128), -7.0, device=dev)
+    elif case == "out_rows":
+        kw["out"] = torch.full((nq - 1, heads, 128), -7.0, device=dev)
+    elif case == "lse_heads":
+        kw["lse"] = torch.full((nq, heads // 2), -7.0, device=dev)
+    elif case == "ids_rows":
+        ids = ids[:2]
+    elif case == "width_past_ids":
+        kw["width"] = 257
+    say(f"selection_attention rejects {case}")
+    torch.cuda.synchronize()
+    with pytest.raises(ValueError):
+        qsa.selection_attention(q, k, v, ids, **kw)
+    torch.cuda.synchronize()
+    for t in (kw["out"], kw["lse"]):
+        assert (t == -7.0).all(), "a rejected call wrote its output"
