@@ -161,6 +161,21 @@ def secondary(torch, qsa, synth, dev, reps=50):
     out["decode_nq3_select_us"] = round(time_us(lambda i: qsa.select(q, k, w, 4, wl.width, "decode", scores=s,
                                                                       ids=ids, counts=cnt, ws=ws,
                                                                       stream=cur())), 2)
+    # The same 3 queries x 8 heads over the decode contexts of the top-k
+    # figures (scores and top-k, one call).
+    by_cells = {}
+    for nb in synth.C2_BLOCKS:
+        wlc = synth.SelectWorkload(f"C1@{nb}", nq=3, heads=8, n_blocks=nb, block_size=4, width=2048,
+                                   call="decode")
+        qc, kc, wc = [torch.from_numpy(x).to(dev) for x in wlc.tensors()]
+        wsc = qsa.workspace(qsa.topk_workspace_bytes(3, nb, 4, 2048, "decode"), dev)
+        sc = torch.empty((3, nb), device=dev)
+        idc = torch.empty((3, 2048), dtype=torch.int32, device=dev)
+        cc = torch.empty((3,), dtype=torch.int32, device=dev)
+        by_cells[str(nb * 4)] = round(time_us(lambda i: qsa.select(qc, kc, wc, 4, 2048, "decode", scores=sc, ids=idc,
+                                                                   counts=cc, ws=wsc, stream=cur())), 2)
+        del qc, kc, wc, wsc, sc
+    out["decode_nq3_select_us_by_cells"] = by_cells
     wl3 = synth.c3()
     q3, k3, w3 = [torch.from_numpy(x).to(dev) for x in wl3.tensors()]
     ws3 = qsa.workspace(qsa.topk_workspace_bytes(wl3.nq, wl3.n_blocks, 4, wl3.width, "decode"), dev)

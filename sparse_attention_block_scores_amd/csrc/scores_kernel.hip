@@ -92,6 +92,106 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 && HP >= 4 && MR == 1 ? 4 : 2) voi
     }
 }
 
+// FP32 scores of long rows when every padded (query, head) row fits one
+// 32-row tile (a few queries with few heads over a long context). The slab
+// grid would leave one live wave per workgroup (the rest padding), scoring
+// its column group's key tiles one after another. Here the workgroup stages
+// the 32 q rows in LDS once (coalesced), every wave takes them as its A
+// operand, and each wave scores key tiles of its own: a tile is loaded
+// coalesced into the wave's LDS area (rows padded to 132 floats, as in the
+// slab kernels) and read back as the B operand. Waves share nothing after
+// the prologue, so the loop has no barrier. (Keeping the wave's next tile in
+// flight in registers put that array in scratch memory; with up to 2,048
+// tiles every wave has one tile, and two waves per SIMD overlap the rest.)
+constexpr int kLongWaves = 8;
+constexpr int kLongMinTiles = 1024;  // shorter rows keep the slab grid
+
+template <int HP>
+__global__ __launch_bounds__(kLongWaves * 64, 2) void scores_longrow_kernel(ScoreArgs a, int n_tiles, int tiles_per_wg)
+{
+    static_assert(HP <= 32, "every row inside one 32-row tile");
+    constexpr int NT = kLongWaves * 64;
+    __shared__ __attribute__((aligned(16))) float q_lds[kTileBlocks * kLdsRow];
+    __shared__ __attribute__((aligned(16))) float k_lds[kLongWaves][kTileBlocks * kLdsRow];
+    __shared__ float w_lds[32];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, half = lane >> 5;
+
+    const int tb = (int)blockIdx.x * tiles_per_wg;
+    const int te = min(tb + tiles_per_wg, n_tiles);
+    int t = tb + wv;
+    // q rows 0..31 of the tile (zero past nq x heads) and their weights.
+    for (int f = tid; f < kTileBlocks * 32; f += NT) {
+        const int r = f >> 5, c = f & 31, qi = r / HP, h = r % HP;
+        const bool ok = qi < a.nq && h < a.heads;
+        const float4 v = ok ? reinterpret_cast<const float4 *>(a.q + ((int64_t)qi * a.heads + h) * kHeadDim)[c]
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4 *>(&q_lds[r * kLdsRow + 4 * c]) = v;
+    }
+    if (tid < 32) {
+        const int qi = tid / HP, h = tid % HP;
+        w_lds[tid] = (qi < a.nq && h < a.heads) ? a.w[(int64_t)qi * a.heads + h] : 0.f;
+    }
+    __syncthreads();
+    float4 qa4[16];
+    {
+        const float *src = q_lds + li * kLdsRow + 64 * half;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            qa4[u] = *reinterpret_cast<const float4 *>(src + 4 * u);
+    }
+
+    for (; t < te; t += kLongWaves) {
+        // Tile t's 32 key rows (16 KiB, consecutive in memory) through
+        // registers: lane l takes float4 l + 64u, u < 16 (row (l + 64u) / 32,
+        // part (l + 64u) % 32). Rows past the last block read block
+        // n_blocks - 1 (their scores are not stored).
+        float4 nxt[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int f = lane + 64 * u;
+            const int b = min(t * kTileBlocks + (f >> 5), a.n_blocks - 1);
+            nxt[u] = reinterpret_cast<const float4 *>(a.k + (int64_t)b * kHeadDim)[f & 31];
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int f = lane + 64 * u;
+            *reinterpret_cast<float4 *>(&k_lds[wv][(f >> 5) * kLdsRow + 4 * (f & 31)]) = nxt[u];
+        }
+        f32x16 acc[1];
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            acc[0][v] = 0.f;
+        const float *kb = &k_lds[wv][li * kLdsRow + 64 * half];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const float4 b = *reinterpret_cast<const float4 *>(kb + 4 * u);
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa4[u].x, b.x, acc[0], 0, 0, 0);
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa4[u].y, b.y, acc[0], 0, 0, 0);
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa4[u].z, b.z, acc[0], 0, 0, 0);
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa4[u].w, b.w, acc[0], 0, 0, 0);
+        }
+        score_epilogue<HP, 1>(
+            acc, a, 0, 0, half, t * kTileBlocks + li,
+            [&](int, int v) { return w_lds[8 * (v >> 2) + 4 * half + (v & 3)]; },
+            [&](int q, int b, float x) { a.scores[(int64_t)q * a.ld + b] = x; });
+    }
+}
+
+template <int HP>
+hipError_t launch_longrow(const ScoreArgs &a, hipStream_t s)
+{
+    const int n_tiles = (a.n_blocks + kTileBlocks - 1) / kTileBlocks;
+    // Up to 256 workgroups (one per CU), each a multiple of 8 tiles.
+    const int per_wave = (n_tiles + 256 * kLongWaves - 1) / (256 * kLongWaves);
+    const int tiles_per_wg = per_wave * kLongWaves;
+    const int wgs = (n_tiles + tiles_per_wg - 1) / tiles_per_wg;
+    hipLaunchKernelGGL((scores_longrow_kernel<HP>), dim3((unsigned)wgs), dim3(kLongWaves * 64), 0, s, a, n_tiles,
+                       tiles_per_wg);
+    return hipGetLastError();
+}
+
 template <int HP, int MR, int NW, bool BF16>
 hipError_t launch_cfg(const ScoreArgs &a, hipStream_t s)
 {
@@ -136,6 +236,10 @@ hipError_t launch_hp(const ScoreArgs &a, hipStream_t s)
         return launch_cfg<HP, 2, 4, BF16>(a, s);
     } else {
         const int64_t rows = (int64_t)a.nq * HP;
+        if constexpr (!BF16) {
+            if (rows <= 32 && a.n_blocks >= kLongMinTiles * kTileBlocks)
+                return launch_longrow<HP>(a, s);
+        }
         if constexpr (HP >= 4) {  // 1 or 2 heads: the epilogue's partial sums need more VGPRs
             if (rows >= 16 * 512) {
                 // BF16 with 8 or more heads: eight-wave workgroups of two row

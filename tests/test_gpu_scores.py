@@ -77,6 +77,24 @@ def test_many_rows(heads, nq, n_blocks):
     assert (s[:, n_blocks:] == 7.0).all(), "columns past n_blocks were written"
 
 
+@pytest.mark.parametrize("heads,nq,n_blocks", [(8, 3, 65536 + 77), (32, 1, 32768), (3, 5, 40000),
+                                               (1, 19, 131072 + 5), (2, 16, 65536 + 31), (8, 3, 32767)])
+def test_few_rows_long_context(heads, nq, n_blocks):
+    """Every padded (query, head) row inside one 32-row tile over 1,024 or more
+    key tiles: one key tile per wave, several per wave past 2,048 tiles,
+    partial last tiles; 32,767 blocks (one tile short) keep the slab grid."""
+    tag = f"gpu/scores/long/{heads}/{nq}/{n_blocks}"
+    q = synth.normal(tag + "/q", (nq, heads, 128))
+    k = synth.normal(tag + "/k", (n_blocks, 128))
+    w = synth.uniform01(tag + "/w", (nq, heads)) * 2.0 - 0.5  # some negative weights too
+    say(f"scores few rows heads={heads} nq={nq} nb={n_blocks}")
+    s = gpu_scores(q, k, w, ld=n_blocks + 3, fill=7.0)
+    ref = oracle.block_scores(q, k, w)
+    terms = oracle.block_scores(np.abs(q), np.abs(k), np.abs(w))
+    assert_scores_close(s[:, :n_blocks], ref, f"few rows h={heads} nq={nq} nb={n_blocks}", terms)
+    assert (s[:, n_blocks:] == 7.0).all(), "columns past n_blocks were written"
+
+
 def test_decode_select_shapes_full():
     for wl in (synth.c1(), synth.c3()):
         q, k, w = wl.tensors()
